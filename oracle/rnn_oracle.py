@@ -1,0 +1,304 @@
+"""Plain fp64 implementation of the stacked RNN forward pass and its
+backward-through-time (BPTT).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Slow on purpose: one
+time step at a time, one matrix product per term, no blocking, no fusion, no
+hoisting of the input projection.  Every function here is pinned by the
+tests in ``tests/test_oracle_*.py`` (hand-worked GRU values, zero-weight
+closed forms, central finite differences, invariants, and ``torch.nn`` fp64
+special cases); none is left unpinned.
+
+Notation (per layer ``l`` and direction ``d``)
+----------------------------------------------
+* ``G`` gate blocks of width ``H`` each, in memory order
+  ``rnn_tanh: [a]``, ``lstm: [i, f, g, o]``, ``gru: [r, z, n]``.
+* ``gi_t = x_t W_ih^T + b_ih`` and ``gh_t = h_prev W_hh^T + b_hh``, both
+  ``[B, G*H]`` -- the two ``F.linear`` calls of the PyTorch GRU snippet in
+  oneDNN issue #218 "rnn training example?", applied to every cell type.
+* ``h_prev`` is ``h_{t-1}`` for ``d = 0`` and ``h_{t+1}`` for ``d = 1``
+  (direction 1 walks ``t = T-1 .. 0``); the first ``h_prev`` is
+  ``h0[l*D + d]``.
+
+Cell equations
+--------------
+* GRU, PyTorch/cuDNN flavour (the flavour the same issue says PyTorch and
+  cuDNN share; equations listed under "PyTorch equations" and in the snippet):
+  ``r = s(gi_r + gh_r)``, ``z = s(gi_z + gh_z)``,
+  ``n = tanh(gi_n + r * gh_n)``, ``h = (1 - z) * n + z * h_prev``.
+* GRU, TensorFlow flavour (listed as "Tensorflow" and as the flavour oneDNN
+  first implemented): ``n = tanh(gi_n + (r * h_prev) W_hn^T + b_hn)``; ``h``
+  as PyTorch.  The stray closing parenthesis printed in that line is read as
+  a typo.
+* GRU, original-paper flavour ("Note that in the paper"): ``n`` as
+  TensorFlow, ``h = (1 - z) * h_prev + z * n``.
+* LSTM (named on the MXNet "fused RNN operator" page, equations not printed):
+  the standard two-bias form ``a = gi + gh`` split ``[i, f, g, o]``,
+  ``i, f, o = s(.)``, ``g = tanh(.)``, ``c = f * c_prev + i * g``,
+  ``h = o * tanh(c)``; no peepholes, no projection, no forget-bias offset.
+* Vanilla RNN (named on the same page as "Vanilla RNN", equations not
+  printed): ``h = tanh(gi + gh)``.
+
+Stacking (Keras issue #3692, the ``CudnnLSTM(num_layers, ...)`` descriptor;
+MXNet page, "5-layers ... with bi-direction"): the input of layer 0 is ``x``,
+the input of layer ``l > 0`` is ``y_{l-1}``, the concatenation
+``[h^(0) | h^(1)]`` along features; ``y_l[t, :, d*H:(d+1)*H] = h_t^(d)``;
+``hy[l*D + d]`` (and ``cy``) is the last state produced: ``h_{T-1}`` for
+``d = 0`` and ``h_0`` for ``d = 1`` (shapes ``(num_layers*num_directions,
+batch, hidden)`` from the hx/cx/hy/cy question in oneDNN issue #218).
+
+Backward (the pages only say forward results are reused by the backward
+pass, MXNet page "Operator Registration"; the chain rule below is derived by
+hand and pinned by central finite differences): see :func:`backward`.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+MODES = ("rnn_tanh", "lstm", "gru")
+GATES = {"rnn_tanh": 1, "lstm": 4, "gru": 3}
+GRU_VARIANTS = ("pytorch", "tf", "paper")
+
+
+def _sigmoid(a):
+    # logistic function; exp overflow for very negative a gives 1/inf = 0,
+    # which is the correct limit
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-a))
+
+
+def _blocks(a, n):
+    """Split the last axis of ``a`` into ``n`` equal gate blocks."""
+    return np.split(a, n, axis=-1)
+
+
+def cell_forward(mode, x_t, h_prev, c_prev, p, gru_variant="pytorch"):
+    """One cell step.  Returns ``(h, c, saved)`` where ``saved`` holds what
+    the backward pass needs for this step.
+
+    ``x_t`` ``[B, I]``, ``h_prev``/``c_prev`` ``[B, H]`` (``c_prev`` ignored
+    unless LSTM), ``p`` a dict with ``w_ih [G*H, I]``, ``w_hh [G*H, H]``,
+    ``b_ih [G*H]``, ``b_hh [G*H]``.
+    """
+    gi = x_t @ p["w_ih"].T + p["b_ih"]
+    if mode == "rnn_tanh":
+        gh = h_prev @ p["w_hh"].T + p["b_hh"]
+        h = np.tanh(gi + gh)
+        return h, None, {"h": h}
+    if mode == "lstm":
+        gh = h_prev @ p["w_hh"].T + p["b_hh"]
+        a_i, a_f, a_g, a_o = _blocks(gi + gh, 4)
+        i = _sigmoid(a_i)
+        f = _sigmoid(a_f)
+        g = np.tanh(a_g)
+        o = _sigmoid(a_o)
+        c = f * c_prev + i * g
+        h = o * np.tanh(c)
+        return h, c, {"i": i, "f": f, "g": g, "o": o, "c": c, "c_prev": c_prev}
+    if mode == "gru":
+        H = h_prev.shape[1]
+        gi_r, gi_z, gi_n = _blocks(gi, 3)
+        w_hr, w_hz, w_hn = (p["w_hh"][k * H:(k + 1) * H] for k in range(3))
+        b_hr, b_hz, b_hn = (p["b_hh"][k * H:(k + 1) * H] for k in range(3))
+        r = _sigmoid(gi_r + h_prev @ w_hr.T + b_hr)
+        z = _sigmoid(gi_z + h_prev @ w_hz.T + b_hz)
+        if gru_variant == "pytorch":
+            gh_n = h_prev @ w_hn.T + b_hn
+            n = np.tanh(gi_n + r * gh_n)
+            h = (1.0 - z) * n + z * h_prev
+            return h, None, {"r": r, "z": z, "n": n, "gh_n": gh_n}
+        if gru_variant in ("tf", "paper"):
+            n = np.tanh(gi_n + (r * h_prev) @ w_hn.T + b_hn)
+            if gru_variant == "tf":
+                h = (1.0 - z) * n + z * h_prev
+            else:
+                h = (1.0 - z) * h_prev + z * n
+            return h, None, {"r": r, "z": z, "n": n}
+        raise ValueError(f"unknown GRU variant {gru_variant!r}")
+    raise ValueError(f"unknown mode {mode!r}")
+
+
+def _check_params(mode, params, num_layers, num_dirs, input_size, hidden):
+    G = GATES[mode]
+    assert len(params) == num_layers
+    for l in range(num_layers):
+        assert len(params[l]) == num_dirs
+        I_l = input_size if l == 0 else num_dirs * hidden
+        for d in range(num_dirs):
+            p = params[l][d]
+            assert p["w_ih"].shape == (G * hidden, I_l), (l, d, p["w_ih"].shape)
+            assert p["w_hh"].shape == (G * hidden, hidden)
+            assert p["b_ih"].shape == (G * hidden,)
+            assert p["b_hh"].shape == (G * hidden,)
+
+
+def forward(mode, x, params, h0=None, c0=None, num_dirs=1, gru_variant="pytorch",
+            keep=False):
+    """Stacked, optionally bidirectional forward pass in fp64.
+
+    ``x`` ``[T, B, I]`` (TNC, the layout named in the oneDNN issue's
+    packed-sequence question); ``params[l][d]`` as in :func:`cell_forward`;
+    ``h0``/``c0`` ``[L*D, B, H]`` or ``None`` (zeros).
+
+    Returns ``(y, hy, cy, cache)``: ``y [T, B, D*H]`` of the top layer,
+    ``hy``/``cy`` ``[L*D, B, H]`` (``cy`` is ``None`` unless LSTM) and, if
+    ``keep``, the per-step intermediates the backward pass reuses (the MXNet
+    page's "reserved workspace"), else ``None``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T, B, I = x.shape
+    L = len(params)
+    D = num_dirs
+    H = params[0][0]["w_hh"].shape[1]
+    _check_params(mode, params, L, D, I, H)
+    if mode != "gru" and gru_variant != "pytorch":
+        raise ValueError("gru_variant only applies to mode 'gru'")
+    h0 = np.zeros((L * D, B, H)) if h0 is None else np.asarray(h0, np.float64)
+    if mode == "lstm":
+        c0 = np.zeros((L * D, B, H)) if c0 is None else np.asarray(c0, np.float64)
+    hy = np.zeros((L * D, B, H))
+    cy = np.zeros((L * D, B, H)) if mode == "lstm" else None
+    cache = {"layer_inputs": [], "steps": {}, "gru_variant": gru_variant} if keep else None
+
+    layer_in = x
+    for l in range(L):
+        if keep:
+            cache["layer_inputs"].append(layer_in)
+        y_l = np.zeros((T, B, D * H))
+        for d in range(D):
+            p = params[l][d]
+            h = h0[l * D + d]
+            c = c0[l * D + d] if mode == "lstm" else None
+            order = range(T) if d == 0 else range(T - 1, -1, -1)
+            for t in order:
+                h_prev = h
+                h, c, saved = cell_forward(mode, layer_in[t], h_prev, c, p, gru_variant)
+                y_l[t, :, d * H:(d + 1) * H] = h
+                if keep:
+                    saved["h_prev"] = h_prev
+                    cache["steps"][(l, d, t)] = saved
+            hy[l * D + d] = h
+            if mode == "lstm":
+                cy[l * D + d] = c
+        layer_in = y_l
+    return layer_in, hy, cy, cache
+
+
+def backward(mode, params, cache, dy, dhy=None, dcy=None, num_dirs=1):
+    """Backward through time for :func:`forward` (PyTorch/cuDNN GRU flavour
+    only).
+
+    Gradients of the scalar ``sum(y*dy) + sum(hy*dhy) + sum(cy*dcy)``.
+    Returns ``(dx, dh0, dc0, dparams)`` with ``dparams[l][d]`` holding
+    ``w_ih, w_hh, b_ih, b_hh`` gradients (overwritten, not accumulated into
+    anything the caller passed).
+
+    Per layer from the top down, per direction, walking opposite to that
+    direction's forward order, with ``dh = dhy[l*D+d]``, ``dc = dcy[l*D+d]``
+    at the start, each step adds ``dY_l[t, :, d*H:(d+1)*H]`` to ``dh`` and
+    then:
+
+    * vanilla: ``da = dh * (1 - h^2)``; ``dG_i = dG_h = da``.
+    * LSTM: ``tau = tanh(c)``; ``do = dh * tau``;
+      ``dc += dh * o * (1 - tau^2)``; ``di = dc * g``; ``dg = dc * i``;
+      ``df = dc * c_prev``;
+      ``dG = [di*i(1-i), df*f(1-f), dg*(1-g^2), do*o(1-o)] = dG_i = dG_h``;
+      the carry becomes ``dc * f``.
+    * GRU: ``dn = dh * (1 - z)``; ``dz = dh * (h_prev - n)``;
+      ``da_n = dn * (1 - n^2)``; ``da_r = da_n * gh_n * r(1-r)``;
+      ``da_z = dz * z(1-z)``; ``dG_i = [da_r, da_z, da_n]``;
+      ``dG_h = [da_r, da_z, da_n * r]``; plus the direct term ``dh * z``.
+
+    Then ``dh_prev = dG_h W_hh (+ dh*z for GRU)``, ``dX_l[t] += dG_i W_ih``,
+    ``dW_ih += dG_i^T x_t``, ``dW_hh += dG_h^T h_prev``,
+    ``db_ih += sum_b dG_i``, ``db_hh += sum_b dG_h``.  ``dX_l`` is
+    ``dY_{l-1}``; ``dX_0`` is ``dx``.
+    """
+    if cache is None:
+        raise ValueError("backward needs the cache of forward(..., keep=True)")
+    if cache["gru_variant"] != "pytorch":
+        raise NotImplementedError("backward covers the PyTorch/cuDNN GRU flavour only")
+    L = len(params)
+    D = num_dirs
+    dy = np.asarray(dy, np.float64)
+    T, B, _ = dy.shape
+    H = params[0][0]["w_hh"].shape[1]
+    dhy = np.zeros((L * D, B, H)) if dhy is None else np.asarray(dhy, np.float64)
+    if mode == "lstm":
+        dcy = np.zeros((L * D, B, H)) if dcy is None else np.asarray(dcy, np.float64)
+    dh0 = np.zeros((L * D, B, H))
+    dc0 = np.zeros((L * D, B, H)) if mode == "lstm" else None
+    dparams = [[None] * D for _ in range(L)]
+
+    dY = dy
+    for l in range(L - 1, -1, -1):
+        layer_in = cache["layer_inputs"][l]
+        dX = np.zeros_like(layer_in)
+        for d in range(D):
+            p = params[l][d]
+            g = {k: np.zeros_like(v) for k, v in p.items()}
+            dh = dhy[l * D + d].copy()
+            dc = dcy[l * D + d].copy() if mode == "lstm" else None
+            # reverse of the forward order of this direction
+            order = range(T - 1, -1, -1) if d == 0 else range(T)
+            for t in order:
+                s = cache["steps"][(l, d, t)]
+                h_prev = s["h_prev"]
+                dh = dh + dY[t, :, d * H:(d + 1) * H]
+                direct = 0.0
+                if mode == "rnn_tanh":
+                    da = dh * (1.0 - s["h"] ** 2)
+                    dG_i = dG_h = da
+                elif mode == "lstm":
+                    i, f, gg, o, c = s["i"], s["f"], s["g"], s["o"], s["c"]
+                    tau = np.tanh(c)
+                    d_o = dh * tau
+                    dc = dc + dh * o * (1.0 - tau ** 2)
+                    d_i = dc * gg
+                    d_g = dc * i
+                    d_f = dc * s["c_prev"]
+                    dG_i = dG_h = np.concatenate(
+                        [d_i * i * (1.0 - i), d_f * f * (1.0 - f),
+                         d_g * (1.0 - gg ** 2), d_o * o * (1.0 - o)], axis=1)
+                    dc = dc * f
+                else:  # gru, PyTorch/cuDNN flavour
+                    r, z, n, gh_n = s["r"], s["z"], s["n"], s["gh_n"]
+                    dn = dh * (1.0 - z)
+                    dz = dh * (h_prev - n)
+                    da_n = dn * (1.0 - n ** 2)
+                    da_r = da_n * gh_n * r * (1.0 - r)
+                    da_z = dz * z * (1.0 - z)
+                    dG_i = np.concatenate([da_r, da_z, da_n], axis=1)
+                    dG_h = np.concatenate([da_r, da_z, da_n * r], axis=1)
+                    direct = dh * z
+                dX[t] += dG_i @ p["w_ih"]
+                g["w_ih"] += dG_i.T @ layer_in[t]
+                g["w_hh"] += dG_h.T @ h_prev
+                g["b_ih"] += dG_i.sum(axis=0)
+                g["b_hh"] += dG_h.sum(axis=0)
+                dh = dG_h @ p["w_hh"] + direct
+            dh0[l * D + d] = dh
+            if mode == "lstm":
+                dc0[l * D + d] = dc
+            dparams[l][d] = g
+        dY = dX
+    return dY, dh0, dc0, dparams
+
+
+def forward_flops(mode, T, B, input_size, hidden, num_layers, num_dirs):
+    """GEMM flops of one forward pass, ``2*M*N*K`` per product:
+    ``sum_{l,d} 2*T*B*G*H*(I_l + H)``.  Pointwise work is not counted (the
+    GFLOPS column of the cuDNN-5 optimisation table in Keras issue #3692
+    gives no definition; this is the plain GEMM count)."""
+    G = GATES[mode]
+    tot = 0
+    for l in range(num_layers):
+        I_l = input_size if l == 0 else num_dirs * hidden
+        tot += num_dirs * 2 * T * B * G * hidden * (I_l + hidden)
+    return tot
+
+
+def train_step_flops(mode, T, B, input_size, hidden, num_layers, num_dirs):
+    """Forward + backward-data (dX at every layer, dh recurrence) +
+    backward-weights (dW_ih, dW_hh): three times the forward count."""
+    return 3 * forward_flops(mode, T, B, input_size, hidden, num_layers, num_dirs)

@@ -1,0 +1,270 @@
+"""Checks that pin the fp64 oracle to things other than itself.
+
+Each check takes the oracle *module* as an argument so that the mutation test
+can run the same checks against deliberately broken copies of the oracle.
+Every check returns the worst error it saw (a float); callers compare it with
+a tolerance.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def zero_params(G, I, H, L=1, D=1):
+    out = []
+    for l in range(L):
+        I_l = I if l == 0 else D * H
+        out.append([{"w_ih": np.zeros((G * H, I_l)), "w_hh": np.zeros((G * H, H)),
+                     "b_ih": np.zeros(G * H), "b_hh": np.zeros(G * H)} for _ in range(D)])
+    return out
+
+
+def rand_case(mode, L, D, T, B, I, H, seed, scale=0.6):
+    """Small random case in fp64 (own generator; the oracle pins do not need
+    the working-precision rounding of the GPU inputs)."""
+    G = {"rnn_tanh": 1, "lstm": 4, "gru": 3}[mode]
+    rng = np.random.default_rng(seed)
+    params = []
+    for l in range(L):
+        I_l = I if l == 0 else D * H
+        params.append([{"w_ih": rng.uniform(-scale, scale, (G * H, I_l)),
+                        "w_hh": rng.uniform(-scale, scale, (G * H, H)),
+                        "b_ih": rng.uniform(-scale, scale, G * H),
+                        "b_hh": rng.uniform(-scale, scale, G * H)} for _ in range(D)])
+    x = rng.normal(size=(T, B, I))
+    h0 = rng.normal(size=(L * D, B, H)) * 0.5
+    c0 = rng.normal(size=(L * D, B, H)) * 0.5 if mode == "lstm" else None
+    dy = rng.normal(size=(T, B, D * H))
+    dhy = rng.normal(size=(L * D, B, H))
+    dcy = rng.normal(size=(L * D, B, H)) if mode == "lstm" else None
+    return dict(params=params, x=x, h0=h0, c0=c0, dy=dy, dhy=dhy, dcy=dcy)
+
+
+def normwise(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / den) if a.size else 0.0
+
+
+# ---------------------------------------------------------------- GRU variants
+def check_gru_worked_values(orc):
+    """Worst absolute error against the hand-worked values of the three GRU
+    flavours (golden fixture)."""
+    spec = json.load(open(os.path.join(GOLDEN, "gru_variants_worked.json")))
+    inp = spec["inputs"]
+    worst = 0.0
+    for case in spec["cases"]:
+        b_iz = math.log(3.0) if case["b_iz"] == "ln3" else float(case["b_iz"])
+        p = {"w_ih": np.zeros((3, 1)), "w_hh": np.zeros((3, 1)),
+             "b_ih": np.array([inp["b_ir"], b_iz, inp["b_in"]]),
+             "b_hh": np.array([inp["b_hr"], inp["b_hz"], inp["b_hn"]])}
+        x = np.full((1, 1, 1), inp["x"])
+        h0 = np.full((1, 1, 1), inp["h_prev"])
+        for variant in ("pytorch", "tf", "paper"):
+            y, hy, _, _ = orc.forward("gru", x, [[p]], h0=h0, gru_variant=variant)
+            worst = max(worst, abs(float(y[0, 0, 0]) - case[variant]),
+                        abs(float(hy[0, 0, 0]) - case[variant]))
+    return worst
+
+
+# ---------------------------------------------------------------- closed forms
+def check_closed_forms(orc):
+    spec = json.load(open(os.path.join(GOLDEN, "closed_forms.json")))
+    worst = 0.0
+    # GRU: b_in = 1, everything else 0, h0 = 0
+    for T_s, val in spec["gru_constant_input"]["values"].items():
+        T = int(T_s)
+        p = zero_params(3, 2, 3)
+        p[0][0]["b_ih"][6:9] = 1.0
+        x = np.zeros((T, 2, 2))
+        y, hy, _, _ = orc.forward("gru", x, p)
+        worst = max(worst, float(np.max(np.abs(hy - val))))
+        # the formula itself at every step, nonzero h0
+        h0 = np.full((1, 2, 3), 0.3)
+        y, hy, _, _ = orc.forward("gru", x, p, h0=h0)
+        tb = math.tanh(1.0)
+        for t in range(T):
+            ref = tb + 2.0 ** -(t + 1) * (0.3 - tb)
+            worst = max(worst, float(np.max(np.abs(y[t] - ref))))
+    # LSTM: b_ih = 1, b_hh = 0, c0 = 0
+    for T_s, val in spec["lstm_all_bias_one"]["values"].items():
+        T = int(T_s)
+        p = zero_params(4, 3, 2)
+        p[0][0]["b_ih"][:] = 1.0
+        x = np.zeros((T, 2, 3))
+        y, hy, cy, _ = orc.forward("lstm", x, p)
+        worst = max(worst, float(np.max(np.abs(hy - val))))
+    for T_s, val in spec["lstm_zero_bias_c0_one"]["values"].items():
+        T = int(T_s)
+        p = zero_params(4, 3, 2)
+        x = np.zeros((T, 1, 3))
+        y, hy, cy, _ = orc.forward("lstm", x, p, c0=np.ones((1, 1, 2)))
+        worst = max(worst, float(np.max(np.abs(hy - val))),
+                    float(np.max(np.abs(cy - 2.0 ** -T))))
+    # LSTM general constant-gate recurrence with distinct gate biases
+    b = np.array([0.3, -0.7, 0.9, 0.2])
+    p = zero_params(4, 1, 1)
+    p[0][0]["b_ih"][:] = b
+    T = 7
+    c0 = 0.4
+    y, hy, cy, _ = orc.forward("lstm", np.zeros((T, 1, 1)), p, c0=np.full((1, 1, 1), c0),
+                               h0=np.full((1, 1, 1), -0.8))
+    s = lambda a: 1.0 / (1.0 + math.exp(-a))
+    i, f, g, o = s(b[0]), s(b[1]), math.tanh(b[2]), s(b[3])
+    for t in range(T):
+        n = t + 1
+        c_ref = f ** n * c0 + i * g * (1 - f ** n) / (1 - f)
+        worst = max(worst, abs(float(y[t, 0, 0]) - o * math.tanh(c_ref)))
+    # vanilla: h_t = tanh(b_ih + b_hh) independent of h0
+    p = zero_params(1, 2, 3)
+    p[0][0]["b_ih"][:] = [0.1, -0.4, 2.0]
+    p[0][0]["b_hh"][:] = [0.5, 0.3, -1.0]
+    y, hy, _, _ = orc.forward("rnn_tanh", np.zeros((4, 2, 2)), p, h0=np.full((1, 2, 3), 0.7))
+    ref = np.tanh(np.array([0.6, -0.1, 1.0]))
+    worst = max(worst, float(np.max(np.abs(y - ref))))
+    return worst
+
+
+def check_bptt_closed_forms(orc):
+    worst = 0.0
+    # GRU, same weights as the forward closed form: only path is z*h -> dh0 = 2^-T g
+    for T in (1, 3, 16):
+        p = zero_params(3, 2, 3)
+        p[0][0]["b_ih"][6:9] = 1.0
+        x = np.zeros((T, 2, 2))
+        _, _, _, cache = orc.forward("gru", x, p, keep=True)
+        g = np.arange(1.0, 7.0).reshape(1, 2, 3)
+        dx, dh0, _, _ = orc.backward("gru", p, cache, np.zeros((T, 2, 3)), dhy=g)
+        worst = max(worst, float(np.max(np.abs(dh0 - 2.0 ** -T * g))))
+        worst = max(worst, float(np.max(np.abs(dx))))
+    # LSTM: dy = dhy = 0, dcy = g -> dc0 = sigmoid(b_f)^T g, dh0 = 0
+    bf = 0.35
+    for T in (1, 4, 9):
+        p = zero_params(4, 2, 3)
+        p[0][0]["b_ih"][3:6] = bf
+        x = np.zeros((T, 2, 2))
+        _, _, _, cache = orc.forward("lstm", x, p, c0=np.full((1, 2, 3), 0.2), keep=True)
+        g = np.linspace(-1, 1, 6).reshape(1, 2, 3)
+        dx, dh0, dc0, _ = orc.backward("lstm", p, cache, np.zeros((T, 2, 3)),
+                                       dhy=np.zeros((1, 2, 3)), dcy=g)
+        f = 1.0 / (1.0 + math.exp(-bf))
+        worst = max(worst, float(np.max(np.abs(dc0 - f ** T * g))),
+                    float(np.max(np.abs(dh0))))
+    # vanilla: dh0 = 0 with zero recurrent weights
+    p = zero_params(1, 2, 3)
+    p[0][0]["b_ih"][:] = 0.4
+    _, _, _, cache = orc.forward("rnn_tanh", np.zeros((5, 2, 2)), p, keep=True)
+    rng = np.random.default_rng(0)
+    _, dh0, _, _ = orc.backward("rnn_tanh", p, cache, rng.normal(size=(5, 2, 3)),
+                                dhy=rng.normal(size=(1, 2, 3)))
+    worst = max(worst, float(np.max(np.abs(dh0))))
+    return worst
+
+
+# ------------------------------------------------------------- torch.nn match
+def _torch_module(mode, I, H, L, D):
+    kw = dict(input_size=I, hidden_size=H, num_layers=L, bidirectional=(D == 2),
+              dtype=torch.float64)
+    if mode == "lstm":
+        return torch.nn.LSTM(**kw)
+    if mode == "gru":
+        return torch.nn.GRU(**kw)
+    return torch.nn.RNN(nonlinearity="tanh", **kw)
+
+
+def check_against_torch(orc, mode, L, D, T=4, B=3, I=5, H=6, seed=11):
+    """Normwise error of the oracle's forward outputs and all gradients
+    against ``torch.nn`` in float64 on the CPU (same equations; PyTorch is
+    the implementation the oneDNN issue names for the GRU flavour)."""
+    case = rand_case(mode, L, D, T, B, I, H, seed)
+    params = case["params"]
+    m = _torch_module(mode, I, H, L, D)
+    with torch.no_grad():
+        for l in range(L):
+            for d in range(D):
+                sfx = f"l{l}" + ("_reverse" if d == 1 else "")
+                for name in ("w_ih", "w_hh", "b_ih", "b_hh"):
+                    tname = {"w_ih": "weight_ih_", "w_hh": "weight_hh_",
+                             "b_ih": "bias_ih_", "b_hh": "bias_hh_"}[name] + sfx
+                    getattr(m, tname).copy_(torch.from_numpy(params[l][d][name]))
+    x = torch.from_numpy(case["x"]).requires_grad_(True)
+    h0 = torch.from_numpy(case["h0"]).requires_grad_(True)
+    if mode == "lstm":
+        c0 = torch.from_numpy(case["c0"]).requires_grad_(True)
+        out, (hn, cn) = m(x, (h0, c0))
+    else:
+        out, hn = m(x, h0)
+    loss = (out * torch.from_numpy(case["dy"])).sum() + (hn * torch.from_numpy(case["dhy"])).sum()
+    if mode == "lstm":
+        loss = loss + (cn * torch.from_numpy(case["dcy"])).sum()
+    loss.backward()
+
+    y, hy, cy, cache = orc.forward(mode, case["x"], params, h0=case["h0"], c0=case["c0"],
+                                   num_dirs=D, keep=True)
+    errs = [normwise(y, out.detach().numpy()), normwise(hy, hn.detach().numpy())]
+    if mode == "lstm":
+        errs.append(normwise(cy, cn.detach().numpy()))
+    dx, dh0, dc0, dparams = orc.backward(mode, params, cache, case["dy"], dhy=case["dhy"],
+                                         dcy=case["dcy"], num_dirs=D)
+    errs += [normwise(dx, x.grad.numpy()), normwise(dh0, h0.grad.numpy())]
+    if mode == "lstm":
+        errs.append(normwise(dc0, c0.grad.numpy()))
+    for l in range(L):
+        for d in range(D):
+            sfx = f"l{l}" + ("_reverse" if d == 1 else "")
+            for name, tname in (("w_ih", "weight_ih_"), ("w_hh", "weight_hh_"),
+                                ("b_ih", "bias_ih_"), ("b_hh", "bias_hh_")):
+                errs.append(normwise(dparams[l][d][name], getattr(m, tname + sfx).grad.numpy()))
+    return max(errs)
+
+
+# --------------------------------------------------------- finite differences
+def _loss(orc, mode, case, D):
+    y, hy, cy, _ = orc.forward(mode, case["x"], case["params"], h0=case["h0"], c0=case["c0"],
+                               num_dirs=D)
+    v = float(np.sum(y * case["dy"]) + np.sum(hy * case["dhy"]))
+    if mode == "lstm":
+        v += float(np.sum(cy * case["dcy"]))
+    return v
+
+
+def check_finite_differences(orc, mode, L, D, T=3, B=2, I=3, H=4, seed=5, eps=1e-6):
+    """Worst normwise error of every analytic gradient against central
+    differences of the scalar loss ``sum(y*dy) + sum(hy*dhy) + sum(cy*dcy)``."""
+    case = rand_case(mode, L, D, T, B, I, H, seed)
+    _, _, _, cache = orc.forward(mode, case["x"], case["params"], h0=case["h0"], c0=case["c0"],
+                                 num_dirs=D, keep=True)
+    dx, dh0, dc0, dparams = orc.backward(mode, case["params"], cache, case["dy"],
+                                         dhy=case["dhy"], dcy=case["dcy"], num_dirs=D)
+
+    def fd(arr):
+        g = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp = _loss(orc, mode, case, D)
+            arr[idx] = old - eps
+            lm = _loss(orc, mode, case, D)
+            arr[idx] = old
+            g[idx] = (lp - lm) / (2 * eps)
+        return g
+
+    errs = [normwise(dx, fd(case["x"])), normwise(dh0, fd(case["h0"]))]
+    if mode == "lstm":
+        errs.append(normwise(dc0, fd(case["c0"])))
+    for l in range(L):
+        for d in range(D):
+            for name in ("w_ih", "w_hh", "b_ih", "b_hh"):
+                errs.append(normwise(dparams[l][d][name], fd(case["params"][l][d][name])))
+    return max(errs)
