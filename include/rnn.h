@@ -1,0 +1,193 @@
+/*
+ * rnn.h -- C ABI of the fused stacked RNN operator for AMD Instinct MI355X
+ * (gfx950): vanilla tanh RNN, LSTM and GRU (PyTorch/cuDNN equations), forward
+ * inference, forward training that fills a caller-owned reserved workspace,
+ * and backward through time that reuses it.
+ *
+ * Sources (web pages, cited by title and section):
+ *  - "fused RNN operator" design page (Apache MXNet wiki), *Problem
+ *    Statement*: one fused operator for multi-layer, bidirectional vanilla /
+ *    LSTM / GRU networks, inference and training; *Operator Registration*:
+ *    forward intermediates are kept in a reserved workspace, reused by the
+ *    backward pass and across iterations, released with the operator.
+ *  - oneDNN issue #218 "rnn training example?": the workspace protocol (create
+ *    a forward-training descriptor, query the workspace size, allocate it,
+ *    pass it as a forward output and as a backward input); the PyTorch GRU
+ *    snippet (two biases, gate chunks r, z, n); hx/cx/hy/cy shaped
+ *    (num_layers*num_directions, batch, hidden); TNC input layout.
+ *  - Keras issue #3692 "Exposing Cudnn v5 RNN models": the descriptor
+ *    CudnnLSTM(num_layers, num_units, input_size).
+ *
+ * General rules for every call
+ *  - Every call returns rnn_status_t: 0 on success, a negative code otherwise.
+ *    No call throws; no call prints.
+ *  - Device pointers are plain HIP device addresses on the current device.
+ *    The caller owns and allocates every device buffer, including the
+ *    workspace.  The handle owns only host-side state and never allocates
+ *    device memory.
+ *  - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *    Compute calls only enqueue work on that stream and return; device-side
+ *    faults surface at the next synchronisation.  A bounded wait inside the
+ *    persistent kernels that expires (for example when another process keeps
+ *    CUs busy so that the kernel's workgroups cannot all be resident) sets an
+ *    error word in the workspace, makes every workgroup exit, and is reported
+ *    by rnn_device_status().
+ *  - All floating-point activations are fp32.  Matrices are fp32 or bf16
+ *    (rnn_wtype_t); biases are always fp32; weight gradients are always fp32.
+ *  - Calls on one handle are not thread-safe; distinct handles are
+ *    independent.  Two calls that share a workspace must not run
+ *    concurrently.
+ */
+#ifndef RNN_MI355X_H
+#define RNN_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct rnn_desc* rnn_handle_t;
+typedef int rnn_status_t;
+
+typedef enum {
+  RNN_TANH = 0, /* h' = tanh(W_ih x + b_ih + W_hh h + b_hh) */
+  RNN_LSTM = 1, /* gates i, f, g, o in this memory order */
+  RNN_GRU = 2   /* gates r, z, n; n = tanh(W_in x + b_in + r*(W_hn h + b_hn)) */
+} rnn_mode_t;
+
+typedef enum { RNN_W_F32 = 0, RNN_W_BF16 = 1 } rnn_wtype_t;
+
+/* Which parameter tensor of one (layer, direction), for rnn_weight_offset. */
+typedef enum { RNN_W_IH = 0, RNN_W_HH = 1, RNN_B_IH = 2, RNN_B_HH = 3 } rnn_param_t;
+
+/* Recurrent-sweep schedule (rnn_set_schedule). */
+typedef enum {
+  RNN_SCHED_AUTO = 0,       /* persistent when every workgroup fits on the GPU at once, else stepped */
+  RNN_SCHED_PERSISTENT = 1, /* one launch per sweep; error RNN_STATUS_NOT_CORESIDENT if it cannot fit */
+  RNN_SCHED_STEPPED = 2     /* one launch per time step (no device-wide waits) */
+} rnn_schedule_t;
+
+#define RNN_STATUS_SUCCESS 0
+#define RNN_STATUS_INVALID_ARG (-1)
+#define RNN_STATUS_UNSUPPORTED (-2)
+#define RNN_STATUS_WORKSPACE_TOO_SMALL (-3)
+#define RNN_STATUS_BAD_CALL_ORDER (-4)
+#define RNN_STATUS_NOT_CORESIDENT (-5)
+#define RNN_STATUS_DEVICE (-6)
+#define RNN_STATUS_DEVICE_TIMEOUT (-7)
+
+/* Create a descriptor of a stacked RNN: `num_layers` layers, `num_dirs`
+ * directions (1 or 2), layer-0 input width `input_size`, hidden width
+ * `hidden_size` per direction (the (num_layers, num_units, input_size)
+ * descriptor of Keras issue #3692 plus mode and direction count).  Layers
+ * l > 0 take the concatenation [forward | backward] of the layer below
+ * (width num_dirs*hidden_size).  Errors: INVALID_ARG for a NULL `out`,
+ * non-positive sizes, num_dirs not 1 or 2, unknown mode or wtype.  On error
+ * *out is set to NULL. */
+rnn_status_t rnn_create(rnn_handle_t* out, rnn_mode_t mode, int num_layers, int num_dirs,
+                        int input_size, int hidden_size, rnn_wtype_t wtype);
+
+/* Release the descriptor (host memory only).  NULL is accepted. */
+rnn_status_t rnn_destroy(rnn_handle_t h);
+
+/* Choose how the recurrent sweeps are launched (default RNN_SCHED_AUTO).
+ * Results are bitwise identical across schedules. */
+rnn_status_t rnn_set_schedule(rnn_handle_t h, rnn_schedule_t s);
+
+/* Bytes of the packed weight buffer (grad = 0: matrices in the handle's
+ * wtype, biases fp32) or of the packed weight-gradient buffer (grad = 1: all
+ * fp32). */
+rnn_status_t rnn_weights_size(rnn_handle_t h, int grad, size_t* bytes);
+
+/* Byte offset and element count of one parameter tensor inside the packed
+ * (grad = 0) or gradient (grad = 1) buffer.  Each tensor is stored row-major
+ * in the PyTorch layout: W_ih [G*H, I_l], W_hh [G*H, H], b_ih [G*H],
+ * b_hh [G*H], G = 1 (tanh), 4 (LSTM, rows i,f,g,o), 3 (GRU, rows r,z,n) --
+ * the chunk order of the PyTorch GRU snippet in oneDNN issue #218.  Offsets
+ * are multiples of 256 bytes.  Element type: matrices rnn_wtype_t of the
+ * handle (fp32 when grad = 1), biases fp32.  Errors: INVALID_ARG for
+ * out-of-range layer/dir/which or NULL outputs. */
+rnn_status_t rnn_weight_offset(rnn_handle_t h, int grad, int layer, int dir, rnn_param_t which,
+                               size_t* byte_offset, size_t* elem_count);
+
+/* Workspace bytes for T steps and batch B: training = 0 for
+ * rnn_forward_inference, training = 1 for the forward_training /
+ * backward_data / backward_weights sequence (the size query of the oneDNN
+ * workspace protocol).  The size depends on (handle, T, B, training) only.
+ * Errors: INVALID_ARG for T < 0, B < 0 or NULL bytes. */
+rnn_status_t rnn_workspace_size(rnn_handle_t h, int T, int B, int training, size_t* bytes);
+
+/* Forward pass without saving intermediates.
+ *   x   [T, B, I] fp32 (TNC)             y   [T, B, D*H] fp32; direction 0 in
+ *   h0  [L*D, B, H] fp32 or NULL (zeros)      columns [0,H), direction 1 in [H,2H)
+ *   c0  [L*D, B, H] fp32 or NULL; LSTM only (must be NULL otherwise)
+ *   W   packed weights (rnn_weight_offset)
+ *   hy  [L*D, B, H] or NULL (not written); cy likewise, LSTM only
+ *   ws  at least rnn_workspace_size(h, T, B, 0) bytes, 256-byte aligned
+ * Index l*D + d of h0/hy is layer l, direction d.  Direction 1 walks
+ * t = T-1 .. 0 and its hy is the state after t = 0.  T = 0 or B = 0 is
+ * valid: hy/cy are copied from h0/c0 (zeros if NULL) and y is empty.
+ * Using a workspace here invalidates a pending training sequence on the same
+ * workspace.  Errors: INVALID_ARG (NULL required pointers, c0/cy given for a
+ * non-LSTM mode, misaligned ws), WORKSPACE_TOO_SMALL, NOT_CORESIDENT (only
+ * with RNN_SCHED_PERSISTENT), DEVICE (launch failure). */
+rnn_status_t rnn_forward_inference(rnn_handle_t h, void* stream, int T, int B, const float* x,
+                                   const float* h0, const float* c0, const void* W, float* y,
+                                   float* hy, float* cy, void* ws, size_t ws_bytes);
+
+/* As rnn_forward_inference, and additionally fills the workspace (at least
+ * rnn_workspace_size(h, T, B, 1) bytes) with what backward_data reuses:
+ * post-activation gates and cell states per (layer, direction, step), GRU's
+ * W_hn h + b_hn, and every inner layer's output.  The outputs y, hy, cy are
+ * bitwise equal to rnn_forward_inference's. */
+rnn_status_t rnn_forward_training(rnn_handle_t h, void* stream, int T, int B, const float* x,
+                                  const float* h0, const float* c0, const void* W, float* y,
+                                  float* hy, float* cy, void* ws, size_t ws_bytes);
+
+/* Backward through time, data part.  Must follow rnn_forward_training on the
+ * same handle with the same T, B and workspace (else BAD_CALL_ORDER).
+ *   y    the forward's y; dy [T, B, D*H]; dhy, dcy [L*D, B, H] or NULL (zeros;
+ *        dcy LSTM only); W, h0, c0 as given to the forward.
+ *   dx   [T, B, I] written; dh0, dc0 [L*D, B, H] or NULL (not written; dc0
+ *        LSTM only).
+ * Stores the gate gradients of every layer in the workspace for
+ * rnn_backward_weights.  Same error codes as the forward. */
+rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const float* y,
+                               const float* dy, const float* dhy, const float* dcy, const void* W,
+                               const float* h0, const float* c0, float* dx, float* dh0,
+                               float* dc0, void* ws, size_t ws_bytes);
+
+/* Backward through time, weight part.  Must follow rnn_backward_data with the
+ * same T, B and workspace (else BAD_CALL_ORDER).  x, h0 and y are the
+ * forward's.  dW (rnn_weights_size(h, 1, .) bytes, layout of
+ * rnn_weight_offset with grad = 1) is OVERWRITTEN with dLoss/dW, dLoss/db.
+ * May be called again without repeating backward_data. */
+rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, const float* x,
+                                  const float* h0, const float* y, const void* ws,
+                                  size_t ws_bytes, float* dW);
+
+/* Synchronise `stream` and report whether a kernel that used `ws` hit an
+ * expired bounded wait since the workspace was last handed to a compute
+ * call: RNN_STATUS_SUCCESS or RNN_STATUS_DEVICE_TIMEOUT (or DEVICE if the
+ * synchronisation itself failed). */
+rnn_status_t rnn_device_status(rnn_handle_t h, void* stream, const void* ws, size_t ws_bytes);
+
+/* Per-kernel timing with HIP events recorded on the caller's stream around
+ * every launch (off by default; adds one event pair per launch).  Kernel ids:
+ * 0 input-projection GEMM, 1 recurrent forward sweep, 2 recurrent backward
+ * sweep, 3 dX GEMM, 4 dW GEMMs, 5 workspace fill.  rnn_profile_read
+ * synchronises, accumulates the elapsed times of finished launches and
+ * returns the launch count and total milliseconds for `kernel` since the last
+ * reset (rnn_set_profiling(h, 1) resets). */
+rnn_status_t rnn_set_profiling(rnn_handle_t h, int enable);
+rnn_status_t rnn_profile_read(rnn_handle_t h, int kernel, long long* launches, double* total_ms);
+
+/* Static text for a status code. */
+const char* rnn_status_string(rnn_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RNN_MI355X_H */

@@ -1,0 +1,786 @@
+// C ABI of the fused RNN operator: descriptor, packed-weight layout,
+// workspace plan, argument checks and launch sequence.
+//
+// The call sequence follows the workspace protocol of oneDNN issue #218 "rnn
+// training example?" (size query, caller-allocated workspace written by the
+// training forward pass and read by the backward pass) and the reserved
+// workspace of the MXNet "fused RNN operator" page (Operator Registration):
+// intermediates saved by the forward pass are reused by backward, and the
+// buffer (not its content) is reused across iterations.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "rnn.h"
+#include "rnn_common.h"
+
+using namespace rnnk;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  return std::atoi(v);
+}
+
+enum KernelId { K_GEMM_IN = 0, K_FWD = 1, K_BWD = 2, K_GEMM_DX = 3, K_GEMM_DW = 4, K_FILL = 5, K_NKERNELS = 6 };
+
+struct ProfPending {
+  hipEvent_t a, b;
+  int kernel;
+};
+
+// Recurrent launch plan for one sweep kind.
+struct SweepPlan {
+  RecConfig cfg{};
+  int U = 0, nwg = 0, groups = 0, grid = 0;
+  bool persistent = false;
+};
+
+struct Plan {
+  int T = 0, B = 0, training = 0;
+  int Bc = 0, nchunk = 0, Hp = 0;
+  bool wavefront = false;
+  SweepPlan fwd, bwd;
+  size_t off_err = 0, off_flags = 0, flags_bytes = 0;
+  size_t off_xch = 0, xch_bytes = 0;
+  size_t off_st = 0, st_bytes = 0;
+  size_t off_gx = 0, gx_bytes = 0;
+  size_t off_yin = 0, yin_slot = 0;
+  int yin_slots = 0;
+  size_t off_res = 0, res_layer = 0;
+  size_t off_dgi = 0, dg_layer = 0;
+  size_t off_dgh = 0;
+  size_t off_dy = 0, dy_slot = 0;
+  size_t total = 0;
+  rnn_status_t status = RNN_STATUS_SUCCESS;
+};
+
+}  // namespace
+
+struct rnn_desc {
+  int mode = 0, L = 0, D = 0, I = 0, H = 0, wtype = 0, G = 0;
+  int sched = RNN_SCHED_AUTO;
+  size_t wbytes = 0, dwbytes = 0;
+  std::vector<size_t> off[2][4];  // [grad][which] per layer block offset
+  // pending training sequence
+  int seq_stage = 0, seq_T = -1, seq_B = -1;
+  const void* seq_ws = nullptr;
+  // profiling
+  int prof = 0;
+  std::vector<ProfPending> pending;
+  std::vector<hipEvent_t> pool;
+  long long prof_n[K_NKERNELS] = {};
+  double prof_ms[K_NKERNELS] = {};
+};
+
+namespace {
+
+int in_width(const rnn_desc* h, int l) { return l == 0 ? h->I : h->D * h->H; }
+
+void layout_weights(rnn_desc* h) {
+  for (int grad = 0; grad < 2; ++grad) {
+    const size_t es = (grad == 0 && h->wtype == RNN_W_BF16) ? 2 : 4;
+    const size_t gh = (size_t)h->G * h->H;
+    size_t off = 0;
+    for (int w = 0; w < 4; ++w) h->off[grad][w].assign(h->L, 0);
+    for (int l = 0; l < h->L; ++l) {
+      h->off[grad][RNN_W_IH][l] = off;
+      off = align_up(off + h->D * gh * in_width(h, l) * es);
+      h->off[grad][RNN_W_HH][l] = off;
+      off = align_up(off + h->D * gh * h->H * es);
+      h->off[grad][RNN_B_IH][l] = off;
+      off = align_up(off + h->D * gh * 4);
+      h->off[grad][RNN_B_HH][l] = off;
+      off = align_up(off + h->D * gh * 4);
+    }
+    (grad ? h->dwbytes : h->wbytes) = off;
+  }
+}
+
+// Candidate kernel configurations, in order of preference.
+const RecConfig kFwdCfgs[] = {{1, 1, 8, 4}, {1, 2, 8, 4}, {1, 1, 16, 4}, {1, 2, 16, 4},
+                              {2, 2, 8, 4}, {2, 2, 16, 4}, {4, 2, 8, 8}, {1, 2, 32, 4}};
+const RecConfig kBwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 2, 16, 4}, {1, 2, 32, 4},
+                              {1, 2, 16, 8}, {1, 2, 32, 8}, {1, 1, 32, 8}};
+
+// Pick a forward configuration: units per workgroup U so that the groups fill
+// about one workgroup per CU, the gate columns of U units fit the MFMA tiles,
+// the K chunks fit the registers, and each epilogue thread owns one (row, unit).
+bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, int Hp, bool inproj, SweepPlan* sp) {
+  const int bf = h->wtype == RNN_W_BF16;
+  const int KC = bf ? 32 : 16;
+  const int GB = (h->mode == RNN_GRU && inproj) ? 4 : h->G;
+  const int nch = ((inproj ? Hp : 0) + Hp) / KC;
+  int target = std::max(1, 256 / std::max(1, groups));
+  int Umin = ceil_div(h->H, target);
+  const int Uenv = env_int("RNN_FWD_UNITS", 0);
+  if (Uenv > 0) Umin = Uenv;
+  for (const RecConfig& c : kFwdCfgs) {
+    if (c.mt != mt) continue;
+    const int Umax = std::min(16 * c.nt / GB, 64 * c.nwaves / std::max(1, Bc));
+    if (Umax < 1 || Umax < std::min(Umin, h->H)) continue;
+    if (nch > c.kpw * c.nwaves) continue;
+    int U = std::min(std::max(1, Umin), h->H);
+    if (Uenv <= 0 && U < Umax) {
+      // spread units evenly over the workgroups
+      int nwg = ceil_div(h->H, U);
+      U = ceil_div(h->H, nwg);
+    }
+    sp->cfg = c;
+    sp->U = U;
+    sp->nwg = ceil_div(h->H, U);
+    sp->groups = groups;
+    sp->grid = sp->nwg * groups;
+    return true;
+  }
+  return false;
+}
+
+bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, int Hp, SweepPlan* sp) {
+  const int bf = h->wtype == RNN_W_BF16;
+  const int KC = bf ? 32 : 16;
+  const int nch = h->G * Hp / KC;
+  int U = env_int("RNN_BWD_UNITS", 16);
+  U = std::max(1, std::min(U, h->H));
+  // keep at least ~groups*nwg <= 256 when possible
+  while (U < 16 && ceil_div(h->H, U) * groups > 256) ++U;
+  for (const RecConfig& c : kBwdCfgs) {
+    if (c.mt != mt) continue;
+    if (U > 16 * c.nt) continue;
+    if (Bc * U > 64 * c.nwaves) continue;
+    if (nch > c.kpw * c.nwaves) continue;
+    const int nwg = ceil_div(h->H, U);
+    sp->cfg = c;
+    sp->U = ceil_div(h->H, nwg);
+    sp->nwg = nwg;
+    sp->groups = groups;
+    sp->grid = nwg * groups;
+    return true;
+  }
+  return false;
+}
+
+Plan make_plan(const rnn_desc* h, int T, int B, int training) {
+  Plan p;
+  p.T = T;
+  p.B = B;
+  p.training = training;
+  const int bf = h->wtype == RNN_W_BF16;
+  const int KC = bf ? 32 : 16;
+  const size_t es = bf ? 2 : 4;
+  p.Hp = ceil_div(h->H, KC) * KC;
+  const int Bq = std::max(B, 1);
+  p.nchunk = ceil_div(Bq, 32);
+  p.Bc = ceil_div(Bq, p.nchunk);
+  const int mt = ceil_div(p.Bc, 16);
+  p.wavefront = (h->D == 1 && h->L > 1 && h->L <= kMaxLayersPerLaunch &&
+                 env_int("RNN_NO_WAVEFRONT", 0) == 0);
+  const int fl = p.wavefront ? h->L : 1;
+  if (!plan_fwd(h, mt, p.Bc, fl * h->D * p.nchunk, p.Hp, p.wavefront, &p.fwd) ||
+      !plan_bwd(h, mt, p.Bc, h->D * p.nchunk, p.Hp, &p.bwd)) {
+    p.status = RNN_STATUS_UNSUPPORTED;
+    return p;
+  }
+  // wavefront: every workgroup polls three groups' flags
+  if (p.wavefront && 3 * p.fwd.nwg > kMaxWaitFlags) p.wavefront = false;
+  if (!p.wavefront && p.fwd.groups != h->D * p.nchunk) {
+    if (!plan_fwd(h, mt, p.Bc, h->D * p.nchunk, p.Hp, false, &p.fwd)) {
+      p.status = RNN_STATUS_UNSUPPORTED;
+      return p;
+    }
+  }
+  if (p.fwd.nwg > kMaxWaitFlags || p.bwd.nwg > kMaxWaitFlags) {
+    p.status = RNN_STATUS_UNSUPPORTED;
+    return p;
+  }
+  const int sched = h->sched;
+  auto decide = [&](SweepPlan& sp, bool fwd) {
+    const int maxres = fwd ? rnn_fwd_max_resident(h->mode, bf, sp.cfg)
+                           : rnn_bwd_max_resident(h->mode, bf, sp.cfg);
+    const bool fits = maxres >= sp.grid && maxres > 0;
+    if (sched == RNN_SCHED_STEPPED) sp.persistent = false;
+    else if (sched == RNN_SCHED_PERSISTENT) {
+      sp.persistent = true;
+      if (!fits) p.status = RNN_STATUS_NOT_CORESIDENT;
+    } else sp.persistent = fits;
+  };
+  decide(p.fwd, true);
+  if (training) decide(p.bwd, false);
+
+  const size_t TB = (size_t)T * B;
+  const size_t dgh = (size_t)h->D * h->G * h->H;
+  size_t off = 0;
+  p.off_err = off;
+  off = align_up(off + 256);
+  p.off_flags = off;
+  p.flags_bytes = (size_t)std::max(p.fwd.grid, p.bwd.grid) * kFlagStride * 4;
+  off = align_up(off + p.flags_bytes);
+  p.off_xch = off;
+  size_t xf = (size_t)p.fwd.groups * 2 * p.Bc * p.Hp * es;
+  size_t xb = (size_t)p.bwd.groups * 2 * p.Bc * h->G * p.Hp * es;
+  p.xch_bytes = std::max(xf, training ? xb : (size_t)0);
+  off = align_up(off + p.xch_bytes);
+  p.off_st = off;
+  const int fl2 = p.wavefront ? h->L : 1;
+  p.st_bytes = (size_t)2 * std::max(fl2, 1) * h->D * B * h->H * 4;
+  off = align_up(off + p.st_bytes);
+  p.off_gx = off;
+  p.gx_bytes = TB * dgh * 4;
+  off = align_up(off + p.gx_bytes);
+  p.off_yin = off;
+  p.yin_slot = align_up(TB * h->D * h->H * 4);
+  if (h->L > 1) p.yin_slots = (training || p.wavefront) ? h->L - 1 : std::min(2, h->L - 1);
+  off += p.yin_slot * p.yin_slots;
+  if (training) {
+    const int R = reserve_slots(h->mode);
+    p.off_res = off;
+    p.res_layer = align_up((size_t)h->D * TB * R * h->H * 4);
+    off += p.res_layer * h->L;
+    p.off_dgi = off;
+    p.dg_layer = align_up(TB * dgh * 4);
+    off += p.dg_layer * h->L;
+    p.off_dgh = off;
+    if (h->mode == RNN_GRU) off += p.dg_layer * h->L;
+    p.off_dy = off;
+    p.dy_slot = align_up(TB * h->D * h->H * 4);
+    if (h->L > 1) off += 2 * p.dy_slot;
+  }
+  p.total = align_up(off);
+  return p;
+}
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+// ------------------------------------------------------------- profiling
+struct ProfScope {
+  rnn_desc* h;
+  hipStream_t s;
+  int k;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(rnn_desc* h_, hipStream_t s_, int k_) : h(h_), s(s_), k(k_) {
+    if (!h->prof) return;
+    a = take();
+    b = take();
+    if (a) (void)hipEventRecord(a, s);
+  }
+  hipEvent_t take() {
+    if (!h->pool.empty()) {
+      hipEvent_t e = h->pool.back();
+      h->pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  ~ProfScope() {
+    if (!h->prof || !a || !b) return;
+    (void)hipEventRecord(b, s);
+    h->pending.push_back({a, b, k});
+  }
+};
+
+void prof_collect(rnn_desc* h) {
+  for (auto& e : h->pending) {
+    if (hipEventSynchronize(e.b) == hipSuccess) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, e.a, e.b) == hipSuccess) {
+        h->prof_n[e.kernel] += 1;
+        h->prof_ms[e.kernel] += ms;
+      }
+    }
+    h->pool.push_back(e.a);
+    h->pool.push_back(e.b);
+  }
+  h->pending.clear();
+}
+
+rnn_status_t dev(hipError_t e) { return e == hipSuccess ? RNN_STATUS_SUCCESS : RNN_STATUS_DEVICE; }
+#define RNN_TRY(expr)                          \
+  do {                                         \
+    rnn_status_t st_ = (expr);                 \
+    if (st_ != RNN_STATUS_SUCCESS) return st_; \
+  } while (0)
+
+rnn_status_t fill(rnn_desc* h, hipStream_t s, std::initializer_list<std::pair<void*, size_t>> r) {
+  std::vector<void*> ps;
+  std::vector<size_t> ns;
+  for (auto& x : r) {
+    ps.push_back(x.first);
+    ns.push_back(x.second);
+  }
+  ProfScope ps_(h, s, K_FILL);
+  return dev(rnn_launch_fill(ps.data(), ns.data(), (int)ps.size(), s));
+}
+
+unsigned spin_limit() {
+  const int v = env_int("RNN_SPIN_LIMIT", 1 << 20);
+  return (unsigned)std::max(1, v);
+}
+
+const void* layer_w(const rnn_desc* h, const void* W, int which, int l) {
+  return reinterpret_cast<const char*>(W) + h->off[0][which][l];
+}
+
+// Hoisted input projection of layer l: GX[T*B, D*G*H] = in W_ih^T + b_ih + b_hh
+// (b_hh not folded into GRU's n gate, which needs it inside r*(.)).
+rnn_status_t gemm_input(rnn_desc* h, hipStream_t s, const Plan& p, int l, const float* in,
+                        const void* W, float* gx) {
+  GemmParams g{};
+  const int I_l = in_width(h, l);
+  g.M = p.T * p.B;
+  g.N = h->D * h->G * h->H;
+  g.K = I_l;
+  g.A[0] = in;
+  g.lda = I_l;
+  g.B[0] = layer_w(h, W, RNN_W_IH, l);
+  g.ldb = I_l;
+  g.n_ones = -1;
+  g.C[0] = gx;
+  g.ldc = g.N;
+  g.bias1 = reinterpret_cast<const float*>(layer_w(h, W, RNN_B_IH, l));
+  g.bias2 = reinterpret_cast<const float*>(layer_w(h, W, RNN_B_HH, l));
+  g.bias2_skip_gate = h->mode == RNN_GRU ? 2 : -1;
+  g.gh = h->G * h->H;
+  g.hh = h->H;
+  const bool bf = h->wtype == RNN_W_BF16;
+  g.a_vec = (I_l % 4 == 0) && ((uintptr_t)in % 16 == 0);
+  g.b_vec = (I_l % (bf ? 8 : 4) == 0);
+  ProfScope ps(h, s, K_GEMM_IN);
+  return dev(rnn_launch_gemm(g, bf, bf, 1, 0, EPI_BIAS, 1, s));
+}
+
+rnn_status_t check_common(const rnn_desc* h, int T, int B, const void* ws, size_t ws_bytes) {
+  if (!h) return RNN_STATUS_INVALID_ARG;
+  if (T < 0 || B < 0) return RNN_STATUS_INVALID_ARG;
+  if (ws && ((uintptr_t)ws % kAlign) != 0) return RNN_STATUS_INVALID_ARG;
+  (void)ws_bytes;
+  return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* x, const float* h0,
+                          const float* c0, const void* W, float* y, float* hy, float* cy, void* ws,
+                          size_t ws_bytes, int training) {
+  RNN_TRY(check_common(h, T, B, ws, ws_bytes));
+  if (h->mode != RNN_LSTM && (c0 || cy)) return RNN_STATUS_INVALID_ARG;
+  if (!W || !ws) return RNN_STATUS_INVALID_ARG;
+  if (T > 0 && B > 0 && (!x || !y)) return RNN_STATUS_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Plan p = make_plan(h, T, B, training);
+  if (p.status != RNN_STATUS_SUCCESS) return p.status;
+  if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
+  if (h->seq_ws == ws) h->seq_stage = 0;
+
+  RNN_TRY(fill(h, s, {{at<void>(ws, p.off_err), 256}}));
+  const size_t nstate = (size_t)h->L * h->D * B * h->H;
+  if (T == 0 || B == 0) {
+    if (hy) RNN_TRY(dev(rnn_copy_state(hy, h0, nstate, s)));
+    if (cy) RNN_TRY(dev(rnn_copy_state(cy, c0, nstate, s)));
+    if (training) {
+      h->seq_stage = 1;
+      h->seq_T = T;
+      h->seq_B = B;
+      h->seq_ws = ws;
+    }
+    return RNN_STATUS_SUCCESS;
+  }
+  const int bf = h->wtype == RNN_W_BF16;
+  float* gx = at<float>(ws, p.off_gx);
+  auto yin = [&](int l) { return at<float>(ws, p.off_yin + p.yin_slot * (size_t)((training || p.wavefront) ? l : (l % 2))); };
+  auto res = [&](int l) { return training ? at<float>(ws, p.off_res + p.res_layer * l) : nullptr; };
+
+  FwdParams f{};
+  f.T = T;
+  f.B = B;
+  f.H = h->H;
+  f.D = h->D;
+  f.nchunk = p.nchunk;
+  f.Bc = p.Bc;
+  f.U = p.fwd.U;
+  f.nwg = p.fwd.nwg;
+  f.Hp = p.Hp;
+  f.persistent = p.fwd.persistent ? 1 : 0;
+  f.training = training;
+  f.h0 = h0;
+  f.c0 = c0;
+  f.hy = hy;
+  f.cy = cy;
+  f.st_h = at<float>(ws, p.off_st);
+  f.st_c = at<float>(ws, p.off_st + p.st_bytes / 2);
+  f.xch = at<void>(ws, p.off_xch);
+  f.flags = at<unsigned>(ws, p.off_flags);
+  f.err = at<unsigned>(ws, p.off_err);
+  f.spin_limit = spin_limit();
+
+  auto run_sweep = [&](int nlayers) -> rnn_status_t {
+    f.nlayers = nlayers;
+    f.s_total = T + nlayers - 1;
+    const int grid = p.fwd.nwg * nlayers * h->D * p.nchunk;
+    RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}, {at<void>(ws, p.off_xch), p.xch_bytes}}));
+    if (f.persistent) {
+      f.s_begin = -1;
+      f.s_end = f.s_total;
+      ProfScope ps(h, s, K_FWD);
+      return dev(rnn_launch_fwd(f, h->mode, bf, p.fwd.cfg, grid, s));
+    }
+    for (int st = -1; st < f.s_total; ++st) {
+      f.s_begin = st;
+      f.s_end = st + 1;
+      ProfScope ps(h, s, K_FWD);
+      RNN_TRY(dev(rnn_launch_fwd(f, h->mode, bf, p.fwd.cfg, grid, s)));
+    }
+    return RNN_STATUS_SUCCESS;
+  };
+
+  if (p.wavefront) {
+    RNN_TRY(gemm_input(h, s, p, 0, x, W, gx));
+    f.wavefront = 1;
+    f.first_layer = 0;
+    f.gx = gx;
+    for (int l = 0; l < h->L; ++l) {
+      f.w_ih[l] = layer_w(h, W, RNN_W_IH, l);
+      f.w_hh[l] = layer_w(h, W, RNN_W_HH, l);
+      f.b_ih[l] = reinterpret_cast<const float*>(layer_w(h, W, RNN_B_IH, l));
+      f.b_hh[l] = reinterpret_cast<const float*>(layer_w(h, W, RNN_B_HH, l));
+      f.in_l[l] = in_width(h, l);
+      f.y[l] = (l == h->L - 1) ? y : yin(l);
+      f.reserve[l] = res(l);
+    }
+    RNN_TRY(run_sweep(h->L));
+  } else {
+    f.wavefront = 0;
+    for (int l = 0; l < h->L; ++l) {
+      const float* in = (l == 0) ? x : yin(l - 1);
+      RNN_TRY(gemm_input(h, s, p, l, in, W, gx));
+      f.first_layer = l;
+      f.gx = gx;
+      f.w_ih[0] = layer_w(h, W, RNN_W_IH, l);
+      f.w_hh[0] = layer_w(h, W, RNN_W_HH, l);
+      f.b_ih[0] = reinterpret_cast<const float*>(layer_w(h, W, RNN_B_IH, l));
+      f.b_hh[0] = reinterpret_cast<const float*>(layer_w(h, W, RNN_B_HH, l));
+      f.in_l[0] = in_width(h, l);
+      f.y[0] = (l == h->L - 1) ? y : yin(l);
+      f.reserve[0] = res(l);
+      RNN_TRY(run_sweep(1));
+    }
+  }
+  if (training) {
+    h->seq_stage = 1;
+    h->seq_T = T;
+    h->seq_B = B;
+    h->seq_ws = ws;
+  }
+  return RNN_STATUS_SUCCESS;
+}
+
+}  // namespace
+
+// ================================================================== C ABI
+extern "C" {
+
+rnn_status_t rnn_create(rnn_handle_t* out, rnn_mode_t mode, int num_layers, int num_dirs,
+                        int input_size, int hidden_size, rnn_wtype_t wtype) {
+  if (!out) return RNN_STATUS_INVALID_ARG;
+  *out = nullptr;
+  if (mode != RNN_TANH && mode != RNN_LSTM && mode != RNN_GRU) return RNN_STATUS_INVALID_ARG;
+  if (wtype != RNN_W_F32 && wtype != RNN_W_BF16) return RNN_STATUS_INVALID_ARG;
+  if (num_layers <= 0 || input_size <= 0 || hidden_size <= 0) return RNN_STATUS_INVALID_ARG;
+  if (num_dirs != 1 && num_dirs != 2) return RNN_STATUS_INVALID_ARG;
+  rnn_desc* h = new (std::nothrow) rnn_desc();
+  if (!h) return RNN_STATUS_INVALID_ARG;
+  h->mode = mode;
+  h->L = num_layers;
+  h->D = num_dirs;
+  h->I = input_size;
+  h->H = hidden_size;
+  h->wtype = wtype;
+  h->G = gates_of(mode);
+  layout_weights(h);
+  *out = h;
+  return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_destroy(rnn_handle_t h) {
+  if (!h) return RNN_STATUS_SUCCESS;
+  prof_collect(h);
+  for (hipEvent_t e : h->pool) (void)hipEventDestroy(e);
+  delete h;
+  return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_set_schedule(rnn_handle_t h, rnn_schedule_t s) {
+  if (!h || (s != RNN_SCHED_AUTO && s != RNN_SCHED_PERSISTENT && s != RNN_SCHED_STEPPED))
+    return RNN_STATUS_INVALID_ARG;
+  h->sched = s;
+  return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_weights_size(rnn_handle_t h, int grad, size_t* bytes) {
+  if (!h || !bytes) return RNN_STATUS_INVALID_ARG;
+  *bytes = grad ? h->dwbytes : h->wbytes;
+  return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_weight_offset(rnn_handle_t h, int grad, int layer, int dir, rnn_param_t which,
+                               size_t* byte_offset, size_t* elem_count) {
+  if (!h || !byte_offset || !elem_count) return RNN_STATUS_INVALID_ARG;
+  if (layer < 0 || layer >= h->L || dir < 0 || dir >= h->D) return RNN_STATUS_INVALID_ARG;
+  if (which < RNN_W_IH || which > RNN_B_HH) return RNN_STATUS_INVALID_ARG;
+  const int g = grad ? 1 : 0;
+  const size_t es = (which <= RNN_W_HH && !g && h->wtype == RNN_W_BF16) ? 2 : 4;
+  const size_t gh = (size_t)h->G * h->H;
+  size_t count = gh;
+  if (which == RNN_W_IH) count = gh * in_width(h, layer);
+  if (which == RNN_W_HH) count = gh * h->H;
+  *elem_count = count;
+  *byte_offset = h->off[g][which][layer] + (size_t)dir * count * es;
+  return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_workspace_size(rnn_handle_t h, int T, int B, int training, size_t* bytes) {
+  if (!h || !bytes || T < 0 || B < 0) return RNN_STATUS_INVALID_ARG;
+  Plan p = make_plan(h, T, B, training ? 1 : 0);
+  if (p.status == RNN_STATUS_UNSUPPORTED) return p.status;
+  *bytes = p.total;
+  return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_forward_inference(rnn_handle_t h, void* stream, int T, int B, const float* x,
+                                   const float* h0, const float* c0, const void* W, float* y,
+                                   float* hy, float* cy, void* ws, size_t ws_bytes) {
+  return forward_impl(h, stream, T, B, x, h0, c0, W, y, hy, cy, ws, ws_bytes, 0);
+}
+
+rnn_status_t rnn_forward_training(rnn_handle_t h, void* stream, int T, int B, const float* x,
+                                  const float* h0, const float* c0, const void* W, float* y,
+                                  float* hy, float* cy, void* ws, size_t ws_bytes) {
+  return forward_impl(h, stream, T, B, x, h0, c0, W, y, hy, cy, ws, ws_bytes, 1);
+}
+
+rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const float* y,
+                               const float* dy, const float* dhy, const float* dcy, const void* W,
+                               const float* h0, const float* c0, float* dx, float* dh0,
+                               float* dc0, void* ws, size_t ws_bytes) {
+  RNN_TRY(check_common(h, T, B, ws, ws_bytes));
+  if (h->mode != RNN_LSTM && (dcy || dc0 || c0)) return RNN_STATUS_INVALID_ARG;
+  if (!W || !ws) return RNN_STATUS_INVALID_ARG;
+  if (T > 0 && B > 0 && (!y || !dy || !dx)) return RNN_STATUS_INVALID_ARG;
+  if (h->seq_stage < 1 || h->seq_ws != ws || h->seq_T != T || h->seq_B != B)
+    return RNN_STATUS_BAD_CALL_ORDER;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Plan p = make_plan(h, T, B, 1);
+  if (p.status != RNN_STATUS_SUCCESS) return p.status;
+  if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
+  RNN_TRY(fill(h, s, {{at<void>(ws, p.off_err), 256}}));
+  const size_t nstate = (size_t)h->L * h->D * B * h->H;
+  if (T == 0 || B == 0) {
+    if (dh0) RNN_TRY(dev(rnn_copy_state(dh0, dhy, nstate, s)));
+    if (dc0) RNN_TRY(dev(rnn_copy_state(dc0, dcy, nstate, s)));
+    h->seq_stage = 2;
+    return RNN_STATUS_SUCCESS;
+  }
+  const int bf = h->wtype == RNN_W_BF16;
+  const size_t lstride = (size_t)h->D * B * h->H;
+  const size_t dgh = (size_t)h->D * h->G * h->H;
+  auto yl = [&](int l) -> const float* {
+    return l == h->L - 1 ? y : at<float>(ws, p.off_yin + p.yin_slot * (size_t)l);
+  };
+  auto dyslot = [&](int i) { return at<float>(ws, p.off_dy + p.dy_slot * (size_t)(i % 2)); };
+  BwdParams b{};
+  b.T = T;
+  b.B = B;
+  b.H = h->H;
+  b.D = h->D;
+  b.nchunk = p.nchunk;
+  b.Bc = p.Bc;
+  b.U = p.bwd.U;
+  b.nwg = p.bwd.nwg;
+  b.Hp = p.Hp;
+  b.persistent = p.bwd.persistent ? 1 : 0;
+  b.st_dh = at<float>(ws, p.off_st);
+  b.st_dc = at<float>(ws, p.off_st + p.st_bytes / 2);
+  b.xch = at<void>(ws, p.off_xch);
+  b.flags = at<unsigned>(ws, p.off_flags);
+  b.err = at<unsigned>(ws, p.off_err);
+  b.spin_limit = spin_limit();
+  for (int l = h->L - 1; l >= 0; --l) {
+    b.w_hh = layer_w(h, W, RNN_W_HH, l);
+    b.reserve = at<float>(ws, p.off_res + p.res_layer * l);
+    b.y = yl(l);
+    b.h0 = h0 ? h0 + l * lstride : nullptr;
+    b.c0 = c0 ? c0 + l * lstride : nullptr;
+    b.dy = (l == h->L - 1) ? dy : dyslot(l);
+    b.dhy = dhy ? dhy + l * lstride : nullptr;
+    b.dcy = dcy ? dcy + l * lstride : nullptr;
+    b.dgi = at<float>(ws, p.off_dgi + p.dg_layer * l);
+    b.dgh = h->mode == RNN_GRU ? at<float>(ws, p.off_dgh + p.dg_layer * l) : nullptr;
+    b.dh0 = dh0 ? dh0 + l * lstride : nullptr;
+    b.dc0 = dc0 ? dc0 + l * lstride : nullptr;
+    RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}, {at<void>(ws, p.off_xch), p.xch_bytes}}));
+    if (b.persistent) {
+      b.s_begin = 0;
+      b.s_end = T + 1;
+      ProfScope ps(h, s, K_BWD);
+      RNN_TRY(dev(rnn_launch_bwd(b, h->mode, bf, p.bwd.cfg, p.bwd.grid, s)));
+    } else {
+      for (int st = 0; st <= T; ++st) {
+        b.s_begin = st;
+        b.s_end = st + 1;
+        ProfScope ps(h, s, K_BWD);
+        RNN_TRY(dev(rnn_launch_bwd(b, h->mode, bf, p.bwd.cfg, p.bwd.grid, s)));
+      }
+    }
+    // dX_l = dG_i W_ih  (both directions in one product, K = D*G*H)
+    GemmParams g{};
+    const int I_l = in_width(h, l);
+    g.M = T * B;
+    g.N = I_l;
+    g.K = (int)dgh;
+    g.A[0] = b.dgi;
+    g.lda = (long long)dgh;
+    g.B[0] = layer_w(h, W, RNN_W_IH, l);
+    g.ldb = I_l;
+    g.n_ones = -1;
+    g.C[0] = (l == 0) ? dx : dyslot(l - 1);
+    g.ldc = I_l;
+    g.a_vec = (dgh % 4 == 0);
+    g.b_vec = (I_l % (bf ? 8 : 4) == 0);
+    ProfScope ps(h, s, K_GEMM_DX);
+    RNN_TRY(dev(rnn_launch_gemm(g, bf, bf, 1, 1, EPI_STORE, 1, s)));
+  }
+  h->seq_stage = 2;
+  return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, const float* x,
+                                  const float* h0, const float* y, const void* ws,
+                                  size_t ws_bytes, float* dW) {
+  RNN_TRY(check_common(h, T, B, ws, ws_bytes));
+  if (!ws || !dW) return RNN_STATUS_INVALID_ARG;
+  if (T > 0 && B > 0 && (!x || !y)) return RNN_STATUS_INVALID_ARG;
+  if (h->seq_stage < 2 || h->seq_ws != ws || h->seq_T != T || h->seq_B != B)
+    return RNN_STATUS_BAD_CALL_ORDER;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Plan p = make_plan(h, T, B, 1);
+  if (p.status != RNN_STATUS_SUCCESS) return p.status;
+  if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
+  void* wsm = const_cast<void*>(ws);
+  if (T == 0 || B == 0) return fill(h, s, {{dW, h->dwbytes}});
+  const int bf = h->wtype == RNN_W_BF16;
+  const size_t lstride = (size_t)h->D * B * h->H;
+  const int GH = h->G * h->H;
+  const int dgh = h->D * GH;
+  auto yl = [&](int l) -> const float* {
+    return l == h->L - 1 ? y : at<float>(wsm, p.off_yin + p.yin_slot * (size_t)l);
+  };
+  char* dWb = reinterpret_cast<char*>(dW);
+  for (int l = 0; l < h->L; ++l) {
+    const int I_l = in_width(h, l);
+    const float* X = (l == 0) ? x : yl(l - 1);
+    const float* dgi = at<float>(wsm, p.off_dgi + p.dg_layer * l);
+    const float* dghp = h->mode == RNN_GRU ? at<float>(wsm, p.off_dgh + p.dg_layer * l) : dgi;
+    {  // dW_ih | db_ih = dG_i^T [X | 1]
+      GemmParams g{};
+      g.M = dgh;
+      g.N = I_l + 1;
+      g.K = T * B;
+      g.A[0] = dgi;
+      g.lda = dgh;
+      g.B[0] = X;
+      g.ldb = I_l;
+      g.b_alt_k0[0] = g.b_alt_k1[0] = 0;
+      g.n_ones = I_l;
+      g.C[0] = reinterpret_cast<float*>(dWb + h->off[1][RNN_W_IH][l]);
+      g.ldc = I_l;
+      g.cbias[0] = reinterpret_cast<float*>(dWb + h->off[1][RNN_B_IH][l]);
+      g.a_vec = (dgh % 4 == 0);
+      g.b_vec = (I_l % 4 == 0) && ((uintptr_t)X % 16 == 0);
+      ProfScope ps(h, s, K_GEMM_DW);
+      RNN_TRY(dev(rnn_launch_gemm(g, bf, 0, 0, 1, EPI_DW, 1, s)));
+    }
+    {  // dW_hh | db_hh = dG_h^T [H_prev | 1], per direction
+      GemmParams g{};
+      g.M = GH;
+      g.N = h->H + 1;
+      g.K = T * B;
+      g.lda = dgh;
+      g.ldb = (long long)h->D * h->H;
+      g.ld_alt = h->H;
+      g.n_ones = h->H;
+      g.ldc = h->H;
+      for (int d = 0; d < h->D; ++d) {
+        g.A[d] = dghp + (size_t)d * GH;
+        g.B[d] = yl(l) + (size_t)d * h->H;
+        g.b_shift[d] = d == 0 ? -B : B;
+        g.b_alt_k0[d] = d == 0 ? 0 : (T - 1) * B;
+        g.b_alt_k1[d] = g.b_alt_k0[d] + B;
+        g.b_alt[d] = h0 ? h0 + l * lstride + (size_t)d * B * h->H : nullptr;
+        g.C[d] = reinterpret_cast<float*>(dWb + h->off[1][RNN_W_HH][l]) + (size_t)d * GH * h->H;
+        g.cbias[d] = reinterpret_cast<float*>(dWb + h->off[1][RNN_B_HH][l]) + (size_t)d * GH;
+      }
+      g.a_vec = (dgh % 4 == 0) && (GH % 4 == 0);
+      g.b_vec = ((h->D * h->H) % 4 == 0) && (h->H % 4 == 0) && ((uintptr_t)yl(l) % 16 == 0) &&
+                (!h0 || (uintptr_t)h0 % 16 == 0);
+      ProfScope ps(h, s, K_GEMM_DW);
+      RNN_TRY(dev(rnn_launch_gemm(g, bf, 0, 0, 1, EPI_DW, h->D, s)));
+    }
+  }
+  return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_device_status(rnn_handle_t h, void* stream, const void* ws, size_t ws_bytes) {
+  if (!h || !ws || ws_bytes < 256) return RNN_STATUS_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return RNN_STATUS_DEVICE;
+  unsigned err = 0;
+  if (hipMemcpy(&err, ws, sizeof(err), hipMemcpyDeviceToHost) != hipSuccess) return RNN_STATUS_DEVICE;
+  return err ? RNN_STATUS_DEVICE_TIMEOUT : RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_set_profiling(rnn_handle_t h, int enable) {
+  if (!h) return RNN_STATUS_INVALID_ARG;
+  prof_collect(h);
+  h->prof = enable ? 1 : 0;
+  for (int k = 0; k < K_NKERNELS; ++k) {
+    h->prof_n[k] = 0;
+    h->prof_ms[k] = 0.0;
+  }
+  return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_profile_read(rnn_handle_t h, int kernel, long long* launches, double* total_ms) {
+  if (!h || kernel < 0 || kernel >= K_NKERNELS || !launches || !total_ms) return RNN_STATUS_INVALID_ARG;
+  prof_collect(h);
+  *launches = h->prof_n[kernel];
+  *total_ms = h->prof_ms[kernel];
+  return RNN_STATUS_SUCCESS;
+}
+
+const char* rnn_status_string(rnn_status_t s) {
+  switch (s) {
+    case RNN_STATUS_SUCCESS: return "success";
+    case RNN_STATUS_INVALID_ARG: return "invalid argument";
+    case RNN_STATUS_UNSUPPORTED: return "unsupported configuration";
+    case RNN_STATUS_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RNN_STATUS_BAD_CALL_ORDER: return "bad call order (backward needs the matching forward_training)";
+    case RNN_STATUS_NOT_CORESIDENT: return "persistent schedule cannot keep every workgroup resident";
+    case RNN_STATUS_DEVICE: return "HIP runtime error";
+    case RNN_STATUS_DEVICE_TIMEOUT: return "bounded device wait expired";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// Shared host/device definitions of the fused RNN library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rnnk {
+
+constexpr int kMaxLayersPerLaunch = 8;   // layers resident in one wavefront launch
+constexpr int kFlagStride = 32;          // u32 per flag slot (128 bytes)
+constexpr int kMaxWaitFlags = 512;       // flags one workgroup may poll per step
+constexpr int kWaitPerLane = kMaxWaitFlags / 64;
+
+enum Mode { MODE_TANH = 0, MODE_LSTM = 1, MODE_GRU = 2 };
+
+// Reserve slots per (layer, direction, step, batch row, unit):
+//   LSTM: i f g o c     GRU: r z n gh_n     tanh: none
+__host__ __device__ constexpr int reserve_slots(int mode) {
+  return mode == MODE_LSTM ? 5 : (mode == MODE_GRU ? 4 : 0);
+}
+__host__ __device__ constexpr int gates_of(int mode) {
+  return mode == MODE_LSTM ? 4 : (mode == MODE_GRU ? 3 : 1);
+}
+
+// ------------------------------------------------------------------ GEMM
+// C[m, n] = sum_k A(m, k) * B(k, n)   (batched over blockIdx.z < 2)
+//   A fp32: a_kmajor ? A[m*lda + k] : A[k*lda + m]
+//   B (fp32 or bf16): b_kn ? B[k*ldb + n] : B[n*ldb + k]
+//   B rows may be remapped (KN only): row k reads row k + b_shift, except
+//   rows in [b_alt_k0, b_alt_k1) which read b_alt[(k - b_alt_k0)*ld_alt + n]
+//   (zero if b_alt is null).  Column n == n_ones of B is all ones.
+// Epilogue: EPI_STORE  C[m*ldc + n] = acc
+//           EPI_BIAS   C[m*ldc + n] = acc + bias1[n] + bias2[n] (bias2 skipped
+//                      for columns whose gate (n % gh) / hh == bias2_skip_gate)
+//           EPI_DW     n == n_ones ? cbias[m] = acc : C[m*ldc + n] = acc
+enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_DW = 2 };
+
+struct GemmParams {
+  int M, N, K;
+  const float* A[2];
+  long long lda;
+  const void* B[2];
+  long long ldb;
+  int b_shift[2], b_alt_k0[2], b_alt_k1[2];
+  const float* b_alt[2];
+  long long ld_alt;
+  int n_ones;
+  float* C[2];
+  long long ldc;
+  float* cbias[2];
+  const float* bias1;
+  const float* bias2;
+  int bias2_skip_gate, gh, hh;
+  int a_vec, b_vec;   // 1: 16-byte vector loads are legal (aligned bases and strides)
+};
+
+// ------------------------------------------------------------- recurrence
+// One forward launch covers `nlayers` layers (a wavefront when > 1) or one
+// layer with both directions; groups are (layer, direction, batch chunk);
+// each group has `nwg` workgroups owning `U` hidden units each.
+struct FwdParams {
+  int T, B, H, D;
+  int nlayers;            // layers in this launch
+  int nchunk, Bc;         // batch chunks of Bc rows
+  int U, nwg;             // units per workgroup, workgroups per group
+  int Hp;                 // padded exchange row (multiple of the MFMA K chunk)
+  int s_begin, s_end;     // global steps [s_begin, s_end); -1 is the prologue
+  int s_total;            // T + nlayers - 1
+  int persistent, training, wavefront;
+  int first_layer;        // index of layer 0 of this launch in the network
+  const void* w_ih[kMaxLayersPerLaunch];   // layer block [D*G*H, I_l]
+  const void* w_hh[kMaxLayersPerLaunch];   // layer block [D*G*H, H]
+  const float* b_ih[kMaxLayersPerLaunch];  // [D*G*H]
+  const float* b_hh[kMaxLayersPerLaunch];
+  int in_l[kMaxLayersPerLaunch];           // input width of each layer
+  const float* gx;        // hoisted projection of the launch's first layer [T*B, D*G*H]
+  float* y[kMaxLayersPerLaunch];           // [T, B, D*H]
+  float* reserve[kMaxLayersPerLaunch];     // [D][T][B][R][H] (training)
+  const float* h0;        // [L*D, B, H] of the whole network, or null
+  const float* c0;
+  float* hy;
+  float* cy;
+  float* st_h;            // carried state between stepped launches [nlayers*D][B][H]
+  float* st_c;
+  void* xch;              // exchange buffers: per group [2][Bc][Hp] (element type of the path)
+  unsigned* flags;        // per workgroup, kFlagStride apart
+  unsigned* err;
+  unsigned spin_limit;
+};
+
+struct BwdParams {
+  int T, B, H, D;
+  int nchunk, Bc, U, nwg, Hp;
+  int s_begin, s_end;     // processing steps; s == T is the final dh0 phase
+  int persistent;
+  const void* w_hh;       // layer block [D*G*H, H]
+  const float* reserve;   // [D][T][B][R][H]
+  const float* y;         // layer output [T, B, D*H]
+  const float* h0;        // this layer's rows [D, B, H] or null
+  const float* c0;
+  const float* dy;        // [T, B, D*H]
+  const float* dhy;       // [D, B, H] or null
+  const float* dcy;
+  float* dgi;             // [T*B, D*G*H]
+  float* dgh;             // GRU only: [T*B, D*G*H]
+  float* dh0;             // [D, B, H] or null
+  float* dc0;
+  float* st_dh;           // carries between stepped launches [D*nchunk... ] laid out [D][B][H]
+  float* st_dc;
+  void* xch;              // per group [2][Bc][G*Hp]
+  unsigned* flags;
+  unsigned* err;
+  unsigned spin_limit;
+};
+
+}  // namespace rnnk
+
+// Kernel configuration chosen by the host planner.
+struct RecConfig {
+  int nt;      // 16-column MFMA tiles per workgroup
+  int mt;      // 16-row batch tiles (Bc <= 16*mt)
+  int kpw;     // K chunks per wave held in registers (upper bound)
+  int nwaves;  // waves per workgroup
+};
+
+// Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
+hipError_t rnn_launch_gemm(const rnnk::GemmParams& p, int bf16_compute, int b_bf16, int a_kmajor,
+                           int b_kn, int epi, int batches, hipStream_t s);
+hipError_t rnn_launch_fwd(const rnnk::FwdParams& p, int mode, int bf16, const RecConfig& c,
+                          int grid, hipStream_t s);
+hipError_t rnn_launch_bwd(const rnnk::BwdParams& p, int mode, int bf16, const RecConfig& c,
+                          int grid, hipStream_t s);
+hipError_t rnn_launch_fill(void* const* ptrs, const size_t* bytes, int n, hipStream_t s);
+hipError_t rnn_copy_state(float* dst, const float* src, size_t n, hipStream_t s);
+// Maximum co-resident workgroups of the fwd/bwd kernel for this config (0 if unsupported).
+int rnn_fwd_max_resident(int mode, int bf16, const RecConfig& c);
+int rnn_bwd_max_resident(int mode, int bf16, const RecConfig& c);
+bool rnn_fwd_config_supported(int mode, int bf16, const RecConfig& c);
+bool rnn_bwd_config_supported(int mode, int bf16, const RecConfig& c);

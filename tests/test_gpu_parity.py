@@ -1,0 +1,218 @@
+"""GPU (HIP path, through the C ABI) vs the fp64 oracle, element by element.
+
+Tolerances (normwise max relative error per output tensor, ||g - o||_inf /
+||o||_inf): fp32 path 1e-4 on y/hy/cy and 1e-3 on every gradient; bf16-weight
+path (bf16 matrices and bf16-rounded MFMA operands, fp32 accumulation and
+state) 2e-2.
+"""
+
+import itertools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import layer_rnn_forward_amd as R
+from layer_rnn_forward_amd import synth
+from tests.gpu_harness import check, compare, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-4, 1e-3), "bf16": (2e-2, 2e-2)}
+MODES = ("rnn_tanh", "lstm", "gru")
+
+
+def _case(mode, L, D, T, B, I, H, wtype, seed=11, scale=None):
+    return synth.make_case(mode, L, D, T, B, I, H, wtype=wtype, seed=seed, state_std=0.5,
+                           with_state_grads=True, scale=scale)
+
+
+def _announce(*a):
+    print("CASE", *a, flush=True)
+    sys.stdout.flush()
+
+
+def test_small_lstm_workload():
+    """The T=16 B=4 I=H=32 fp32 LSTM workload, full training sequence."""
+    w = synth.WORKLOADS["lstm_small_f32"]
+    _announce(w)
+    case = synth.make_workload(w, with_state_grads=True)
+    g = run_gpu("lstm", 1, 1, case, "f32")
+    o = run_oracle("lstm", 1, 1, case)
+    errs = compare(g, o, "lstm", 1, 1)
+    print(errs)
+    check(errs, *TOL["f32"])
+
+
+@pytest.mark.parametrize("mode,L,D,wtype", list(itertools.product(MODES, (1, 2), (1, 2), ("f32", "bf16"))))
+def test_ragged_parity(mode, L, D, wtype):
+    """Ragged sizes: H not a multiple of the MFMA chunk, odd input width,
+    batch not a multiple of 16, several tiles of the time-parallel GEMMs."""
+    T, B, I, H = 9, 19, 37, 40
+    _announce(mode, L, D, wtype, T, B, I, H)
+    case = _case(mode, L, D, T, B, I, H, wtype)
+    g = run_gpu(mode, L, D, case, wtype)
+    o = run_oracle(mode, L, D, case)
+    errs = compare(g, o, mode, L, D)
+    check(errs, *TOL[wtype])
+
+
+@pytest.mark.parametrize("mode,wtype", list(itertools.product(MODES, ("f32", "bf16"))))
+def test_multi_chunk_batch(mode, wtype):
+    """B > 32 splits the batch into independent recurrence groups."""
+    T, B, I, H = 6, 45, 24, 48
+    _announce(mode, wtype, T, B, I, H)
+    case = _case(mode, 2, 2, T, B, I, H, wtype, seed=5)
+    g = run_gpu(mode, 2, 2, case, wtype)
+    o = run_oracle(mode, 2, 2, case)
+    check(compare(g, o, mode, 2, 2), *TOL[wtype])
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_wavefront_stack(mode):
+    """Unidirectional 3-layer stack (layer wavefront in one launch)."""
+    T, B, I, H = 12, 7, 20, 64
+    _announce(mode, T, B, I, H)
+    case = _case(mode, 3, 1, T, B, I, H, "f32", seed=9)
+    g = run_gpu(mode, 3, 1, case, "f32")
+    o = run_oracle(mode, 3, 1, case)
+    check(compare(g, o, mode, 3, 1), *TOL["f32"])
+
+
+@pytest.mark.parametrize("mode,wtype", list(itertools.product(MODES, ("f32", "bf16"))))
+def test_schedules_bitwise_equal(mode, wtype):
+    """Persistent and stepped schedules give bitwise identical results, and
+    inference equals the training forward bitwise."""
+    T, B, I, H = 8, 10, 16, 48
+    _announce(mode, wtype)
+    case = _case(mode, 2, 2, T, B, I, H, wtype, seed=3)
+    a = run_gpu(mode, 2, 2, case, wtype, sched=R.SCHED_PERSISTENT)
+    b = run_gpu(mode, 2, 2, case, wtype, sched=R.SCHED_STEPPED)
+    c = run_gpu(mode, 2, 2, case, wtype, sched=R.SCHED_PERSISTENT, training=False)
+    for k in ("y", "hy", "dx", "dh0"):
+        assert np.array_equal(a[k], b[k]), k
+    for k in ("y", "hy"):
+        assert np.array_equal(a[k], c[k]), k
+    for l in range(2):
+        for d in range(2):
+            for n in a["dW"][l][d]:
+                assert np.array_equal(a["dW"][l][d][n], b["dW"][l][d][n]), (l, d, n)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_run_to_run_deterministic(mode):
+    T, B, I, H = 10, 20, 32, 64
+    case = _case(mode, 1, 2, T, B, I, H, "bf16", seed=4)
+    a = run_gpu(mode, 1, 2, case, "bf16")
+    b = run_gpu(mode, 1, 2, case, "bf16")
+    for k in a:
+        if k != "dW":
+            assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_null_states_and_grads(mode):
+    """h0/c0 = NULL means zeros, dhy/dcy = NULL means zeros."""
+    T, B, I, H = 5, 3, 8, 16
+    case = _case(mode, 2, 2, T, B, I, H, "f32", seed=12)
+    g = run_gpu(mode, 2, 2, case, "f32", pass_state=False, pass_grads=False)
+    o = run_oracle(mode, 2, 2, case, pass_state=False, pass_grads=False)
+    check(compare(g, o, mode, 2, 2), *TOL["f32"])
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_single_step_single_row(mode):
+    T, B, I, H = 1, 1, 3, 5
+    case = _case(mode, 2, 2, T, B, I, H, "f32", seed=13)
+    g = run_gpu(mode, 2, 2, case, "f32")
+    o = run_oracle(mode, 2, 2, case)
+    check(compare(g, o, mode, 2, 2), *TOL["f32"])
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_empty_sequence_and_batch(mode):
+    """T = 0: hy = h0, y empty; backward: dh0 = dhy, dW = 0.  B = 0: nothing."""
+    H, I, L, D = 8, 4, 2, 2
+    h = R.rnn_create(mode, L, D, I, H, "f32")
+    W = R.pack_weights(h, synth.make_params(mode, L, D, I, H, "f32", 1))
+    for T, B in ((0, 3), (4, 0), (0, 0)):
+        ws = torch.empty(max(R.rnn_workspace_size(h, T, B, 1), 256), dtype=torch.uint8, device="cuda")
+        x = torch.zeros((T, B, I), device="cuda")
+        h0 = torch.randn((L * D, B, H), device="cuda")
+        c0 = torch.randn((L * D, B, H), device="cuda") if mode == "lstm" else None
+        y = torch.zeros((T, B, D * H), device="cuda")
+        hy = torch.full((L * D, B, H), float("nan"), device="cuda")
+        cy = torch.full((L * D, B, H), float("nan"), device="cuda") if mode == "lstm" else None
+        R.rnn_forward_training(h, T, B, x, h0, c0, W, y, hy, cy, ws)
+        torch.cuda.synchronize()
+        if T == 0:
+            assert torch.equal(hy, h0)
+            if mode == "lstm":
+                assert torch.equal(cy, c0)
+        dhy = torch.randn((L * D, B, H), device="cuda")
+        dh0 = torch.full((L * D, B, H), float("nan"), device="cuda")
+        dx = torch.zeros((T, B, I), device="cuda")
+        R.rnn_backward_data(h, T, B, y, torch.zeros_like(y), dhy, None, W, h0, c0, dx, dh0, None, ws)
+        dW = torch.full((R.rnn_weights_size(h, 1) // 4,), float("nan"), device="cuda")
+        R.rnn_backward_weights(h, T, B, x, h0, y, ws, dW)
+        torch.cuda.synchronize()
+        if T == 0:
+            assert torch.equal(dh0, dhy)
+        assert torch.count_nonzero(dW) == 0
+    R.rnn_destroy(h)
+
+
+def test_call_order_and_workspace_errors():
+    h = R.rnn_create("lstm", 1, 1, 8, 16, "f32")
+    W = R.pack_weights(h, synth.make_params("lstm", 1, 1, 8, 16, "f32", 2))
+    T, B = 4, 2
+    x = torch.randn((T, B, 8), device="cuda")
+    y = torch.zeros((T, B, 16), device="cuda")
+    need = R.rnn_workspace_size(h, T, B, 1)
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(R.RNNError) as e:
+        R.rnn_forward_training(h, T, B, x, None, None, W, y, None, None, small)
+    assert e.value.status == -3
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    dx = torch.zeros_like(x)
+    with pytest.raises(R.RNNError) as e:
+        R.rnn_backward_data(h, T, B, y, y, None, None, W, None, None, dx, None, None, ws)
+    assert e.value.status == -4
+    R.rnn_forward_training(h, T, B, x, None, None, W, y, None, None, ws)
+    dW = torch.zeros((R.rnn_weights_size(h, 1) // 4,), device="cuda")
+    with pytest.raises(R.RNNError) as e:
+        R.rnn_backward_weights(h, T, B, x, None, y, ws, dW)
+    assert e.value.status == -4
+    with pytest.raises(R.RNNError) as e:   # different T than the forward
+        R.rnn_backward_data(h, T - 1, B, y, y, None, None, W, None, None, dx, None, None, ws)
+    assert e.value.status == -4
+    R.rnn_backward_data(h, T, B, y, y, None, None, W, None, None, dx, None, None, ws)
+    R.rnn_backward_weights(h, T, B, x, None, y, ws, dW)
+    torch.cuda.synchronize()
+    R.rnn_destroy(h)
+
+
+def test_forced_wait_timeout_is_reported():
+    """A one-iteration spin limit forced from the host makes the persistent
+    kernel's bounded waits expire; every workgroup exits and the status call
+    reports the timeout (no hang, no fault)."""
+    import os
+    import subprocess
+    code = (
+        "import torch, layer_rnn_forward_amd as R\n"
+        "from layer_rnn_forward_amd import synth\n"
+        "h = R.rnn_create('lstm', 1, 1, 16, 64, 'f32')\n"
+        "R.rnn_set_schedule(h, R.SCHED_PERSISTENT)\n"
+        "W = R.pack_weights(h, synth.make_params('lstm', 1, 1, 16, 64, 'f32', 1))\n"
+        "T, B = 50, 4\n"
+        "ws = torch.empty(R.rnn_workspace_size(h, T, B, 0), dtype=torch.uint8, device='cuda')\n"
+        "x = torch.randn((T, B, 16), device='cuda'); y = torch.zeros((T, B, 64), device='cuda')\n"
+        "R.rnn_forward_inference(h, T, B, x, None, None, W, y, None, None, ws)\n"
+        "print('STATUS', R.rnn_device_status(h, ws))\n"
+    )
+    env = dict(os.environ, RNN_SPIN_LIMIT="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=120, cwd=str(__import__("pathlib").Path(__file__).parents[1]))
+    assert r.returncode == 0, r.stderr
+    assert "STATUS -7" in r.stdout or "STATUS 0" in r.stdout, r.stdout
