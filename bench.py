@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused RNN operator on one MI355X.
+
+One step = one full training pass of the hot path on one batch of synthetic
+input: rnn_forward_training + rnn_backward_data + rnn_backward_weights
+(hoisted input GEMM, persistent recurrent sweep with fused gates, reserve
+fill, BPTT sweep, dX GEMM, dW GEMMs).  Workload: single-layer unidirectional
+LSTM at the Deep Speech 2 shape (T=300, B=20, input=800, hidden=800), bf16
+weights with fp32 state and accumulation (headline); the fp32-weight variant
+is reported next to it.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  GFLOP/s counts GEMM flops only (2*M*N*K): forward
+2*T*B*G*H*(I+H), training step three times that.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "fused RNN train-step GFLOP/s + fwd ms at DS2 shape (T300 B20 H800); % MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
+HBM_GBS = 8000.0
+
+
+def flops(mode, T, B, I, H, L, D):
+    G = {"rnn_tanh": 1, "lstm": 4, "gru": 3}[mode]
+    f = 0
+    for l in range(L):
+        I_l = I if l == 0 else D * H
+        f += D * 2 * T * B * G * H * (I_l + H)
+    return f
+
+
+class Runner:
+    def __init__(self, w, torch, R, synth):
+        self.torch, self.R = torch, R
+        self.w = w
+        case = synth.make_workload(w)
+        T, B, I, H, L, D = w.T, w.B, w.input_size, w.hidden, w.layers, w.dirs
+        self.T, self.B = T, B
+        self.h = R.rnn_create(w.mode, L, D, I, H, w.wtype)
+        dev = "cuda"
+        f32 = torch.float32
+        t = lambda a: None if a is None else torch.as_tensor(a, dtype=torch.float64).to(f32).to(dev)
+        self.W = R.pack_weights(self.h, case["params"], dev)
+        self.x, self.h0, self.c0 = t(case["x"]), t(case["h0"]), t(case["c0"])
+        self.dy = t(case["dy"])
+        self.y = torch.empty((T, B, D * H), device=dev)
+        self.hy = torch.empty((L * D, B, H), device=dev)
+        self.cy = torch.empty((L * D, B, H), device=dev) if w.mode == "lstm" else None
+        self.dx = torch.empty((T, B, I), device=dev)
+        self.dh0 = torch.empty((L * D, B, H), device=dev)
+        self.dc0 = torch.empty((L * D, B, H), device=dev) if w.mode == "lstm" else None
+        self.dW = torch.empty((R.rnn_weights_size(self.h, 1) // 4,), device=dev)
+        self.ws = torch.empty(R.rnn_workspace_size(self.h, T, B, 1), dtype=torch.uint8, device=dev)
+        self.ws_inf = torch.empty(R.rnn_workspace_size(self.h, T, B, 0), dtype=torch.uint8, device=dev)
+
+    def train_step(self):
+        R, T, B = self.R, self.T, self.B
+        R.rnn_forward_training(self.h, T, B, self.x, self.h0, self.c0, self.W, self.y, self.hy,
+                               self.cy, self.ws)
+        R.rnn_backward_data(self.h, T, B, self.y, self.dy, None, None, self.W, self.h0, self.c0,
+                            self.dx, self.dh0, self.dc0, self.ws)
+        R.rnn_backward_weights(self.h, T, B, self.x, self.h0, self.y, self.ws, self.dW)
+
+    def fwd(self):
+        self.R.rnn_forward_inference(self.h, self.T, self.B, self.x, self.h0, self.c0, self.W,
+                                     self.y, self.hy, self.cy, self.ws_inf)
+
+    def timed(self, fn, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        times = []
+        s = torch.cuda.current_stream()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(s)
+            fn()
+            b.record(s)
+            times.append((a, b))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = [a.elapsed_time(b) for a, b in times]
+        return ms, wall
+
+
+def cpu_baseline(w, synth, T_sample):
+    """The fp64 oracle on the host cores, on the first T_sample steps of the
+    same workload (forward + backward through time + weight gradients)."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from oracle import rnn_oracle as orc
+    case = synth.make_workload(w)
+    x = case["x"][:T_sample]
+    dy = case["dy"][:T_sample]
+    D = w.dirs
+    t0 = time.perf_counter()
+    _, _, _, cache = orc.forward(w.mode, x, case["params"], h0=case["h0"], c0=case["c0"],
+                                 num_dirs=D, keep=True)
+    orc.backward(w.mode, case["params"], cache, dy, num_dirs=D)
+    dt = time.perf_counter() - t0
+    f = 3 * flops(w.mode, T_sample, w.B, w.input_size, w.hidden, w.layers, D)
+    cores = None
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+    except Exception:
+        pass
+    return {"value": round(f / dt / 1e9, 3), "unit": "GFLOP/s", "cores": cores or os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{w.name}: first {T_sample} of {w.T} steps, forward_training + "
+                      f"backward_data + backward_weights in fp64, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="lstm_ds2_bf16")
+    ap.add_argument("--cpu-sample-steps", type=int, default=30)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-fp32", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              "(the operator has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import layer_rnn_forward_amd as R
+    from layer_rnn_forward_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    run = Runner(w, torch, R, synth)
+    F_train = 3 * flops(w.mode, w.T, w.B, w.input_size, w.hidden, w.layers, w.dirs)
+    F_fwd = flops(w.mode, w.T, w.B, w.input_size, w.hidden, w.layers, w.dirs)
+
+    # forward-inference latency
+    fwd_ms, _ = run.timed(run.fwd, max(5, args.steps // 2), args.warmup)
+    # training steps, per-kernel HIP events recorded by the library on this stream
+    for _ in range(args.warmup):
+        run.train_step()
+    torch.cuda.synchronize()
+    R.rnn_set_profiling(run.h, True)
+    step_ms, wall = run.timed(run.train_step, args.steps, 0)
+    kern = {}
+    for k, name in enumerate(R.KERNEL_NAMES):
+        n, ms = R.rnn_profile_read(run.h, k)
+        if n:
+            kern[name] = {"launches": n, "avg_us": round(1000 * ms / n, 3), "total_ms": round(ms, 3)}
+    R.rnn_set_profiling(run.h, False)
+    assert R.rnn_device_status(run.h, run.ws) == 0
+
+    T_ms = float(np.mean(step_ms))
+    value = F_train / (T_ms * 1e-3) / 1e9
+    peak = PEAK_TFLOPS[w.wtype]
+    # dominant kernel: the one with the largest total time
+    dom = max(kern.items(), key=lambda kv: kv[1]["total_ms"])
+    G = {"rnn_tanh": 1, "lstm": 4, "gru": 3}[w.mode]
+    per_launch_flops = {
+        "recurrent_fwd": 2.0 * w.T * w.B * G * w.hidden * w.hidden * w.dirs,
+        "recurrent_bwd": 2.0 * w.T * w.B * G * w.hidden * w.hidden * w.dirs,
+        "gemm_input": 2.0 * w.T * w.B * G * w.hidden * w.input_size * w.dirs,
+        "gemm_dx": 2.0 * w.T * w.B * G * w.hidden * w.input_size * w.dirs,
+    }
+    dname, dk = dom
+    launches_per_step = dk["launches"] / args.steps
+    if dname in per_launch_flops and w.layers == 1:
+        achieved = per_launch_flops[dname] / (dk["avg_us"] * 1e-6) / 1e12
+        roof = {"kernel": dname, "bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": None,
+                "avg_launch_us": dk["avg_us"],
+                "algorithmic_flops_per_launch": per_launch_flops[dname]}
+    else:
+        roof = {"kernel": dname, "bound": "mfma", "achieved": None, "peak": peak,
+                "unit": "TFLOP/s", "frac": None, "traffic": None, "avg_launch_us": dk["avg_us"]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(T_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.wtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian inputs, uniform weights; no data set)",
+        "config": {"workload": w.name, "mode": w.mode, "layers": w.layers, "dirs": w.dirs,
+                   "T": w.T, "B": w.B, "input": w.input_size, "hidden": w.hidden,
+                   "weights": w.wtype, "state_accum": "f32"},
+        "fwd_ms": round(float(np.median(fwd_ms)), 4),
+        "pct_mfma_peak": round(100.0 * value / (peak * 1000.0), 4),
+        "train_step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
+        "kernels": kern,
+        "roofline": roof,
+    }
+    if not args.no_fp32 and w.wtype == "bf16":
+        w32 = synth.WORKLOADS.get(args.workload.replace("bf16", "f32"))
+        if w32 is not None:
+            r32 = Runner(w32, torch, R, synth)
+            f_ms, _ = r32.timed(r32.fwd, max(5, args.steps // 2), args.warmup)
+            s_ms, _ = r32.timed(r32.train_step, args.steps, args.warmup)
+            v32 = F_train / (float(np.mean(s_ms)) * 1e-3) / 1e9
+            out["fp32_weights"] = {"value": round(v32, 3), "unit": "GFLOP/s",
+                                   "ms_per_step": round(float(np.mean(s_ms)), 4),
+                                   "fwd_ms": round(float(np.median(f_ms)), 4),
+                                   "pct_mfma_peak": round(100.0 * v32 / (PEAK_TFLOPS["f32"] * 1000), 4)}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_sample_steps)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -21,6 +21,16 @@
 // units, exchanges the recurrent gate gradients dG_h, computes
 // dh = dG_h W_hh for its units on MFMA, and applies the hand-derived BPTT
 // formulas to the reserved forward intermediates.
+//
+// Exchange protocol.  The vector one step produces (h, or dG_h) goes into a
+// ring with one entry per step, so no address is ever written twice within a
+// sweep.  Each producer owns whole 128-byte lines of an entry (its slice:
+// rows x units, zero-padded), writes them with agent-scope stores, waits for
+// their completion and then stores its step flag (agent scope).  A consumer
+// polls the flags with agent-scope loads and then reads the entry with plain
+// loads: no cache can hold a stale copy of a line that was never read before
+// its single writer completed, so no cache write-back or invalidation is
+// needed per step, and the workgroups of one XCD share the entry through L2.
 #include <type_traits>
 
 #include "device_util.h"
@@ -51,12 +61,11 @@ __device__ __forceinline__ uint4 pack_frag(const uint32_t (&v)[BF16 ? 8 : 4]) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Wave 0 polls the flags of up to three groups (ranges of nwg workgroups),
-// then performs the agent acquire; the workgroup barrier follows.  Returns
-// false (for every thread) if the bounded wait expired or another workgroup
-// reported an error.
+// Wave 0 polls the flags of up to two groups (ranges of nwg workgroups); the
+// workgroup barrier follows.  Returns false (for every thread) if the bounded
+// wait expired or another workgroup reported an error.
 __device__ bool wait_groups(const unsigned* flags, unsigned* err, unsigned spin_limit,
-                            const int (&g)[3], int ng, int nwg, unsigned target, int* s_flag) {
+                            const int (&g)[2], int ng, int nwg, unsigned target, int* s_flag) {
   const int tid = threadIdx.x;
   if (tid < 64) {
     const int lane = tid;
@@ -80,7 +89,6 @@ __device__ bool wait_groups(const unsigned* flags, unsigned* err, unsigned spin_
       __builtin_amdgcn_s_sleep(1);
     }
     if (lane == 0) *s_flag = ok ? 1 : 0;
-    acquire_agent();
   }
   __syncthreads();
   const bool ok = *s_flag != 0;
@@ -88,12 +96,59 @@ __device__ bool wait_groups(const unsigned* flags, unsigned* err, unsigned spin_
   return ok;
 }
 
+// Every wave waits for completion of its stores (the ring stores are agent
+// scope), then one thread publishes the flag.
 __device__ __forceinline__ void publish(unsigned* flags, unsigned v) {
   drain_stores();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    release_agent();
-    flag_store(flags + (size_t)blockIdx.x * kFlagStride, v);
+  if (threadIdx.x == 0) flag_store(flags + (size_t)blockIdx.x * kFlagStride, v);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void ring_store(char* base, size_t off, float v) {
+  if constexpr (BF16)
+    __hip_atomic_store(reinterpret_cast<uint16_t*>(base + off), f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    __hip_atomic_store(reinterpret_cast<float*>(base + off), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// MFMA over the K chunks this wave holds: A fragments are gathered from ring
+// entries by `addr(k0, row, valid&)` (16 bytes per lane), all loads of a batch
+// issued before its MFMAs (branch-free; invalid lanes load a valid address and
+// are zeroed) so that their latencies overlap.
+template <bool BF16, int NT, int MT, int KPW, int NW, class AddrF>
+__device__ __forceinline__ void mfma_sweep(f32x4 (&acc)[MT][NT], const uint4 (&wf)[KPW][NT],
+                                           int wave, int fr, int fq, int nch, int Bact,
+                                           AddrF addr) {
+  constexpr int KC = kchunk<BF16>();
+  constexpr int PER = KC / 4;
+  constexpr int KB = KPW < 8 ? KPW : 8;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KPW; kb += KB) {
+    uint4 av[KB][MT];
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const int gc = wave + (kb + kk) * NW;
+      const int k0 = gc * KC + fq * PER;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 16 + fr;
+        bool v = gc < nch && row < Bact;
+        const char* a = addr(k0, row, v);
+        const uint4 t = *reinterpret_cast<const uint4*>(a);
+        av[kk][mt] = v ? t : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_chunk<BF16>(av[kk][mt], wf[kb + kk][nt], acc[mt][nt]);
   }
 }
 
@@ -106,8 +161,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   constexpr int PER = KC / 4;
   constexpr int NCOL = NT * 16;
   constexpr int NROW = MT * 16;
-  constexpr int NTHR = NW * 64;
-  using X = XT<BF16>;
+  constexpr int ES = BF16 ? 2 : 4;
 
   __shared__ float red[NW][NROW][NCOL + 1];
   __shared__ float sh_h[NROW * NCOL];
@@ -124,23 +178,22 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   const int d = (grp / p.nchunk) % p.D;
   const int li = grp / (p.nchunk * p.D);
   const int layer = p.first_layer + li;
-  const int U = p.U, H = p.H, D = p.D, B = p.B, T = p.T, Hp = p.Hp;
+  const int U = p.U, H = p.H, D = p.D, B = p.B, T = p.T;
   const int GH = G * H;
   const int u0 = slice * U;
-  const int Uact = min(U, H - u0);
+  const int Uact = max(0, min(U, H - u0));
   const int b0 = c * p.Bc;
   const int Bact = min(p.Bc, B - b0);
   const bool inproj = p.wavefront && li > 0;
   const int GB = (MODE == MODE_GRU && inproj) ? 4 : G;   // column blocks
   const int I_l = p.in_l[li];
-  const int Ipx = inproj ? Hp : 0;
-  const int nch = (Ipx + Hp) / KC;
+  const int Kh = p.nwg * U;               // padded width of h (unit order)
+  const int Kx = inproj ? Kh : 0;         // the layer below's h in the wavefront
+  const int nch = (Kx + Kh + KC - 1) / KC;
   const int DC = p.D * p.nchunk;
 
-  X* xch = reinterpret_cast<X*>(p.xch);
-  const size_t gstride = (size_t)2 * p.Bc * Hp;
-  X* my_x = xch + (size_t)grp * gstride;
-  const X* below_x = inproj ? xch + (size_t)(grp - DC) * gstride : nullptr;
+  char* ring = reinterpret_cast<char*>(p.xch) + (size_t)grp * p.ring_group;
+  const char* ring_below = inproj ? reinterpret_cast<const char*>(p.xch) + (size_t)(grp - DC) * p.ring_group : nullptr;
   const void* wih = p.w_ih[li];
   const void* whh = p.w_hh[li];
 
@@ -168,10 +221,10 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
           const int k = gc * KC + fq * PER + e;
-          if (k < Ipx) {
+          if (k < Kx) {
             if (use_x && k < I_l) v[e] = w_bits<BF16>(wih, row * I_l + k);
           } else {
-            const int kh = k - Ipx;
+            const int kh = k - Kx;
             if (use_h && kh < H) v[e] = w_bits<BF16>(whh, row * H + kh);
           }
         }
@@ -180,22 +233,26 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     }
   }
 
-  // ---- initial state
-  const int q = tid;                   // epilogue pair owned by this thread
-  const bool qv = q < Bact * Uact;
-  const int qb = qv ? q / Uact : 0, qj = qv ? q - (q / Uact) * Uact : 0;
+  // ---- epilogue ownership: thread q <-> (row qb, unit qj) over Bact x U
+  const int q = tid;
+  const bool qw = q < Bact * U;             // writes the ring (zeros for padded units)
+  const int qb = qw ? q / U : 0, qj = qw ? q - (q / U) * U : 0;
+  const bool qv = qw && qj < Uact;          // a real (row, unit)
   const int qu = u0 + qj, qbg = b0 + qb;
   const size_t st_idx = (((size_t)li * D + d) * B + qbg) * H + qu;
   const size_t hx_idx = (((size_t)layer * D + d) * B + qbg) * H + qu;
+  const size_t my_off = (size_t)slice * p.slice + ((size_t)qb * U + qj) * ES;
+
   if (p.s_begin < 0) {
+    float hv = 0.f, cv = 0.f;
     if (qv) {
-      const float hv = p.h0 ? p.h0[hx_idx] : 0.f;
-      const float cv = (MODE == MODE_LSTM && p.c0) ? p.c0[hx_idx] : 0.f;
+      hv = p.h0 ? p.h0[hx_idx] : 0.f;
+      cv = (MODE == MODE_LSTM && p.c0) ? p.c0[hx_idx] : 0.f;
       sh_h[qb * NCOL + qj] = hv;
       sh_c[qb * NCOL + qj] = cv;
-      const int first = p.wavefront ? li : 0;
-      my_x[(size_t)(first & 1) * p.Bc * Hp + (size_t)qb * Hp + qu] = to_x<BF16>(hv);
     }
+    const int first = p.wavefront ? li : 0;
+    if (qw) ring_store<BF16>(ring + (size_t)first * p.ring_step, my_off, hv);
     if (p.persistent) publish(p.flags, 1u);
   } else if (qv) {
     sh_h[qb * NCOL + qj] = p.st_h[st_idx];
@@ -203,16 +260,9 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   }
   __syncthreads();
 
-  int wgroups[3];
-  int nwait = 0;
-  if (p.wavefront) {
-    for (int o = -1; o <= 1; ++o) {
-      const int l2 = li + o;
-      if (l2 >= 0 && l2 < p.nlayers) wgroups[nwait++] = grp + o * DC;
-    }
-  } else {
-    wgroups[nwait++] = grp;
-  }
+  int wgroups[2] = {grp, grp};
+  int nwait = 1;
+  if (inproj) { wgroups[0] = grp - DC; wgroups[1] = grp; nwait = 2; }
 
   const size_t ystride_t = (size_t)B * D * H;
   for (int s = max(p.s_begin, 0); s < p.s_end; ++s) {
@@ -251,28 +301,18 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
 
     if (active) {
       f32x4 acc[MT][NT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const X* hsrc = my_x + (size_t)(s & 1) * p.Bc * Hp;
-      const X* xsrc = inproj ? below_x + (size_t)(s & 1) * p.Bc * Hp : nullptr;
-#pragma unroll
-      for (int kk = 0; kk < KPW; ++kk) {
-        const int gc = wave + kk * NW;
-        if (gc < nch) {
-          const int k0 = gc * KC + fq * PER;
-          const X* src = (k0 < Ipx) ? xsrc + k0 : hsrc + (k0 - Ipx);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const int row = mt * 16 + fr;
-            uint4 a = make_uint4(0u, 0u, 0u, 0u);
-            if (row < Bact) a = *reinterpret_cast<const uint4*>(src + (size_t)row * Hp);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_chunk<BF16>(a, wf[kk][nt], acc[mt][nt]);
-          }
-        }
-      }
+      const char* eh = ring + (size_t)s * p.ring_step;
+      const char* ex = inproj ? ring_below + (size_t)s * p.ring_step : nullptr;
+      const int pslice = p.slice;
+      mfma_sweep<BF16, NT, MT, KPW, NW>(acc, wf, wave, fr, fq, nch, Bact,
+          [&](int k0, int row, bool& v) -> const char* {
+            const bool xpart = k0 < Kx;
+            const int kk = xpart ? k0 : k0 - Kx;
+            v = v && kk < Kh;
+            const int pp = kk / U, j0 = kk - pp * U;
+            const char* base = xpart ? ex : eh;
+            return v ? base + (size_t)pp * pslice + ((size_t)row * U + j0) * ES : eh;
+          });
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -281,6 +321,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
           for (int r = 0; r < 4; ++r) red[wave][mt * 16 + fq * 4 + r][nt * 16 + fr] = acc[mt][nt][r];
       __syncthreads();
 
+      float hnew = 0.f;
       if (qv) {
         float pre[4];
 #pragma unroll
@@ -293,7 +334,6 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
           pre[gb] = v;
         }
         const float hprev = sh_h[qb * NCOL + qj];
-        float hnew;
         float* res = (p.training && R > 0)
                          ? p.reserve[li] + (((size_t)d * T + t) * B + qbg) * R * H + qu
                          : nullptr;
@@ -322,8 +362,8 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         }
         sh_h[qb * NCOL + qj] = hnew;
         p.y[li][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = hnew;
-        my_x[(size_t)((s + 1) & 1) * p.Bc * Hp + (size_t)qb * Hp + qu] = to_x<BF16>(hnew);
       }
+      if (qw) ring_store<BF16>(ring + (size_t)(s + 1) * p.ring_step, my_off, hnew);
     }
     if (p.persistent) publish(p.flags, (unsigned)(s + 2));
     __syncthreads();
@@ -349,7 +389,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   constexpr int PER = KC / 4;
   constexpr int NCOL = NT * 16;
   constexpr int NROW = MT * 16;
-  using X = XT<BF16>;
+  constexpr int ES = BF16 ? 2 : 4;
 
   __shared__ float red[NW][NROW][NCOL + 1];
   __shared__ float sh_dh[NROW * NCOL];
@@ -363,20 +403,19 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   const int grp = wg / p.nwg;
   const int c = grp % p.nchunk;
   const int d = grp / p.nchunk;
-  const int U = p.U, H = p.H, D = p.D, B = p.B, T = p.T, Hp = p.Hp;
+  const int U = p.U, H = p.H, D = p.D, B = p.B, T = p.T;
   const int GH = G * H;
-  const int KP = G * Hp;
+  const int Kh = p.nwg * U;
+  const int KP = G * Kh;
   const int u0 = slice * U;
-  const int Uact = min(U, H - u0);
+  const int Uact = max(0, min(U, H - u0));
   const int b0 = c * p.Bc;
   const int Bact = min(p.Bc, B - b0);
-  const int nch = KP / KC;
+  const int nch = (KP + KC - 1) / KC;
 
-  X* xch = reinterpret_cast<X*>(p.xch);
-  const size_t gstride = (size_t)2 * p.Bc * KP;
-  X* my_x = xch + (size_t)grp * gstride;
+  char* ring = reinterpret_cast<char*>(p.xch) + (size_t)grp * p.ring_group;
 
-  // ---- W_hh^T slice -> registers: B(k = g*Hp + uu, n = j) = W_hh[g*H + uu][u0 + j]
+  // ---- W_hh^T slice -> registers: B(k = g*Kh + uu, n = j) = W_hh[g*H + uu][u0 + j]
   uint4 wf[KPW][NT];
 #pragma unroll
   for (int kk = 0; kk < KPW; ++kk) {
@@ -391,8 +430,8 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
           const int k = gc * KC + fq * PER + e;
-          const int g = k / Hp, uu = k - g * Hp;
-          if (uu < H) v[e] = w_bits<BF16>(p.w_hh, ((size_t)d * GH + (size_t)g * H + uu) * H + u0 + j);
+          const int g = k / Kh, uu = k - g * Kh;
+          if (g < G && uu < H) v[e] = w_bits<BF16>(p.w_hh, ((size_t)d * GH + (size_t)g * H + uu) * H + u0 + j);
         }
       }
       wf[kk][nt] = pack_frag<BF16>(v);
@@ -400,10 +439,12 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   }
 
   const int q = tid;
-  const bool qv = q < Bact * Uact;
-  const int qb = qv ? q / Uact : 0, qj = qv ? q - (q / Uact) * Uact : 0;
+  const bool qw = q < Bact * U;
+  const int qb = qw ? q / U : 0, qj = qw ? q - (q / U) * U : 0;
+  const bool qv = qw && qj < Uact;
   const int qu = u0 + qj, qbg = b0 + qb;
   const size_t sidx = ((size_t)d * B + qbg) * H + qu;   // [D][B][H] state index
+  const size_t my_off = (size_t)slice * p.slice + ((size_t)qb * G * U + qj) * ES;
   if (qv) {
     if (p.s_begin == 0) {
       sh_dh[qb * NCOL + qj] = p.dhy ? p.dhy[sidx] : 0.f;
@@ -414,7 +455,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
     }
   }
   __syncthreads();
-  int wgroups[3] = {grp, 0, 0};
+  const int wgroups[2] = {grp, grp};
 
   const size_t ystride_t = (size_t)B * D * H;
   for (int s = p.s_begin; s < p.s_end; ++s) {
@@ -446,26 +487,15 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
         if (!wait_groups(p.flags, p.err, p.spin_limit, wgroups, 1, p.nwg, (unsigned)s, &s_flag)) return;
       }
       f32x4 acc[MT][NT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const X* src = my_x + (size_t)(s & 1) * p.Bc * KP;
-#pragma unroll
-      for (int kk = 0; kk < KPW; ++kk) {
-        const int gc = wave + kk * NW;
-        if (gc < nch) {
-          const int k0 = gc * KC + fq * PER;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const int row = mt * 16 + fr;
-            uint4 a = make_uint4(0u, 0u, 0u, 0u);
-            if (row < Bact) a = *reinterpret_cast<const uint4*>(src + (size_t)row * KP + k0);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_chunk<BF16>(a, wf[kk][nt], acc[mt][nt]);
-          }
-        }
-      }
+      const char* e = ring + (size_t)s * p.ring_step;
+      const int pslice = p.slice;
+      mfma_sweep<BF16, NT, MT, KPW, NW>(acc, wf, wave, fr, fq, nch, Bact,
+          [&](int k0, int row, bool& v) -> const char* {
+            const int g = k0 / Kh, uu = k0 - g * Kh;
+            v = v && g < G;
+            const int pp = uu / U, j0 = uu - pp * U;
+            return v ? e + (size_t)pp * pslice + (((size_t)row * G + g) * U + j0) * ES : e;
+          });
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -479,14 +509,15 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
       }
     }
 
-    if (qv) {
-      const float carry = sh_dh[qb * NCOL + qj];
-      if (final_phase) {
-        if (p.dh0) p.dh0[sidx] = dhrec + carry;
+    if (final_phase) {
+      if (qv) {
+        if (p.dh0) p.dh0[sidx] = dhrec + sh_dh[qb * NCOL + qj];
         if (MODE == MODE_LSTM && p.dc0) p.dc0[sidx] = sh_dc[qb * NCOL + qj];
-      } else {
-        const float dh = dhrec + dyv + carry;
-        float dgi[4] = {0.f, 0.f, 0.f, 0.f}, dgh[4] = {0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+      float dgi[4] = {0.f, 0.f, 0.f, 0.f}, dgh[4] = {0.f, 0.f, 0.f, 0.f};
+      if (qv) {
+        const float dh = dhrec + dyv + sh_dh[qb * NCOL + qj];
         float ncarry = 0.f;
         if (MODE == MODE_LSTM) {
           const float ig = rv[0], fg = rv[1], gg = rv[2], og = rv[3], cc = rv[4];
@@ -518,13 +549,16 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
         }
         sh_dh[qb * NCOL + qj] = ncarry;
         const size_t row = ((size_t)t * B + qbg) * D * GH + (size_t)d * GH + qu;
-        X* xo = my_x + (size_t)((s + 1) & 1) * p.Bc * KP + (size_t)qb * KP + qu;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           p.dgi[row + (size_t)g * H] = dgi[g];
           if (MODE == MODE_GRU) p.dgh[row + (size_t)g * H] = dgh[g];
-          xo[(size_t)g * Hp] = to_x<BF16>(dgh[g]);
         }
+      }
+      if (qw) {
+        char* e = ring + (size_t)(s + 1) * p.ring_step;
+#pragma unroll
+        for (int g = 0; g < G; ++g) ring_store<BF16>(e, my_off + (size_t)g * U * ES, dgh[g]);
       }
     }
     if (p.persistent && !final_phase) publish(p.flags, (unsigned)(s + 1));
@@ -581,10 +615,16 @@ struct BwdK {
   X(M, BF, 1, 2, 8, 4)            \
   X(M, BF, 1, 1, 16, 4)           \
   X(M, BF, 1, 2, 16, 4)           \
+  X(M, BF, 2, 1, 8, 4)            \
   X(M, BF, 2, 2, 8, 4)            \
+  X(M, BF, 2, 1, 16, 4)           \
   X(M, BF, 2, 2, 16, 4)           \
+  X(M, BF, 4, 1, 8, 8)            \
   X(M, BF, 4, 2, 8, 8)            \
-  X(M, BF, 1, 2, 32, 4)
+  X(M, BF, 1, 2, 32, 4)           \
+  X(M, BF, 1, 2, 16, 8)           \
+  X(M, BF, 2, 2, 16, 8)           \
+  X(M, BF, 4, 2, 16, 8)
 
 #define RNN_BWD_CONFIGS(X, M, BF) \
   X(M, BF, 1, 1, 8, 4)            \

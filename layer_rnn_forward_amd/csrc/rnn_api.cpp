@@ -48,7 +48,9 @@ struct SweepPlan {
 
 struct Plan {
   int T = 0, B = 0, training = 0;
-  int Bc = 0, nchunk = 0, Hp = 0;
+  int Bc = 0, nchunk = 0;
+  int fslice = 0, bslice = 0;
+  size_t fring_step = 0, fring_group = 0, bring_step = 0, bring_group = 0;
   bool wavefront = false;
   SweepPlan fwd, bwd;
   size_t off_err = 0, off_flags = 0, flags_bytes = 0;
@@ -108,64 +110,69 @@ void layout_weights(rnn_desc* h) {
 }
 
 // Candidate kernel configurations, in order of preference.
-const RecConfig kFwdCfgs[] = {{1, 1, 8, 4}, {1, 2, 8, 4}, {1, 1, 16, 4}, {1, 2, 16, 4},
-                              {2, 2, 8, 4}, {2, 2, 16, 4}, {4, 2, 8, 8}, {1, 2, 32, 4}};
+const RecConfig kFwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 1, 16, 4}, {1, 2, 16, 4}, {2, 1, 8, 4},
+                              {2, 2, 8, 4},  {2, 1, 16, 4}, {2, 2, 16, 4}, {4, 1, 8, 8},  {4, 2, 8, 8},
+                              {1, 2, 32, 4}, {1, 2, 16, 8}, {2, 2, 16, 8}, {4, 2, 16, 8}};
 const RecConfig kBwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 2, 16, 4}, {1, 2, 32, 4},
                               {1, 2, 16, 8}, {1, 2, 32, 8}, {1, 1, 32, 8}};
 
-// Pick a forward configuration: units per workgroup U so that the groups fill
-// about one workgroup per CU, the gate columns of U units fit the MFMA tiles,
-// the K chunks fit the registers, and each epilogue thread owns one (row, unit).
-bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, int Hp, bool inproj, SweepPlan* sp) {
+// Units per workgroup are a multiple of the per-lane MFMA k run (8 bf16 / 4
+// fp32 values, 16 bytes) so that every A fragment of the exchange comes from
+// one producer's slice.
+int unit_quantum(const rnn_desc* h) { return h->wtype == RNN_W_BF16 ? 8 : 4; }
+
+// Pick a forward configuration: U so that all groups together use about
+// `target_wgs` workgroups, the gate columns of U units fit the MFMA tiles, the
+// K chunks fit the registers, and each epilogue thread owns one (row, unit).
+bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepPlan* sp) {
   const int bf = h->wtype == RNN_W_BF16;
   const int KC = bf ? 32 : 16;
+  const int Q = unit_quantum(h);
   const int GB = (h->mode == RNN_GRU && inproj) ? 4 : h->G;
-  const int nch = ((inproj ? Hp : 0) + Hp) / KC;
-  int target = std::max(1, 256 / std::max(1, groups));
-  int Umin = ceil_div(h->H, target);
+  const int target_wgs = std::max(1, env_int("RNN_FWD_TARGET_WGS", 128));
+  int U = ceil_div(ceil_div(h->H * std::max(1, groups), target_wgs), Q) * Q;
   const int Uenv = env_int("RNN_FWD_UNITS", 0);
-  if (Uenv > 0) Umin = Uenv;
-  for (const RecConfig& c : kFwdCfgs) {
-    if (c.mt != mt) continue;
-    const int Umax = std::min(16 * c.nt / GB, 64 * c.nwaves / std::max(1, Bc));
-    if (Umax < 1 || Umax < std::min(Umin, h->H)) continue;
-    if (nch > c.kpw * c.nwaves) continue;
-    int U = std::min(std::max(1, Umin), h->H);
-    if (Uenv <= 0 && U < Umax) {
-      // spread units evenly over the workgroups
-      int nwg = ceil_div(h->H, U);
-      U = ceil_div(h->H, nwg);
+  if (Uenv > 0) U = ceil_div(Uenv, Q) * Q;
+  U = std::max(Q, std::min(U, ceil_div(h->H, Q) * Q));
+  for (int tryU = U; tryU >= Q; tryU -= Q) {
+    const int nwg = ceil_div(h->H, tryU);
+    const int Kh = nwg * tryU;
+    const int nch = ceil_div((inproj ? 2 : 1) * Kh, KC);
+    for (const RecConfig& c : kFwdCfgs) {
+      if (c.mt != mt) continue;
+      if (GB * tryU > 16 * c.nt || Bc * tryU > 64 * c.nwaves) continue;
+      if (nch > c.kpw * c.nwaves) continue;
+      sp->cfg = c;
+      sp->U = tryU;
+      sp->nwg = nwg;
+      sp->groups = groups;
+      sp->grid = nwg * groups;
+      return true;
     }
-    sp->cfg = c;
-    sp->U = U;
-    sp->nwg = ceil_div(h->H, U);
-    sp->groups = groups;
-    sp->grid = sp->nwg * groups;
-    return true;
   }
   return false;
 }
 
-bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, int Hp, SweepPlan* sp) {
+bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, SweepPlan* sp) {
   const int bf = h->wtype == RNN_W_BF16;
   const int KC = bf ? 32 : 16;
-  const int nch = h->G * Hp / KC;
-  int U = env_int("RNN_BWD_UNITS", 16);
-  U = std::max(1, std::min(U, h->H));
-  // keep at least ~groups*nwg <= 256 when possible
-  while (U < 16 && ceil_div(h->H, U) * groups > 256) ++U;
-  for (const RecConfig& c : kBwdCfgs) {
-    if (c.mt != mt) continue;
-    if (U > 16 * c.nt) continue;
-    if (Bc * U > 64 * c.nwaves) continue;
-    if (nch > c.kpw * c.nwaves) continue;
-    const int nwg = ceil_div(h->H, U);
-    sp->cfg = c;
-    sp->U = ceil_div(h->H, nwg);
-    sp->nwg = nwg;
-    sp->groups = groups;
-    sp->grid = nwg * groups;
-    return true;
+  const int Q = unit_quantum(h);
+  int U = ceil_div(std::max(1, env_int("RNN_BWD_UNITS", 8)), Q) * Q;
+  U = std::max(Q, std::min(U, ceil_div(h->H, Q) * Q));
+  for (int tryU = U; tryU >= Q; tryU -= Q) {
+    const int nwg = ceil_div(h->H, tryU);
+    const int nch = ceil_div(h->G * nwg * tryU, KC);
+    for (const RecConfig& c : kBwdCfgs) {
+      if (c.mt != mt) continue;
+      if (tryU > 16 * c.nt || Bc * tryU > 64 * c.nwaves) continue;
+      if (nch > c.kpw * c.nwaves) continue;
+      sp->cfg = c;
+      sp->U = tryU;
+      sp->nwg = nwg;
+      sp->groups = groups;
+      sp->grid = nwg * groups;
+      return true;
+    }
   }
   return false;
 }
@@ -176,9 +183,7 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   p.B = B;
   p.training = training;
   const int bf = h->wtype == RNN_W_BF16;
-  const int KC = bf ? 32 : 16;
   const size_t es = bf ? 2 : 4;
-  p.Hp = ceil_div(h->H, KC) * KC;
   const int Bq = std::max(B, 1);
   p.nchunk = ceil_div(Bq, 32);
   p.Bc = ceil_div(Bq, p.nchunk);
@@ -186,15 +191,15 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   p.wavefront = (h->D == 1 && h->L > 1 && h->L <= kMaxLayersPerLaunch &&
                  env_int("RNN_NO_WAVEFRONT", 0) == 0);
   const int fl = p.wavefront ? h->L : 1;
-  if (!plan_fwd(h, mt, p.Bc, fl * h->D * p.nchunk, p.Hp, p.wavefront, &p.fwd) ||
-      !plan_bwd(h, mt, p.Bc, h->D * p.nchunk, p.Hp, &p.bwd)) {
+  if (!plan_fwd(h, mt, p.Bc, fl * h->D * p.nchunk, p.wavefront, &p.fwd) ||
+      !plan_bwd(h, mt, p.Bc, h->D * p.nchunk, &p.bwd)) {
     p.status = RNN_STATUS_UNSUPPORTED;
     return p;
   }
-  // wavefront: every workgroup polls three groups' flags
-  if (p.wavefront && 3 * p.fwd.nwg > kMaxWaitFlags) p.wavefront = false;
+  // wavefront: every workgroup polls its own and the layer below's flags
+  if (p.wavefront && 2 * p.fwd.nwg > kMaxWaitFlags) p.wavefront = false;
   if (!p.wavefront && p.fwd.groups != h->D * p.nchunk) {
-    if (!plan_fwd(h, mt, p.Bc, h->D * p.nchunk, p.Hp, false, &p.fwd)) {
+    if (!plan_fwd(h, mt, p.Bc, h->D * p.nchunk, false, &p.fwd)) {
       p.status = RNN_STATUS_UNSUPPORTED;
       return p;
     }
@@ -226,8 +231,16 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   p.flags_bytes = (size_t)std::max(p.fwd.grid, p.bwd.grid) * kFlagStride * 4;
   off = align_up(off + p.flags_bytes);
   p.off_xch = off;
-  size_t xf = (size_t)p.fwd.groups * 2 * p.Bc * p.Hp * es;
-  size_t xb = (size_t)p.bwd.groups * 2 * p.Bc * h->G * p.Hp * es;
+  // exchange rings: one entry per step, one 128-byte-aligned slice per producer
+  const int s_total = T + (p.wavefront ? h->L : 1) - 1;
+  p.fslice = (int)(((size_t)p.Bc * p.fwd.U * es + 127) / 128 * 128);
+  p.fring_step = (size_t)p.fwd.nwg * p.fslice;
+  p.fring_group = align_up(p.fring_step * (size_t)(s_total + 1));
+  p.bslice = (int)(((size_t)p.Bc * h->G * p.bwd.U * es + 127) / 128 * 128);
+  p.bring_step = (size_t)p.bwd.nwg * p.bslice;
+  p.bring_group = align_up(p.bring_step * (size_t)(T + 1));
+  size_t xf = (size_t)p.fwd.groups * p.fring_group;
+  size_t xb = (size_t)p.bwd.groups * p.bring_group;
   p.xch_bytes = std::max(xf, training ? xb : (size_t)0);
   off = align_up(off + p.xch_bytes);
   p.off_st = off;
@@ -411,7 +424,9 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   f.Bc = p.Bc;
   f.U = p.fwd.U;
   f.nwg = p.fwd.nwg;
-  f.Hp = p.Hp;
+  f.slice = p.fslice;
+  f.ring_step = (long long)p.fring_step;
+  f.ring_group = (long long)p.fring_group;
   f.persistent = p.fwd.persistent ? 1 : 0;
   f.training = training;
   f.h0 = h0;
@@ -429,7 +444,7 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
     f.nlayers = nlayers;
     f.s_total = T + nlayers - 1;
     const int grid = p.fwd.nwg * nlayers * h->D * p.nchunk;
-    RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}, {at<void>(ws, p.off_xch), p.xch_bytes}}));
+    if (f.persistent) RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
     if (f.persistent) {
       f.s_begin = -1;
       f.s_end = f.s_total;
@@ -608,7 +623,9 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
   b.Bc = p.Bc;
   b.U = p.bwd.U;
   b.nwg = p.bwd.nwg;
-  b.Hp = p.Hp;
+  b.slice = p.bslice;
+  b.ring_step = (long long)p.bring_step;
+  b.ring_group = (long long)p.bring_group;
   b.persistent = p.bwd.persistent ? 1 : 0;
   b.st_dh = at<float>(ws, p.off_st);
   b.st_dc = at<float>(ws, p.off_st + p.st_bytes / 2);
@@ -629,7 +646,7 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
     b.dgh = h->mode == RNN_GRU ? at<float>(ws, p.off_dgh + p.dg_layer * l) : nullptr;
     b.dh0 = dh0 ? dh0 + l * lstride : nullptr;
     b.dc0 = dc0 ? dc0 + l * lstride : nullptr;
-    RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}, {at<void>(ws, p.off_xch), p.xch_bytes}}));
+    if (b.persistent) RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
     if (b.persistent) {
       b.s_begin = 0;
       b.s_end = T + 1;

@@ -63,7 +63,9 @@ struct FwdParams {
   int nlayers;            // layers in this launch
   int nchunk, Bc;         // batch chunks of Bc rows
   int U, nwg;             // units per workgroup, workgroups per group
-  int Hp;                 // padded exchange row (multiple of the MFMA K chunk)
+  int slice;              // bytes of one producer's slice in a ring entry (multiple of 128)
+  long long ring_step;    // bytes of one ring entry (nwg * slice)
+  long long ring_group;   // bytes of one group's ring (entries * ring_step)
   int s_begin, s_end;     // global steps [s_begin, s_end); -1 is the prologue
   int s_total;            // T + nlayers - 1
   int persistent, training, wavefront;
@@ -82,7 +84,7 @@ struct FwdParams {
   float* cy;
   float* st_h;            // carried state between stepped launches [nlayers*D][B][H]
   float* st_c;
-  void* xch;              // exchange buffers: per group [2][Bc][Hp] (element type of the path)
+  void* xch;              // exchange rings: per group [s_total + 1][nwg][slice]
   unsigned* flags;        // per workgroup, kFlagStride apart
   unsigned* err;
   unsigned spin_limit;
@@ -90,7 +92,9 @@ struct FwdParams {
 
 struct BwdParams {
   int T, B, H, D;
-  int nchunk, Bc, U, nwg, Hp;
+  int nchunk, Bc, U, nwg;
+  int slice;              // bytes of one producer's slice (Bc x G x U values, padded to 128)
+  long long ring_step, ring_group;
   int s_begin, s_end;     // processing steps; s == T is the final dh0 phase
   int persistent;
   const void* w_hh;       // layer block [D*G*H, H]
@@ -107,7 +111,7 @@ struct BwdParams {
   float* dc0;
   float* st_dh;           // carries between stepped launches [D*nchunk... ] laid out [D][B][H]
   float* st_dc;
-  void* xch;              // per group [2][Bc][G*Hp]
+  void* xch;              // exchange rings: per group [T + 1][nwg][slice]
   unsigned* flags;
   unsigned* err;
   unsigned spin_limit;
