@@ -94,21 +94,23 @@ class Runner:
         return ms, wall
 
 
-def cpu_baseline(w, synth, T_sample):
-    """The fp64 oracle on the host cores, on the first T_sample steps of the
-    same workload (forward + backward through time + weight gradients)."""
+def cpu_baseline(w, synth, min_seconds):
+    """The fp64 oracle on the host cores: full training steps of the same
+    workload (forward + backward through time + weight gradients), repeated
+    until at least `min_seconds` of CPU work have been timed."""
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from oracle import rnn_oracle as orc
     case = synth.make_workload(w)
-    x = case["x"][:T_sample]
-    dy = case["dy"][:T_sample]
     D = w.dirs
-    t0 = time.perf_counter()
-    _, _, _, cache = orc.forward(w.mode, x, case["params"], h0=case["h0"], c0=case["c0"],
-                                 num_dirs=D, keep=True)
-    orc.backward(w.mode, case["params"], cache, dy, num_dirs=D)
-    dt = time.perf_counter() - t0
-    f = 3 * flops(w.mode, T_sample, w.B, w.input_size, w.hidden, w.layers, D)
+    reps, dt = 0, 0.0
+    while reps == 0 or dt < min_seconds:
+        t0 = time.perf_counter()
+        _, _, _, cache = orc.forward(w.mode, case["x"], case["params"], h0=case["h0"],
+                                     c0=case["c0"], num_dirs=D, keep=True)
+        orc.backward(w.mode, case["params"], cache, case["dy"], num_dirs=D)
+        dt += time.perf_counter() - t0
+        reps += 1
+    f = reps * 3 * flops(w.mode, w.T, w.B, w.input_size, w.hidden, w.layers, D)
     cores = None
     try:
         from threadpoolctl import threadpool_info
@@ -117,8 +119,37 @@ def cpu_baseline(w, synth, T_sample):
         pass
     return {"value": round(f / dt / 1e9, 3), "unit": "GFLOP/s", "cores": cores or os.cpu_count(),
             "kind": "oracle",
-            "sample": f"{w.name}: first {T_sample} of {w.T} steps, forward_training + "
-                      f"backward_data + backward_weights in fp64, {dt:.2f} s"}
+            "sample": f"{w.name}: {reps} full training step(s) (T={w.T}) in fp64 on the host, "
+                      f"forward + backward through time + weight gradients, {dt:.1f} s"}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel sources changed since it was taken."""
+    import glob
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(root, "layer_rnn_forward_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("recurrent.hip", "gemm.hip"))
+    h = hashlib.sha256(src).hexdigest()[:16]
+    for path in glob.glob(os.path.join(root, "profiles", "traffic_*.txt")):
+        for line in open(path):
+            parts = line.split()
+            if len(parts) == 4 and parts[0] == "TRAFFIC" and parts[1] == h and parts[2] == kernel:
+                return int(parts[3])
+    return None
+
+
+def copy_calibration(torch, mib=1024, reps=3):
+    """A plain device-to-device copy of known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    n = mib * 1024 * 1024 // 4
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "reps": reps}))
 
 
 def main():
@@ -127,7 +158,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="lstm_ds2_bf16")
-    ap.add_argument("--cpu-sample-steps", type=int, default=30)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fp32", action="store_true")
     args = ap.parse_args()
@@ -137,6 +169,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import layer_rnn_forward_amd as R
     from layer_rnn_forward_amd import synth
 
@@ -178,7 +213,8 @@ def main():
     if dname in per_launch_flops and w.layers == 1:
         achieved = per_launch_flops[dname] / (dk["avg_us"] * 1e-6) / 1e12
         roof = {"kernel": dname, "bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 5),
+                "traffic": measured_traffic(dname) if w.name == "lstm_ds2_bf16" else None,
                 "avg_launch_us": dk["avg_us"],
                 "algorithmic_flops_per_launch": per_launch_flops[dname]}
     else:
@@ -219,7 +255,7 @@ def main():
                                    "fwd_ms": round(float(np.median(f_ms)), 4),
                                    "pct_mfma_peak": round(100.0 * v32 / (PEAK_TFLOPS["f32"] * 1000), 4)}
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_sample_steps)
+        out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
     print(json.dumps(out))
 
 
