@@ -104,8 +104,9 @@ rnn_status_t rnn_weights_size(rnn_handle_t h, int grad, size_t* bytes);
  * (grad = 0) or gradient (grad = 1) buffer.  Each tensor is stored row-major
  * in the PyTorch layout: W_ih [G*H, I_l], W_hh [G*H, H], b_ih [G*H],
  * b_hh [G*H], G = 1 (tanh), 4 (LSTM, rows i,f,g,o), 3 (GRU, rows r,z,n) --
- * the chunk order of the PyTorch GRU snippet in oneDNN issue #218.  Offsets
- * are multiples of 256 bytes.  Element type: matrices rnn_wtype_t of the
+ * the chunk order of the PyTorch GRU snippet in oneDNN issue #218.  The two
+ * directions of one tensor kind of a layer are adjacent (direction 1 right
+ * after direction 0); each such block starts on 256 bytes.  Element type: matrices rnn_wtype_t of the
  * handle (fp32 when grad = 1), biases fp32.  Errors: INVALID_ARG for
  * out-of-range layer/dir/which or NULL outputs. */
 rnn_status_t rnn_weight_offset(rnn_handle_t h, int grad, int layer, int dir, rnn_param_t which,
@@ -176,7 +177,8 @@ rnn_status_t rnn_device_status(rnn_handle_t h, void* stream, const void* ws, siz
 /* Per-kernel timing with HIP events recorded on the caller's stream around
  * every launch (off by default; adds one event pair per launch).  Kernel ids:
  * 0 input-projection GEMM, 1 recurrent forward sweep, 2 recurrent backward
- * sweep, 3 dX GEMM, 4 dW GEMMs, 5 workspace fill.  rnn_profile_read
+ * sweep, 3 dX GEMM, 4 dW GEMMs, 5 workspace fill, 6 operand preparation
+ * (bf16 conversion and transposes for the GEMMs).  rnn_profile_read
  * synchronises, accumulates the elapsed times of finished launches and
  * returns the launch count and total milliseconds for `kernel` since the last
  * reset (rnn_set_profiling(h, 1) resets). */

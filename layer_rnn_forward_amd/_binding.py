@@ -11,7 +11,7 @@ import torch
 MODES = {"rnn_tanh": 0, "lstm": 1, "gru": 2}
 WTYPES = {"f32": 0, "bf16": 1}
 SCHED_AUTO, SCHED_PERSISTENT, SCHED_STEPPED = 0, 1, 2
-KERNEL_NAMES = ["gemm_input", "recurrent_fwd", "recurrent_bwd", "gemm_dx", "gemm_dw", "fill"]
+KERNEL_NAMES = ["gemm_input", "recurrent_fwd", "recurrent_bwd", "gemm_dx", "gemm_dw", "fill", "prep"]
 STATUS_DEVICE_TIMEOUT = -7
 
 _LIB = None

@@ -45,21 +45,36 @@ __device__ __forceinline__ f32x4 mfma_chunk(const uint4& a, const uint4& b, f32x
 // K values per MFMA chunk: 32 (bf16) or 16 (fp32); each lane holds a quarter.
 template <bool BF16> constexpr int kchunk() { return BF16 ? 32 : 16; }
 
-__device__ __forceinline__ float sigmoidf_(float a) { return 1.0f / (1.0f + expf(-a)); }
+// Logistic and tanh from the hardware base-2 exponential and reciprocal
+// (v_exp_f32, v_rcp_f32, about 1 ulp each): sigmoid(a) = 1 / (1 + 2^(-a log2 e));
+// tanh(a) = sign(a) (1 - 2 / (1 + e^(2|a|))) for |a| >= 1/4, and its Taylor
+// series through the a^11 term below that (truncation < 1e-9 relative), which
+// avoids the cancellation of the identity near zero.
+__device__ __forceinline__ float sigmoidf_(float a) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * a));
+}
+__device__ __forceinline__ float tanhf_(float a) {
+  const float x = fabsf(a);
+  if (x < 0.25f) {
+    const float z = a * a;
+    const float p = -1382.0f / 155925.0f;
+    float r = p * z + 62.0f / 2835.0f;
+    r = r * z - 17.0f / 315.0f;
+    r = r * z + 2.0f / 15.0f;
+    r = r * z - 1.0f / 3.0f;
+    return a + a * z * r;
+  }
+  const float t = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(2.8853900817779268f * x));
+  return copysignf(t, a);
+}
 
 // ---------------------------------------------------------------- coherence
-// Agent-scope flags.  Producer: every wave drains its stores, the workgroup
-// barrier orders them before wave 0's agent release fence, then the flag is
-// stored.  Consumer: relaxed agent loads of the flags, agent acquire fence,
-// workgroup barrier, then ordinary loads of the data.
+// Agent-scope (sc1) loads and stores: coherent across the XCDs' L2 caches.
 __device__ __forceinline__ unsigned flag_load(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void flag_store(unsigned* p, unsigned v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void drain_stores() { __builtin_amdgcn_s_waitcnt(0); }
-__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 }  // namespace rnnk

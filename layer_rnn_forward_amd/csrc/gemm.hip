@@ -1,14 +1,21 @@
 // MFMA GEMM for the time-parallel products of the fused RNN (gfx950):
 //   * the hoisted input projection  GX = X W_ih^T + b   (all steps, both directions)
-//   * the data gradient             dX = dG W_ih
-//   * the weight gradients          dW = dG^T [X | 1]  (bias gradient as the ones column)
-// Computing every time step of the input projection in one product is the
-// "Combining Inputs" / "Combined GEMMs" rows of the cuDNN-5 optimisation table
-// in Keras issue #3692; the weight gradients batch all steps the same way.
+//   * the data gradient             dX = dG W_ih        (B = W_ih^T, pre-transposed)
+//   * the weight gradients          dW = dG^T [X | 1]   (A = dG^T, B = X^T, pre-transposed;
+//                                                        the bias gradient is the ones row of B)
+// Computing every time step of a projection in one product is the "Combining
+// Inputs" / "Combined GEMMs" rows of the cuDNN-5 optimisation table in Keras
+// issue #3692; giving every product the same operand layout is its "Matrix
+// pre-transposition" row.
 //
-// Tile 128x128, K step 32, 256 threads (2x2 waves of 64x64), 16x16 MFMA
-// tiles; operands converted to the compute type while staged into LDS
-// (double-buffered, one barrier per K step).
+// One layout only: C[m, n] = sum_k A[m, k] * B[n, k], both operands
+// K-contiguous, both in the compute type (bf16 with fp32 accumulation, or
+// fp32).  Tile 128x128, K step 32 (fp32) / 64 (bf16), 256 threads as 2x2
+// waves of 64x64 built from 16x16 MFMA tiles; operands staged through
+// double-buffered LDS with 16-byte loads and stores.  Tiles are numbered
+// m-major and dealt to the 8 XCDs in contiguous runs so that the tiles sharing
+// an A row-block share an L2.  Optional split-K writes fp32 partials that a
+// second kernel sums in a fixed order (deterministic).
 #include <type_traits>
 
 #include "device_util.h"
@@ -18,195 +25,98 @@ using namespace rnnk;
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32, NTHR = 256;
+constexpr int BM = 128, BN = 128, NTHR = 256;
 
 template <bool BF16>
-struct LdsT {
+struct Cfg {
   using T = typename std::conditional<BF16, uint16_t, float>::type;
-  static constexpr int STR = BF16 ? (BK + 8) : (BK + 4);  // padded row stride (elements)
+  static constexpr int BK = BF16 ? 64 : 32;          // k per LDS stage
+  static constexpr int EPV = 16 / sizeof(T);         // elements per 16-byte vector
+  static constexpr int STR = BK + EPV;               // padded LDS row (elements)
+  static constexpr int VPR = BK / EPV;               // 16-byte vectors per tile row
+  static constexpr int LPT = BM * VPR / NTHR;        // vectors per thread per operand
 };
 
-// Stage 4 consecutive values (along k) of one row into LDS.
 template <bool BF16>
-__device__ __forceinline__ void lds_put4(typename LdsT<BF16>::T* dst, const float (&v)[4]) {
-  if constexpr (BF16) {
-    uint2 w = make_uint2(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]));
-    *reinterpret_cast<uint2*>(dst) = w;
-  } else {
-    *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-  }
-}
-template <bool BF16>
-__device__ __forceinline__ void lds_put1(typename LdsT<BF16>::T* dst, float v) {
-  if constexpr (BF16) *dst = f2bf(v); else *dst = v;
+__device__ __forceinline__ uint4 load_vec(const typename Cfg<BF16>::T* row, int k, int K, bool rv,
+                                          bool vec_ok) {
+  using T = typename Cfg<BF16>::T;
+  constexpr int EPV = Cfg<BF16>::EPV;
+  if (rv && vec_ok && k + EPV <= K) return *reinterpret_cast<const uint4*>(row + k);
+  T v[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) v[e] = (rv && k + e < K) ? row[k + e] : (T)0;
+  return *reinterpret_cast<const uint4*>(v);
 }
 
-template <bool BF16, bool B_BF16, bool A_KMAJ, bool B_KN, int EPI>
-__global__ __launch_bounds__(NTHR) void gemm_kernel(const GemmParams p) {
-  static_assert(!B_BF16 || BF16, "bf16 B operand needs the bf16 path");
-  using ET = typename LdsT<BF16>::T;
-  constexpr int STR = LdsT<BF16>::STR;
-  __shared__ __attribute__((aligned(16))) ET As[2][BM * STR];
-  __shared__ __attribute__((aligned(16))) ET Bs[2][BN * STR];
+// Ones row for the bias gradient: EPV ones in the compute type, zero past K.
+template <bool BF16>
+__device__ __forceinline__ uint4 ones_vec(int k, int K) {
+  using T = typename Cfg<BF16>::T;
+  constexpr int EPV = Cfg<BF16>::EPV;
+  T v[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) {
+    if constexpr (BF16) v[e] = (k + e < K) ? (uint16_t)0x3f80 : (uint16_t)0;
+    else v[e] = (k + e < K) ? 1.f : 0.f;
+  }
+  return *reinterpret_cast<const uint4*>(v);
+}
+
+template <bool BF16, int EPI>
+__global__ __launch_bounds__(NTHR) void gemm_nt_kernel(const GemmParams p) {
+  using T = typename Cfg<BF16>::T;
+  constexpr int BK = Cfg<BF16>::BK, EPV = Cfg<BF16>::EPV, STR = Cfg<BF16>::STR;
+  constexpr int VPR = Cfg<BF16>::VPR, LPT = Cfg<BF16>::LPT;
+  __shared__ __attribute__((aligned(16))) T As[2][BM * STR];
+  __shared__ __attribute__((aligned(16))) T Bs[2][BN * STR];
 
   const int z = blockIdx.z;
-  const float* __restrict__ A = p.A[z];
   const int M = p.M, N = p.N, K = p.K;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const int ntiles = tm * tn;
+  const int nsplit = p.split_k;
+  // XCD-aware tile order: block b runs on XCD b % 8; give each XCD a contiguous
+  // run of m-major tiles.
+  const int total = ntiles * nsplit;
+  const int bid = blockIdx.x;
+  const int per = (total + 7) / 8;
+  const int lin = (bid % 8) * per + bid / 8;
+  if (lin >= total) return;
+  const int split = lin % nsplit;
+  const int tile = lin / nsplit;
+  const int m0 = (tile / tn) * BM, n0 = (tile % tn) * BN;
+  const int kper = ((K + nsplit - 1) / nsplit + BK - 1) / BK * BK;
+  const int kbeg = split * kper, kend = min(K, kbeg + kper);
+
+  const T* __restrict__ A = reinterpret_cast<const T*>(p.A[z]);
+  const T* __restrict__ Bm = reinterpret_cast<const T*>(p.B[z]);
+  const long long lda = p.lda, ldb = p.ldb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  const long long lda = p.lda, ldb = p.ldb;
-  const int n_ones = p.n_ones;
-  const int shift = p.b_shift[z], ak0 = p.b_alt_k0[z], ak1 = p.b_alt_k1[z];
-  const float* __restrict__ balt = p.b_alt[z];
+  const int fr = lane & 15, fq = lane >> 4;
+  const bool avec = p.a_vec, bvec = p.b_vec;
 
-  // --- staging registers
-  float ra[4][4];
-  float rbf[4][4];   // fp32 B
-  uint4 rbh[2];      // bf16 B (8 values each)
-
-  auto b_row_ptr = [&](int k) -> const float* {  // fp32 KN source row (remapped); null = zero row
-    if (k >= ak0 && k < ak1) return balt ? balt + (long long)(k - ak0) * p.ld_alt : nullptr;
-    return reinterpret_cast<const float*>(p.B[z]) + (long long)(k + shift) * ldb;
-  };
-
+  uint4 ra[LPT], rb[LPT];
   auto load_tile = [&](int k0) {
-    // A: 128 x 32 fp32
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int idx = tid + i * NTHR;
-      if constexpr (A_KMAJ) {
-        int r = idx >> 3, kq = (idx & 7) * 4;
-        int m = m0 + r, k = k0 + kq;
-        const float* src = A + (long long)m * lda + k;
-        if (p.a_vec && m < M && k + 3 < K) {
-          float4 v = *reinterpret_cast<const float4*>(src);
-          ra[i][0] = v.x; ra[i][1] = v.y; ra[i][2] = v.z; ra[i][3] = v.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ra[i][e] = (m < M && k + e < K) ? src[e] : 0.f;
-        }
-      } else {
-        int kr = idx >> 5, mq = (idx & 31) * 4;
-        int k = k0 + kr, m = m0 + mq;
-        const float* src = A + (long long)k * lda + m;
-        if (p.a_vec && k < K && m + 3 < M) {
-          float4 v = *reinterpret_cast<const float4*>(src);
-          ra[i][0] = v.x; ra[i][1] = v.y; ra[i][2] = v.z; ra[i][3] = v.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ra[i][e] = (k < K && m + e < M) ? src[e] : 0.f;
-        }
-      }
-    }
-    // B
-    if constexpr (B_BF16) {
-      const uint16_t* Bh = reinterpret_cast<const uint16_t*>(p.B[z]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int idx = tid + i * NTHR;
-        uint16_t v8[8];
-        if constexpr (!B_KN) {
-          int n = n0 + (idx >> 2), k = k0 + (idx & 3) * 8;
-          const uint16_t* src = Bh + (long long)n * ldb + k;
-          if (p.b_vec && n < N && k + 7 < K) {
-            rbh[i] = *reinterpret_cast<const uint4*>(src);
-            continue;
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v8[e] = (n < N && k + e < K) ? src[e] : (uint16_t)0;
-        } else {
-          int k = k0 + (idx >> 4), n = n0 + (idx & 15) * 8;
-          const uint16_t* src = Bh + (long long)k * ldb + n;
-          if (p.b_vec && k < K && n + 7 < N) {
-            rbh[i] = *reinterpret_cast<const uint4*>(src);
-            continue;
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v8[e] = (k < K && n + e < N) ? src[e] : (uint16_t)0;
-        }
-        rbh[i] = make_uint4(v8[0] | (v8[1] << 16), v8[2] | (v8[3] << 16), v8[4] | (v8[5] << 16),
-                            v8[6] | (v8[7] << 16));
-      }
-    } else {
-      const float* Bf = reinterpret_cast<const float*>(p.B[z]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int idx = tid + i * NTHR;
-        if constexpr (!B_KN) {
-          int n = n0 + (idx >> 3), k = k0 + (idx & 7) * 4;
-          const float* src = Bf + (long long)n * ldb + k;
-          if (p.b_vec && n < N && k + 3 < K) {
-            float4 v = *reinterpret_cast<const float4*>(src);
-            rbf[i][0] = v.x; rbf[i][1] = v.y; rbf[i][2] = v.z; rbf[i][3] = v.w;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rbf[i][e] = (n < N && k + e < K) ? src[e] : 0.f;
-          }
-        } else {
-          int k = k0 + (idx >> 5), n = n0 + (idx & 31) * 4;
-          const float* row = (k < K) ? b_row_ptr(k) : nullptr;
-          bool ones_in = (n_ones >= n && n_ones < n + 4);
-          if (p.b_vec && row && n + 3 < N && !ones_in) {
-            float4 v = *reinterpret_cast<const float4*>(row + n);
-            rbf[i][0] = v.x; rbf[i][1] = v.y; rbf[i][2] = v.z; rbf[i][3] = v.w;
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              int nn = n + e;
-              float v = 0.f;
-              if (k < K && nn < N) v = (nn == n_ones) ? 1.f : (row ? row[nn] : 0.f);
-              rbf[i][e] = v;
-            }
-          }
-        }
-      }
+    for (int i = 0; i < LPT; ++i) {
+      const int idx = tid + i * NTHR;
+      const int r = idx / VPR, kv = (idx % VPR) * EPV;
+      const int m = m0 + r, n = n0 + r, k = k0 + kv;
+      const bool mv = m < M, nv = n < N;
+      ra[i] = load_vec<BF16>(A + (long long)(mv ? m : 0) * lda, k, kend, mv, avec);
+      if (n == p.n_ones) rb[i] = ones_vec<BF16>(k, kend);
+      else rb[i] = load_vec<BF16>(Bm + (long long)(nv ? n : 0) * ldb, k, kend, nv && n != p.n_ones, bvec);
     }
   };
-
   auto store_tile = [&](int buf) {
-    ET* as = As[buf];
-    ET* bs = Bs[buf];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int idx = tid + i * NTHR;
-      if constexpr (A_KMAJ) {
-        int r = idx >> 3, kq = (idx & 7) * 4;
-        lds_put4<BF16>(as + r * STR + kq, ra[i]);
-      } else {
-        int kr = idx >> 5, mq = (idx & 31) * 4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lds_put1<BF16>(as + (mq + e) * STR + kr, ra[i][e]);
-      }
-    }
-    if constexpr (B_BF16) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int idx = tid + i * NTHR;
-        if constexpr (!B_KN) {
-          int n = idx >> 2, k8 = (idx & 3) * 8;
-          *reinterpret_cast<uint4*>(bs + n * STR + k8) = rbh[i];
-        } else {
-          int kr = idx >> 4, n8 = (idx & 15) * 8;
-          const uint32_t w[4] = {rbh[i].x, rbh[i].y, rbh[i].z, rbh[i].w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            bs[(n8 + e) * STR + kr] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int idx = tid + i * NTHR;
-        if constexpr (!B_KN) {
-          int n = idx >> 3, kq = (idx & 7) * 4;
-          lds_put4<BF16>(bs + n * STR + kq, rbf[i]);
-        } else {
-          int kr = idx >> 5, nq = (idx & 31) * 4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) lds_put1<BF16>(bs + (nq + e) * STR + kr, rbf[i][e]);
-        }
-      }
+    for (int i = 0; i < LPT; ++i) {
+      const int idx = tid + i * NTHR;
+      const int r = idx / VPR, kv = (idx % VPR) * EPV;
+      *reinterpret_cast<uint4*>(&As[buf][r * STR + kv]) = ra[i];
+      *reinterpret_cast<uint4*>(&Bs[buf][r * STR + kv]) = rb[i];
     }
   };
 
@@ -216,21 +126,20 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(const GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (K + BK - 1) / BK;
+  const int nk = (kend - kbeg + BK - 1) / BK;
   if (nk > 0) {
-    load_tile(0);
+    load_tile(kbeg);
     store_tile(0);
   }
   __syncthreads();
-  const int fr = lane & 15, fq = lane >> 4;
+  constexpr int CW = BF16 ? 32 : 16;        // k per MFMA chunk
+  constexpr int PER = CW / 4;               // k per lane per chunk
+  constexpr int CH = BK / CW;               // chunks per stage
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile((kt + 1) * BK);
-    const ET* as = As[buf];
-    const ET* bs = Bs[buf];
-    constexpr int CH = BF16 ? 1 : 2;           // MFMA chunks per K step
-    constexpr int CW = BF16 ? 32 : 16;         // k per chunk
-    constexpr int PER = CW / 4;                // k per lane per chunk
+    if (kt + 1 < nk) load_tile(kbeg + (kt + 1) * BK);
+    const T* as = As[buf];
+    const T* bs = Bs[buf];
 #pragma unroll
     for (int ch = 0; ch < CH; ++ch) {
       uint4 af[4], bfr[4];
@@ -250,6 +159,23 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(const GemmParams p) {
   }
 
   // --- epilogue
+  if (nsplit > 1) {
+    // fp32 partial tile for the fixed-order reduction
+    float* part = p.partial + ((size_t)z * nsplit + split) * (size_t)M * N;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int n = n0 + wn + nt * 16 + fr;
+        if (n >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm + mt * 16 + fq * 4 + r;
+          if (m < M) part[(size_t)m * N + n] = acc[mt][nt][r];
+        }
+      }
+    return;
+  }
   float* __restrict__ C = p.C[z];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
@@ -268,7 +194,7 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(const GemmParams p) {
         if (m >= M) continue;
         const float v = acc[mt][nt][r];
         if constexpr (EPI == EPI_DW) {
-          if (n == n_ones) p.cbias[z][m] = v;
+          if (n == p.n_ones) p.cbias[z][m] = v;
           else C[(long long)m * p.ldc + n] = v;
         } else {
           C[(long long)m * p.ldc + n] = v + badd;
@@ -278,31 +204,47 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(const GemmParams p) {
   }
 }
 
-template <bool BF16, bool B_BF16, bool A_KMAJ, bool B_KN, int EPI>
+// Fixed-order sum of the split-K partials, then the dW epilogue.
+__global__ void splitk_reduce_kernel(const GemmParams p) {
+  const int z = blockIdx.y;
+  const size_t MN = (size_t)p.M * p.N;
+  const float* part = p.partial + (size_t)z * p.split_k * MN;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < MN; i += (size_t)gridDim.x * blockDim.x) {
+    float v = 0.f;
+    for (int s = 0; s < p.split_k; ++s) v += part[(size_t)s * MN + i];
+    const int m = (int)(i / p.N), n = (int)(i % p.N);
+    if (n == p.n_ones) p.cbias[z][m] = v;
+    else p.C[z][(long long)m * p.ldc + n] = v;
+  }
+}
+
+template <bool BF16, int EPI>
 hipError_t launch_one(const GemmParams& p, int batches, hipStream_t s) {
-  dim3 grid((p.N + BN - 1) / BN, (p.M + BM - 1) / BM, batches);
-  hipLaunchKernelGGL((gemm_kernel<BF16, B_BF16, A_KMAJ, B_KN, EPI>), grid, dim3(NTHR), 0, s, p);
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.split_k;
+  const int grid = (tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_nt_kernel<BF16, EPI>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.split_k <= 1) return e;
+  size_t mn = (size_t)p.M * p.N;
+  unsigned blocks = (unsigned)std::min<size_t>((mn + 255) / 256, 4096);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks, batches), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t rnn_launch_gemm(const GemmParams& p, int bf16_compute, int b_bf16, int a_kmajor,
-                           int b_kn, int epi, int batches, hipStream_t s) {
+hipError_t rnn_launch_gemm(const GemmParams& p, int bf16, int epi, int batches, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0 || batches <= 0) return hipSuccess;
-  if (batches > 2) return hipErrorInvalidValue;
-  // The combinations the operator uses.
-  if (bf16_compute && b_bf16 && a_kmajor && !b_kn && epi == EPI_BIAS)
-    return launch_one<true, true, true, false, EPI_BIAS>(p, batches, s);
-  if (!bf16_compute && !b_bf16 && a_kmajor && !b_kn && epi == EPI_BIAS)
-    return launch_one<false, false, true, false, EPI_BIAS>(p, batches, s);
-  if (bf16_compute && b_bf16 && a_kmajor && b_kn && epi == EPI_STORE)
-    return launch_one<true, true, true, true, EPI_STORE>(p, batches, s);
-  if (!bf16_compute && !b_bf16 && a_kmajor && b_kn && epi == EPI_STORE)
-    return launch_one<false, false, true, true, EPI_STORE>(p, batches, s);
-  if (bf16_compute && !b_bf16 && !a_kmajor && b_kn && epi == EPI_DW)
-    return launch_one<true, false, false, true, EPI_DW>(p, batches, s);
-  if (!bf16_compute && !b_bf16 && !a_kmajor && b_kn && epi == EPI_DW)
-    return launch_one<false, false, false, true, EPI_DW>(p, batches, s);
+  if (batches > 2 || p.split_k < 1 || (p.split_k > 1 && (epi != EPI_DW || !p.partial)))
+    return hipErrorInvalidValue;
+  if (bf16) {
+    if (epi == EPI_BIAS) return launch_one<true, EPI_BIAS>(p, batches, s);
+    if (epi == EPI_STORE) return launch_one<true, EPI_STORE>(p, batches, s);
+    if (epi == EPI_DW) return launch_one<true, EPI_DW>(p, batches, s);
+  } else {
+    if (epi == EPI_BIAS) return launch_one<false, EPI_BIAS>(p, batches, s);
+    if (epi == EPI_STORE) return launch_one<false, EPI_STORE>(p, batches, s);
+    if (epi == EPI_DW) return launch_one<false, EPI_DW>(p, batches, s);
+  }
   return hipErrorInvalidValue;
 }

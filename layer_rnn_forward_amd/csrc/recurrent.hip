@@ -23,7 +23,7 @@
 // formulas to the reserved forward intermediates.
 //
 // Exchange protocol.  The vector one step produces (h, or dG_h) goes into a
-// ring with one entry per step, so no address is ever written twice within a
+// ring with one entry per step, so no address is written twice within a
 // sweep.  Each producer owns whole 128-byte lines of an entry (its slice:
 // rows x units, zero-padded), writes them with agent-scope stores, waits for
 // their completion and then stores its step flag (agent scope).  A consumer
@@ -31,6 +31,8 @@
 // loads: no cache can hold a stale copy of a line that was never read before
 // its single writer completed, so no cache write-back or invalidation is
 // needed per step, and the workgroups of one XCD share the entry through L2.
+// Every wait is bounded; an expired wait sets the error word and every
+// workgroup leaves the sweep.
 #include <type_traits>
 
 #include "device_util.h"
@@ -59,6 +61,23 @@ __device__ __forceinline__ uint4 pack_frag(const uint32_t (&v)[BF16 ? 8 : 4]) {
     return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
   else
     return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 lds_load16(const char __attribute__((address_space(3)))* p) {
+  const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void ring_store(char* base, size_t off, float v) {
+  if (v != v) v = __uint_as_float(0x7FC00000u);   // canonical NaN: never the sentinel
+  if constexpr (BF16)
+    __hip_atomic_store(reinterpret_cast<uint16_t*>(base + off), f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    __hip_atomic_store(reinterpret_cast<float*>(base + off), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wave 0 polls the flags of up to two groups (ranges of nwg workgroups); the
@@ -99,27 +118,17 @@ __device__ bool wait_groups(const unsigned* flags, unsigned* err, unsigned spin_
 // Every wave waits for completion of its stores (the ring stores are agent
 // scope), then one thread publishes the flag.
 __device__ __forceinline__ void publish(unsigned* flags, unsigned v) {
-  drain_stores();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) flag_store(flags + (size_t)blockIdx.x * kFlagStride, v);
 }
 
-template <bool BF16>
-__device__ __forceinline__ void ring_store(char* base, size_t off, float v) {
-  if constexpr (BF16)
-    __hip_atomic_store(reinterpret_cast<uint16_t*>(base + off), f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    __hip_atomic_store(reinterpret_cast<float*>(base + off), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// MFMA over the K chunks this wave holds: A fragments are gathered from ring
-// entries by `addr(k0, row, valid&)` (16 bytes per lane), all loads of a batch
-// issued before its MFMAs (branch-free; invalid lanes load a valid address and
-// are zeroed) so that their latencies overlap.
-template <bool BF16, int NT, int MT, int KPW, int NW, class AddrF>
+// MFMA over the K chunks this wave holds, A fragments (16 bytes per lane) from
+// `load(k0, row, valid)`; all loads of a batch are issued before its MFMAs.
+template <bool BF16, int NT, int MT, int KPW, int NW, class LoadF>
 __device__ __forceinline__ void mfma_sweep(f32x4 (&acc)[MT][NT], const uint4 (&wf)[KPW][NT],
                                            int wave, int fr, int fq, int nch, int Bact,
-                                           AddrF addr) {
+                                           LoadF load) {
   constexpr int KC = kchunk<BF16>();
   constexpr int PER = KC / 4;
   constexpr int KB = KPW < 8 ? KPW : 8;
@@ -137,10 +146,7 @@ __device__ __forceinline__ void mfma_sweep(f32x4 (&acc)[MT][NT], const uint4 (&w
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int row = mt * 16 + fr;
-        bool v = gc < nch && row < Bact;
-        const char* a = addr(k0, row, v);
-        const uint4 t = *reinterpret_cast<const uint4*>(a);
-        av[kk][mt] = v ? t : make_uint4(0u, 0u, 0u, 0u);
+        av[kk][mt] = load(k0, row, gc < nch && row < Bact);
       }
     }
 #pragma unroll
@@ -150,6 +156,17 @@ __device__ __forceinline__ void mfma_sweep(f32x4 (&acc)[MT][NT], const uint4 (&w
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_chunk<BF16>(av[kk][mt], wf[kb + kk][nt], acc[mt][nt]);
   }
+}
+
+// Copy `bytes` (a multiple of 1024) of a ring entry into LDS with direct
+// global->LDS loads: each wave moves 1 KB per instruction (lane i -> +16*i);
+// nothing goes through registers, so the whole entry is in flight at once.
+__device__ __forceinline__ void stage_to_lds(char __attribute__((address_space(3)))* dst, const char* src,
+                                             int bytes, int wave, int nw, int lane) {
+  for (int c = wave; c < bytes / 1024; c += nw)
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1)))*)(src + (size_t)c * 1024 + lane * 16),
+        (void __attribute__((address_space(3)))*)(dst + c * 1024), 16, 0, 0);
 }
 
 // ====================================================================== fwd
@@ -193,7 +210,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   const int DC = p.D * p.nchunk;
 
   char* ring = reinterpret_cast<char*>(p.xch) + (size_t)grp * p.ring_group;
-  const char* ring_below = inproj ? reinterpret_cast<const char*>(p.xch) + (size_t)(grp - DC) * p.ring_group : nullptr;
+  const char* ring_below = inproj ? reinterpret_cast<const char*>(p.xch) + (size_t)(grp - DC) * p.ring_group : ring;
   const void* wih = p.w_ih[li];
   const void* whh = p.w_hh[li];
 
@@ -265,14 +282,19 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   if (inproj) { wgroups[0] = grp - DC; wgroups[1] = grp; nwait = 2; }
 
   const size_t ystride_t = (size_t)B * D * H;
+  const int pslice = p.slice;
   for (int s = max(p.s_begin, 0); s < p.s_end; ++s) {
     const int t_rel = p.wavefront ? s - li : s;
     const bool active = t_rel >= 0 && t_rel < T;
     const int t = (d == 0) ? t_rel : T - 1 - t_rel;
+    if (!active) {   // uniform across the workgroup; still publishes the step
+      if (p.persistent) publish(p.flags, (unsigned)(s + 2));
+      continue;
+    }
 
-    // prefetch the input part of the pre-activations (independent of other workgroups)
+    // input part of the pre-activations (independent of other workgroups)
     float gxv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (active && qv) {
+    if (qv) {
       if (!inproj) {
         const float* g = p.gx + ((size_t)t * B + qbg) * D * GH + (size_t)d * GH + qu;
 #pragma unroll
@@ -292,81 +314,79 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
       }
     }
     float bhn = 0.f;
-    if (MODE == MODE_GRU && !inproj && active && qv) bhn = p.b_hh[li][(size_t)d * GH + 2 * H + qu];
+    if (MODE == MODE_GRU && !inproj && qv) bhn = p.b_hh[li][(size_t)d * GH + 2 * H + qu];
 
     if (p.persistent) {
       if (!wait_groups(p.flags, p.err, p.spin_limit, wgroups, nwait, p.nwg, (unsigned)(s + 1), &s_flag))
         return;
     }
-
-    if (active) {
-      f32x4 acc[MT][NT];
-      const char* eh = ring + (size_t)s * p.ring_step;
-      const char* ex = inproj ? ring_below + (size_t)s * p.ring_step : nullptr;
-      const int pslice = p.slice;
-      mfma_sweep<BF16, NT, MT, KPW, NW>(acc, wf, wave, fr, fq, nch, Bact,
-          [&](int k0, int row, bool& v) -> const char* {
-            const bool xpart = k0 < Kx;
-            const int kk = xpart ? k0 : k0 - Kx;
-            v = v && kk < Kh;
-            const int pp = kk / U, j0 = kk - pp * U;
-            const char* base = xpart ? ex : eh;
-            return v ? base + (size_t)pp * pslice + ((size_t)row * U + j0) * ES : eh;
-          });
+    f32x4 acc[MT][NT];
+    const char* eh = ring + (size_t)s * p.ring_step;
+    const char* ex = ring_below + (size_t)s * p.ring_step;
+    mfma_sweep<BF16, NT, MT, KPW, NW>(acc, wf, wave, fr, fq, nch, Bact,
+        [&](int k0, int row, bool v) -> uint4 {
+          const bool xpart = k0 < Kx;
+          const int kk = xpart ? k0 : k0 - Kx;
+          v = v && kk < Kh;
+          const int pp = kk / U, j0 = kk - pp * U;
+          const char* a = (xpart ? ex : eh) + (v ? pp * pslice + (row * U + j0) * ES : 0);
+          const uint4 t4 = *reinterpret_cast<const uint4*>(a);
+          return v ? t4 : make_uint4(0u, 0u, 0u, 0u);
+        });
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) red[wave][mt * 16 + fq * 4 + r][nt * 16 + fr] = acc[mt][nt][r];
-      __syncthreads();
-
-      float hnew = 0.f;
-      if (qv) {
-        float pre[4];
-#pragma unroll
-        for (int gb = 0; gb < 4; ++gb) {
-          float v = 0.f;
-          if (gb < GB) {
-#pragma unroll
-            for (int w = 0; w < NW; ++w) v += red[w][qb][gb * U + qj];
-          }
-          pre[gb] = v;
-        }
-        const float hprev = sh_h[qb * NCOL + qj];
-        float* res = (p.training && R > 0)
-                         ? p.reserve[li] + (((size_t)d * T + t) * B + qbg) * R * H + qu
-                         : nullptr;
-        if (MODE == MODE_LSTM) {
-          const float ig = sigmoidf_(pre[0] + gxv[0]);
-          const float fg = sigmoidf_(pre[1] + gxv[1]);
-          const float gg = tanhf(pre[2] + gxv[2]);
-          const float og = sigmoidf_(pre[3] + gxv[3]);
-          const float cn = fg * sh_c[qb * NCOL + qj] + ig * gg;
-          hnew = og * tanhf(cn);
-          sh_c[qb * NCOL + qj] = cn;
-          if (res) {
-            res[0] = ig; res[H] = fg; res[2 * H] = gg; res[3 * H] = og; res[4 * H] = cn;
-          }
-        } else if (MODE == MODE_GRU) {
-          const float rg = sigmoidf_(pre[0] + gxv[0]);
-          const float zg = sigmoidf_(pre[1] + gxv[1]);
-          float ghn, gin;
-          if (inproj) { gin = pre[2] + gxv[2]; ghn = pre[3] + gxv[3]; }
-          else { gin = gxv[2]; ghn = pre[2] + bhn; }
-          const float ng = tanhf(gin + rg * ghn);
-          hnew = (1.f - zg) * ng + zg * hprev;
-          if (res) { res[0] = rg; res[H] = zg; res[2 * H] = ng; res[3 * H] = ghn; }
-        } else {
-          hnew = tanhf(pre[0] + gxv[0]);
-        }
-        sh_h[qb * NCOL + qj] = hnew;
-        p.y[li][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = hnew;
-      }
-      if (qw) ring_store<BF16>(ring + (size_t)(s + 1) * p.ring_step, my_off, hnew);
-    }
-    if (p.persistent) publish(p.flags, (unsigned)(s + 2));
+        for (int r = 0; r < 4; ++r) red[wave][mt * 16 + fq * 4 + r][nt * 16 + fr] = acc[mt][nt][r];
     __syncthreads();
+
+    float hnew = 0.f;
+    if (qv) {
+      float pre[4];
+#pragma unroll
+      for (int gb = 0; gb < 4; ++gb) {
+        float v = 0.f;
+        if (gb < GB) {
+#pragma unroll
+          for (int w = 0; w < NW; ++w) v += red[w][qb][gb * U + qj];
+        }
+        pre[gb] = v;
+      }
+      const float hprev = sh_h[qb * NCOL + qj];
+      float* res = (p.training && R > 0)
+                       ? p.reserve[li] + (((size_t)d * T + t) * B + qbg) * R * H + qu
+                       : nullptr;
+      if (MODE == MODE_LSTM) {
+        const float ig = sigmoidf_(pre[0] + gxv[0]);
+        const float fg = sigmoidf_(pre[1] + gxv[1]);
+        const float gg = tanhf_(pre[2] + gxv[2]);
+        const float og = sigmoidf_(pre[3] + gxv[3]);
+        const float cn = fg * sh_c[qb * NCOL + qj] + ig * gg;
+        hnew = og * tanhf_(cn);
+        sh_c[qb * NCOL + qj] = cn;
+        if (res) {
+          res[0] = ig; res[H] = fg; res[2 * H] = gg; res[3 * H] = og; res[4 * H] = cn;
+        }
+      } else if (MODE == MODE_GRU) {
+        const float rg = sigmoidf_(pre[0] + gxv[0]);
+        const float zg = sigmoidf_(pre[1] + gxv[1]);
+        float ghn, gin;
+        if (inproj) { gin = pre[2] + gxv[2]; ghn = pre[3] + gxv[3]; }
+        else { gin = gxv[2]; ghn = pre[2] + bhn; }
+        const float ng = tanhf_(gin + rg * ghn);
+        hnew = (1.f - zg) * ng + zg * hprev;
+        if (res) { res[0] = rg; res[H] = zg; res[2 * H] = ng; res[3 * H] = ghn; }
+      } else {
+        hnew = tanhf_(pre[0] + gxv[0]);
+      }
+      sh_h[qb * NCOL + qj] = hnew;
+    }
+    // the exchange store first: it is what the other workgroups wait for
+    if (qw) ring_store<BF16>(ring + (size_t)(s + 1) * p.ring_step, my_off, hnew);
+    if (qv) p.y[li][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = hnew;
+    if (p.persistent) publish(p.flags, (unsigned)(s + 2));
+    __syncthreads();   // red and sh_* are reused by the next step
   }
 
   if (qv) {
@@ -455,9 +475,11 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
     }
   }
   __syncthreads();
-  const int wgroups[2] = {grp, grp};
 
+  const int wgroups[2] = {grp, grp};
   const size_t ystride_t = (size_t)B * D * H;
+  const int pslice = p.slice;
+  const int rs = (int)p.ring_step;
   for (int s = p.s_begin; s < p.s_end; ++s) {
     const bool final_phase = (s == T);
     const int t = (d == 0) ? T - 1 - s : s;
@@ -483,19 +505,36 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
 
     float dhrec = 0.f;
     if (s > 0) {
+      f32x4 acc[MT][NT];
+      const char* e = ring + (size_t)s * p.ring_step;
+      auto frag_off = [&](int k0, int row, bool& v) -> int {
+        const int g = k0 / Kh, uu = k0 - g * Kh;
+        v = v && g < G;
+        const int pp = uu / U, j0 = uu - pp * U;
+        return pp * pslice + ((row * G + g) * U + j0) * ES;
+      };
       if (p.persistent) {
         if (!wait_groups(p.flags, p.err, p.spin_limit, wgroups, 1, p.nwg, (unsigned)s, &s_flag)) return;
       }
-      f32x4 acc[MT][NT];
-      const char* e = ring + (size_t)s * p.ring_step;
-      const int pslice = p.slice;
-      mfma_sweep<BF16, NT, MT, KPW, NW>(acc, wf, wave, fr, fq, nch, Bact,
-          [&](int k0, int row, bool& v) -> const char* {
-            const int g = k0 / Kh, uu = k0 - g * Kh;
-            v = v && g < G;
-            const int pp = uu / U, j0 = uu - pp * U;
-            return v ? e + (size_t)pp * pslice + (((size_t)row * G + g) * U + j0) * ES : e;
-          });
+      if (p.stage) {
+        auto lds = (char __attribute__((address_space(3)))*)(dyn_lds);
+        stage_to_lds(lds, e, rs, wave, NW, lane);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        mfma_sweep<BF16, NT, MT, KPW, NW>(acc, wf, wave, fr, fq, nch, Bact,
+            [&](int k0, int row, bool v) -> uint4 {
+              const int off = frag_off(k0, row, v);
+              const uint4 t4 = lds_load16(lds + (v ? off : 0));
+              return v ? t4 : make_uint4(0u, 0u, 0u, 0u);
+            });
+      } else {
+        mfma_sweep<BF16, NT, MT, KPW, NW>(acc, wf, wave, fr, fq, nch, Bact,
+            [&](int k0, int row, bool v) -> uint4 {
+              const int off = frag_off(k0, row, v);
+              const uint4 t4 = *reinterpret_cast<const uint4*>(e + (v ? off : 0));
+              return v ? t4 : make_uint4(0u, 0u, 0u, 0u);
+            });
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -521,7 +560,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
         float ncarry = 0.f;
         if (MODE == MODE_LSTM) {
           const float ig = rv[0], fg = rv[1], gg = rv[2], og = rv[3], cc = rv[4];
-          const float tau = tanhf(cc);
+          const float tau = tanhf_(cc);
           const float d_o = dh * tau;
           const float dc = sh_dc[qb * NCOL + qj] + dh * og * (1.f - tau * tau);
           dgi[0] = dc * gg * ig * (1.f - ig);
@@ -548,21 +587,31 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
           dgh[0] = dgi[0];
         }
         sh_dh[qb * NCOL + qj] = ncarry;
-        const size_t row = ((size_t)t * B + qbg) * D * GH + (size_t)d * GH + qu;
+      }
+      // the exchange stores first: they are what the other workgroups wait for
+      if (qw) {
+        char* en = ring + (size_t)(s + 1) * p.ring_step;
+#pragma unroll
+        for (int g = 0; g < G; ++g) ring_store<BF16>(en, my_off + (size_t)g * U * ES, dgh[g]);
+      }
+      if (qv) {
+        // gate gradients for the dX product ([T*B, D*G*H]) and, transposed
+        // ([D*G*H, T*B]), for the weight-gradient products
+        using X = XT<BF16>;
+        const size_t rowi = (size_t)t * B + qbg;
+        const size_t col0 = (size_t)d * GH + qu;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          p.dgi[row + (size_t)g * H] = dgi[g];
-          if (MODE == MODE_GRU) p.dgh[row + (size_t)g * H] = dgh[g];
+          const size_t col = col0 + (size_t)g * H;
+          const X vi = to_x<BF16>(dgi[g]);
+          reinterpret_cast<X*>(p.dg)[rowi * p.dg_ld + col] = vi;
+          reinterpret_cast<X*>(p.dgT)[col * p.tb_ld + rowi] = vi;
+          if (MODE == MODE_GRU) reinterpret_cast<X*>(p.dghT)[col * p.tb_ld + rowi] = to_x<BF16>(dgh[g]);
         }
-      }
-      if (qw) {
-        char* e = ring + (size_t)(s + 1) * p.ring_step;
-#pragma unroll
-        for (int g = 0; g < G; ++g) ring_store<BF16>(e, my_off + (size_t)g * U * ES, dgh[g]);
       }
     }
     if (p.persistent && !final_phase) publish(p.flags, (unsigned)(s + 1));
-    __syncthreads();
+    __syncthreads();   // red and sh_* are reused by the next step
   }
   if (qv && p.s_end <= T) {
     p.st_dh[sidx] = sh_dh[qb * NCOL + qj];
@@ -573,16 +622,18 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
 // ===================================================================== misc
 struct FillArgs {
   void* p[8];
-  size_t n[8];   // bytes (multiple of 4)
+  size_t n[8];      // bytes (multiple of 4)
+  uint32_t v[8];    // 32-bit fill pattern
   int count;
 };
 
-__global__ void fill_zero_kernel(const FillArgs a) {
+__global__ void fill_kernel(const FillArgs a) {
   for (int i = 0; i < a.count; ++i) {
     uint32_t* dst = reinterpret_cast<uint32_t*>(a.p[i]);
     const size_t nw = a.n[i] / 4;
+    const uint32_t v = a.v[i];
     for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < nw; k += (size_t)gridDim.x * blockDim.x)
-      dst[k] = 0u;
+      dst[k] = v;
   }
 }
 
@@ -595,16 +646,24 @@ __global__ void copy_kernel(float* dst, const float* src, size_t n) {
 template <int MODE, bool BF16, int NT, int MT, int KPW, int NW>
 struct FwdK {
   static const void* fn() { return reinterpret_cast<const void*>(&rnn_fwd_kernel<MODE, BF16, NT, MT, KPW, NW>); }
-  static hipError_t launch(const FwdParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((rnn_fwd_kernel<MODE, BF16, NT, MT, KPW, NW>), dim3(grid), dim3(NW * 64), 0, s, p);
+  static hipError_t launch(const FwdParams& p, int grid, size_t lds, hipStream_t s) {
+    if (lds > 0) {
+      hipError_t e = hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((rnn_fwd_kernel<MODE, BF16, NT, MT, KPW, NW>), dim3(grid), dim3(NW * 64), lds, s, p);
     return hipGetLastError();
   }
 };
 template <int MODE, bool BF16, int NT, int MT, int KPW, int NW>
 struct BwdK {
   static const void* fn() { return reinterpret_cast<const void*>(&rnn_bwd_kernel<MODE, BF16, NT, MT, KPW, NW>); }
-  static hipError_t launch(const BwdParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((rnn_bwd_kernel<MODE, BF16, NT, MT, KPW, NW>), dim3(grid), dim3(NW * 64), 0, s, p);
+  static hipError_t launch(const BwdParams& p, int grid, size_t lds, hipStream_t s) {
+    if (lds > 0) {
+      hipError_t e = hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((rnn_bwd_kernel<MODE, BF16, NT, MT, KPW, NW>), dim3(grid), dim3(NW * 64), lds, s, p);
     return hipGetLastError();
   }
 };
@@ -635,13 +694,35 @@ struct BwdK {
   X(M, BF, 1, 2, 32, 8)           \
   X(M, BF, 1, 1, 32, 8)
 
-template <class KFN>
-int max_resident(const void* f, int nthr) {
+int max_resident(const void* f, int nthr, size_t lds) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, nthr, 0) != hipSuccess) return 0;
+  if (lds > 0) {
+    // static + dynamic LDS must fit the per-workgroup limit; failed runtime
+    // calls are cleared so that no error state leaks to the caller
+    int dev = 0, lim = 0;
+    hipFuncAttributes fa{};
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+        hipFuncGetAttributes(&fa, f) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    if (fa.sharedSizeBytes + lds > (size_t)lim) return 0;
+    if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+  }
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, nthr, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
   int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
   return per_cu * ncu;
 }
 
@@ -650,15 +731,15 @@ int max_resident(const void* f, int nthr) {
 #define RNN_MATCH(c, NT_, MT_, KPW_, NW_) ((c).nt == NT_ && (c).mt == MT_ && (c).kpw == KPW_ && (c).nwaves == NW_)
 
 #define FWD_LAUNCH_CASE(M, BF, NT_, MT_, KPW_, NW_) \
-  if (mode == M && (bf16 != 0) == BF && RNN_MATCH(c, NT_, MT_, KPW_, NW_)) return FwdK<M, BF, NT_, MT_, KPW_, NW_>::launch(p, grid, s);
+  if (mode == M && (bf16 != 0) == BF && RNN_MATCH(c, NT_, MT_, KPW_, NW_)) return FwdK<M, BF, NT_, MT_, KPW_, NW_>::launch(p, grid, lds, s);
 #define FWD_RES_CASE(M, BF, NT_, MT_, KPW_, NW_) \
-  if (mode == M && (bf16 != 0) == BF && RNN_MATCH(c, NT_, MT_, KPW_, NW_)) return max_resident<void>(FwdK<M, BF, NT_, MT_, KPW_, NW_>::fn(), NW_ * 64);
+  if (mode == M && (bf16 != 0) == BF && RNN_MATCH(c, NT_, MT_, KPW_, NW_)) return max_resident(FwdK<M, BF, NT_, MT_, KPW_, NW_>::fn(), NW_ * 64, lds);
 #define FWD_SUP_CASE(M, BF, NT_, MT_, KPW_, NW_) \
   if (mode == M && (bf16 != 0) == BF && RNN_MATCH(c, NT_, MT_, KPW_, NW_)) return true;
 #define BWD_LAUNCH_CASE(M, BF, NT_, MT_, KPW_, NW_) \
-  if (mode == M && (bf16 != 0) == BF && RNN_MATCH(c, NT_, MT_, KPW_, NW_)) return BwdK<M, BF, NT_, MT_, KPW_, NW_>::launch(p, grid, s);
+  if (mode == M && (bf16 != 0) == BF && RNN_MATCH(c, NT_, MT_, KPW_, NW_)) return BwdK<M, BF, NT_, MT_, KPW_, NW_>::launch(p, grid, lds, s);
 #define BWD_RES_CASE(M, BF, NT_, MT_, KPW_, NW_) \
-  if (mode == M && (bf16 != 0) == BF && RNN_MATCH(c, NT_, MT_, KPW_, NW_)) return max_resident<void>(BwdK<M, BF, NT_, MT_, KPW_, NW_>::fn(), NW_ * 64);
+  if (mode == M && (bf16 != 0) == BF && RNN_MATCH(c, NT_, MT_, KPW_, NW_)) return max_resident(BwdK<M, BF, NT_, MT_, KPW_, NW_>::fn(), NW_ * 64, lds);
 #define BWD_SUP_CASE(M, BF, NT_, MT_, KPW_, NW_) \
   if (mode == M && (bf16 != 0) == BF && RNN_MATCH(c, NT_, MT_, KPW_, NW_)) return true;
 
@@ -667,12 +748,12 @@ int max_resident(const void* f, int nthr) {
   CFG(X, MODE_GRU, false) CFG(X, MODE_GRU, true)
 
 hipError_t rnn_launch_fwd(const FwdParams& p, int mode, int bf16, const RecConfig& c, int grid,
-                          hipStream_t s) {
+                          size_t lds, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   RNN_ALL_MODES(RNN_FWD_CONFIGS, FWD_LAUNCH_CASE)
   return hipErrorInvalidValue;
 }
-int rnn_fwd_max_resident(int mode, int bf16, const RecConfig& c) {
+int rnn_fwd_max_resident(int mode, int bf16, const RecConfig& c, size_t lds) {
   RNN_ALL_MODES(RNN_FWD_CONFIGS, FWD_RES_CASE)
   return 0;
 }
@@ -681,12 +762,12 @@ bool rnn_fwd_config_supported(int mode, int bf16, const RecConfig& c) {
   return false;
 }
 hipError_t rnn_launch_bwd(const BwdParams& p, int mode, int bf16, const RecConfig& c, int grid,
-                          hipStream_t s) {
+                          size_t lds, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   RNN_ALL_MODES(RNN_BWD_CONFIGS, BWD_LAUNCH_CASE)
   return hipErrorInvalidValue;
 }
-int rnn_bwd_max_resident(int mode, int bf16, const RecConfig& c) {
+int rnn_bwd_max_resident(int mode, int bf16, const RecConfig& c, size_t lds) {
   RNN_ALL_MODES(RNN_BWD_CONFIGS, BWD_RES_CASE)
   return 0;
 }
@@ -695,7 +776,8 @@ bool rnn_bwd_config_supported(int mode, int bf16, const RecConfig& c) {
   return false;
 }
 
-hipError_t rnn_launch_fill(void* const* ptrs, const size_t* bytes, int n, hipStream_t s) {
+hipError_t rnn_launch_fill(void* const* ptrs, const size_t* bytes, const uint32_t* values, int n,
+                           hipStream_t s) {
   FillArgs a{};
   size_t total = 0;
   int k = 0;
@@ -704,6 +786,7 @@ hipError_t rnn_launch_fill(void* const* ptrs, const size_t* bytes, int n, hipStr
     if (k == 8) return hipErrorInvalidValue;
     a.p[k] = ptrs[i];
     a.n[k] = bytes[i];
+    a.v[k] = values ? values[i] : 0u;
     total += bytes[i];
     ++k;
   }
@@ -712,7 +795,7 @@ hipError_t rnn_launch_fill(void* const* ptrs, const size_t* bytes, int n, hipStr
   size_t blocks = (total / 4 + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ int env_int(const char* name, int dflt) {
   return std::atoi(v);
 }
 
-enum KernelId { K_GEMM_IN = 0, K_FWD = 1, K_BWD = 2, K_GEMM_DX = 3, K_GEMM_DW = 4, K_FILL = 5, K_NKERNELS = 6 };
+enum KernelId { K_GEMM_IN = 0, K_FWD = 1, K_BWD = 2, K_GEMM_DX = 3, K_GEMM_DW = 4, K_FILL = 5, K_PREP = 6, K_NKERNELS = 7 };
 
 struct ProfPending {
   hipEvent_t a, b;
@@ -44,6 +44,7 @@ struct SweepPlan {
   RecConfig cfg{};
   int U = 0, nwg = 0, groups = 0, grid = 0;
   bool persistent = false;
+  size_t lds = 0;   // dynamic LDS for staging ring entries (0: fragments read from global)
 };
 
 struct Plan {
@@ -60,9 +61,11 @@ struct Plan {
   size_t off_yin = 0, yin_slot = 0;
   int yin_slots = 0;
   size_t off_res = 0, res_layer = 0;
-  size_t off_dgi = 0, dg_layer = 0;
-  size_t off_dgh = 0;
+  // gate gradients in the compute type: dG [T*B][dg_ld], dG^T [D*G*H][tb_ld]
+  size_t off_dg = 0, off_dgT = 0, off_dghT = 0, dg_layer = 0, dgT_layer = 0;
+  int dg_ld = 0, tb_ld = 0;
   size_t off_dy = 0, dy_slot = 0;
+  size_t off_scr = 0, scr_bytes = 0;   // operand preparation for the GEMMs
   size_t total = 0;
   rnn_status_t status = RNN_STATUS_SUCCESS;
 };
@@ -177,6 +180,17 @@ bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, SweepPlan* sp) {
   return false;
 }
 
+// Split-K factor of a weight-gradient product: enough workgroups for the
+// 256 CUs, at least 256 k per split.
+int gemm_split(const rnn_desc* h, int M, int N, int K, int batches) {
+  (void)h;
+  const int tiles = ceil_div(M, 128) * ceil_div(N, 128) * std::max(1, batches);
+  int s = ceil_div(512, std::max(1, tiles));
+  s = std::min(s, 8);
+  s = std::min(s, std::max(1, K / 256));
+  return std::max(1, s);
+}
+
 Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   Plan p;
   p.T = T;
@@ -208,10 +222,28 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
     p.status = RNN_STATUS_UNSUPPORTED;
     return p;
   }
+  // exchange rings: one entry per step, one 128-byte-aligned slice per
+  // producer, entries padded to 1 KB (the LDS staging granule)
+  const int s_total = T + (p.wavefront ? h->L : 1) - 1;
+  p.fslice = (int)(((size_t)p.Bc * p.fwd.U * es + 127) / 128 * 128);
+  p.fring_step = ((size_t)p.fwd.nwg * p.fslice + 1023) / 1024 * 1024;
+  p.fring_group = align_up(p.fring_step * (size_t)(s_total + 1));
+  p.bslice = (int)(((size_t)p.Bc * h->G * p.bwd.U * es + 127) / 128 * 128);
+  p.bring_step = ((size_t)p.bwd.nwg * p.bslice + 1023) / 1024 * 1024;
+  p.bring_group = align_up(p.bring_step * (size_t)(T + 1));
+
   const int sched = h->sched;
-  auto decide = [&](SweepPlan& sp, bool fwd) {
-    const int maxres = fwd ? rnn_fwd_max_resident(h->mode, bf, sp.cfg)
-                           : rnn_bwd_max_resident(h->mode, bf, sp.cfg);
+  const bool allow_stage = env_int("RNN_NO_STAGE", 0) == 0;
+  auto decide = [&](SweepPlan& sp, bool fwd, size_t stage_bytes) {
+    auto res = [&](size_t lds) {
+      return fwd ? rnn_fwd_max_resident(h->mode, bf, sp.cfg, lds)
+                 : rnn_bwd_max_resident(h->mode, bf, sp.cfg, lds);
+    };
+    size_t lds = allow_stage ? stage_bytes : 0;
+    int maxres = lds ? res(lds) : 0;
+    if (lds && maxres < sp.grid) lds = 0;
+    if (!lds) maxres = res(0);
+    sp.lds = lds;
     const bool fits = maxres >= sp.grid && maxres > 0;
     if (sched == RNN_SCHED_STEPPED) sp.persistent = false;
     else if (sched == RNN_SCHED_PERSISTENT) {
@@ -219,8 +251,8 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
       if (!fits) p.status = RNN_STATUS_NOT_CORESIDENT;
     } else sp.persistent = fits;
   };
-  decide(p.fwd, true);
-  if (training) decide(p.bwd, false);
+  decide(p.fwd, true, 0);   // the forward reads its fragments straight from the ring
+  if (training) decide(p.bwd, false, p.bring_step);
 
   const size_t TB = (size_t)T * B;
   const size_t dgh = (size_t)h->D * h->G * h->H;
@@ -231,14 +263,6 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   p.flags_bytes = (size_t)std::max(p.fwd.grid, p.bwd.grid) * kFlagStride * 4;
   off = align_up(off + p.flags_bytes);
   p.off_xch = off;
-  // exchange rings: one entry per step, one 128-byte-aligned slice per producer
-  const int s_total = T + (p.wavefront ? h->L : 1) - 1;
-  p.fslice = (int)(((size_t)p.Bc * p.fwd.U * es + 127) / 128 * 128);
-  p.fring_step = (size_t)p.fwd.nwg * p.fslice;
-  p.fring_group = align_up(p.fring_step * (size_t)(s_total + 1));
-  p.bslice = (int)(((size_t)p.Bc * h->G * p.bwd.U * es + 127) / 128 * 128);
-  p.bring_step = (size_t)p.bwd.nwg * p.bslice;
-  p.bring_group = align_up(p.bring_step * (size_t)(T + 1));
   size_t xf = (size_t)p.fwd.groups * p.fring_group;
   size_t xb = (size_t)p.bwd.groups * p.bring_group;
   p.xch_bytes = std::max(xf, training ? xb : (size_t)0);
@@ -254,20 +278,44 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   p.yin_slot = align_up(TB * h->D * h->H * 4);
   if (h->L > 1) p.yin_slots = (training || p.wavefront) ? h->L - 1 : std::min(2, h->L - 1);
   off += p.yin_slot * p.yin_slots;
+  // operand-preparation scratch (fwd: layer input in bf16)
+  int Imax = h->I;
+  for (int l = 1; l < h->L; ++l) Imax = std::max(Imax, in_width(h, l));
+  const size_t Ipad = (size_t)ceil_div(Imax, 8) * 8;
+  p.dg_ld = ceil_div((int)dgh, 8) * 8;
+  p.tb_ld = ceil_div((int)std::max<size_t>(TB, 1), 8) * 8;
+  size_t scr = bf ? align_up(TB * Ipad * 2) : 0;
   if (training) {
     const int R = reserve_slots(h->mode);
     p.off_res = off;
     p.res_layer = align_up((size_t)h->D * TB * R * h->H * 4);
     off += p.res_layer * h->L;
-    p.off_dgi = off;
-    p.dg_layer = align_up(TB * dgh * 4);
+    p.dg_layer = align_up(TB * (size_t)p.dg_ld * es);
+    p.dgT_layer = align_up(dgh * (size_t)p.tb_ld * es);
+    p.off_dg = off;
     off += p.dg_layer * h->L;
-    p.off_dgh = off;
-    if (h->mode == RNN_GRU) off += p.dg_layer * h->L;
+    p.off_dgT = off;
+    off += p.dgT_layer * h->L;
+    p.off_dghT = off;
+    if (h->mode == RNN_GRU) off += p.dgT_layer * h->L;
     p.off_dy = off;
     p.dy_slot = align_up(TB * h->D * h->H * 4);
     if (h->L > 1) off += 2 * p.dy_slot;
+    // backward_data: W_ih^T [I_l][dg_ld]; backward_weights: X^T, H_prev^T, split-K partials
+    scr = std::max(scr, align_up(Ipad * p.dg_ld * es));
+    size_t wts = align_up(Ipad * p.tb_ld * es) + align_up((size_t)h->D * h->H * p.tb_ld * es);
+    size_t part = 0;
+    for (int l = 0; l < h->L; ++l) {
+      const int I_l = in_width(h, l);
+      part = std::max(part, (size_t)gemm_split(h, (int)dgh, I_l + 1, (int)TB, 1) * dgh * (I_l + 1) * 4);
+      part = std::max(part, (size_t)gemm_split(h, h->G * h->H, h->H + 1, (int)TB, h->D) * h->D *
+                                (size_t)h->G * h->H * (h->H + 1) * 4);
+    }
+    scr = std::max(scr, wts + align_up(part));
   }
+  p.off_scr = off;
+  p.scr_bytes = scr;
+  off += scr;
   p.total = align_up(off);
   return p;
 }
@@ -328,16 +376,20 @@ rnn_status_t dev(hipError_t e) { return e == hipSuccess ? RNN_STATUS_SUCCESS : R
     if (st_ != RNN_STATUS_SUCCESS) return st_; \
   } while (0)
 
-rnn_status_t fill(rnn_desc* h, hipStream_t s, std::initializer_list<std::pair<void*, size_t>> r) {
+rnn_status_t fill(rnn_desc* h, hipStream_t s, std::initializer_list<std::pair<void*, size_t>> r,
+                  uint32_t value = 0u) {
   std::vector<void*> ps;
   std::vector<size_t> ns;
+  std::vector<uint32_t> vs;
   for (auto& x : r) {
     ps.push_back(x.first);
     ns.push_back(x.second);
+    vs.push_back(value);
   }
   ProfScope ps_(h, s, K_FILL);
-  return dev(rnn_launch_fill(ps.data(), ns.data(), (int)ps.size(), s));
+  return dev(rnn_launch_fill(ps.data(), ns.data(), vs.data(), (int)ps.size(), s));
 }
+
 
 unsigned spin_limit() {
   const int v = env_int("RNN_SPIN_LIMIT", 1 << 20);
@@ -349,18 +401,35 @@ const void* layer_w(const rnn_desc* h, const void* W, int which, int l) {
 }
 
 // Hoisted input projection of layer l: GX[T*B, D*G*H] = in W_ih^T + b_ih + b_hh
-// (b_hh not folded into GRU's n gate, which needs it inside r*(.)).
+// (b_hh not folded into GRU's n gate, which needs it inside r*(.)).  The bf16
+// path first rounds the layer input to bf16 (the MFMA operand precision).
 rnn_status_t gemm_input(rnn_desc* h, hipStream_t s, const Plan& p, int l, const float* in,
-                        const void* W, float* gx) {
+                        const void* W, float* gx, void* ws) {
   GemmParams g{};
   const int I_l = in_width(h, l);
+  const bool bf = h->wtype == RNN_W_BF16;
+  const int EPV = bf ? 8 : 4;
   g.M = p.T * p.B;
   g.N = h->D * h->G * h->H;
   g.K = I_l;
-  g.A[0] = in;
-  g.lda = I_l;
+  if (bf) {
+    const int ldx = ceil_div(I_l, 8) * 8;
+    void* xb = at<void>(ws, p.off_scr);
+    {
+      ProfScope ps(h, s, K_PREP);
+      RNN_TRY(dev(rnn_launch_convert(in, I_l, xb, ldx, g.M, I_l, s)));
+    }
+    g.A[0] = xb;
+    g.lda = ldx;
+    g.a_vec = 1;
+  } else {
+    g.A[0] = in;
+    g.lda = I_l;
+    g.a_vec = (I_l % EPV == 0) && ((uintptr_t)in % 16 == 0);
+  }
   g.B[0] = layer_w(h, W, RNN_W_IH, l);
   g.ldb = I_l;
+  g.b_vec = (I_l % EPV == 0);
   g.n_ones = -1;
   g.C[0] = gx;
   g.ldc = g.N;
@@ -369,11 +438,9 @@ rnn_status_t gemm_input(rnn_desc* h, hipStream_t s, const Plan& p, int l, const 
   g.bias2_skip_gate = h->mode == RNN_GRU ? 2 : -1;
   g.gh = h->G * h->H;
   g.hh = h->H;
-  const bool bf = h->wtype == RNN_W_BF16;
-  g.a_vec = (I_l % 4 == 0) && ((uintptr_t)in % 16 == 0);
-  g.b_vec = (I_l % (bf ? 8 : 4) == 0);
+  g.split_k = 1;
   ProfScope ps(h, s, K_GEMM_IN);
-  return dev(rnn_launch_gemm(g, bf, bf, 1, 0, EPI_BIAS, 1, s));
+  return dev(rnn_launch_gemm(g, bf, EPI_BIAS, 1, s));
 }
 
 rnn_status_t check_common(const rnn_desc* h, int T, int B, const void* ws, size_t ws_bytes) {
@@ -427,6 +494,7 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   f.slice = p.fslice;
   f.ring_step = (long long)p.fring_step;
   f.ring_group = (long long)p.fring_group;
+  f.stage = p.fwd.lds > 0 ? 1 : 0;
   f.persistent = p.fwd.persistent ? 1 : 0;
   f.training = training;
   f.h0 = h0;
@@ -449,19 +517,19 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
       f.s_begin = -1;
       f.s_end = f.s_total;
       ProfScope ps(h, s, K_FWD);
-      return dev(rnn_launch_fwd(f, h->mode, bf, p.fwd.cfg, grid, s));
+      return dev(rnn_launch_fwd(f, h->mode, bf, p.fwd.cfg, grid, p.fwd.lds, s));
     }
     for (int st = -1; st < f.s_total; ++st) {
       f.s_begin = st;
       f.s_end = st + 1;
       ProfScope ps(h, s, K_FWD);
-      RNN_TRY(dev(rnn_launch_fwd(f, h->mode, bf, p.fwd.cfg, grid, s)));
+      RNN_TRY(dev(rnn_launch_fwd(f, h->mode, bf, p.fwd.cfg, grid, p.fwd.lds, s)));
     }
     return RNN_STATUS_SUCCESS;
   };
 
   if (p.wavefront) {
-    RNN_TRY(gemm_input(h, s, p, 0, x, W, gx));
+    RNN_TRY(gemm_input(h, s, p, 0, x, W, gx, ws));
     f.wavefront = 1;
     f.first_layer = 0;
     f.gx = gx;
@@ -479,7 +547,7 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
     f.wavefront = 0;
     for (int l = 0; l < h->L; ++l) {
       const float* in = (l == 0) ? x : yin(l - 1);
-      RNN_TRY(gemm_input(h, s, p, l, in, W, gx));
+      RNN_TRY(gemm_input(h, s, p, l, in, W, gx, ws));
       f.first_layer = l;
       f.gx = gx;
       f.w_ih[0] = layer_w(h, W, RNN_W_IH, l);
@@ -626,6 +694,7 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
   b.slice = p.bslice;
   b.ring_step = (long long)p.bring_step;
   b.ring_group = (long long)p.bring_group;
+  b.stage = p.bwd.lds > 0 ? 1 : 0;
   b.persistent = p.bwd.persistent ? 1 : 0;
   b.st_dh = at<float>(ws, p.off_st);
   b.st_dc = at<float>(ws, p.off_st + p.st_bytes / 2);
@@ -642,8 +711,11 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
     b.dy = (l == h->L - 1) ? dy : dyslot(l);
     b.dhy = dhy ? dhy + l * lstride : nullptr;
     b.dcy = dcy ? dcy + l * lstride : nullptr;
-    b.dgi = at<float>(ws, p.off_dgi + p.dg_layer * l);
-    b.dgh = h->mode == RNN_GRU ? at<float>(ws, p.off_dgh + p.dg_layer * l) : nullptr;
+    b.dg = at<void>(ws, p.off_dg + p.dg_layer * l);
+    b.dgT = at<void>(ws, p.off_dgT + p.dgT_layer * l);
+    b.dghT = h->mode == RNN_GRU ? at<void>(ws, p.off_dghT + p.dgT_layer * l) : nullptr;
+    b.dg_ld = p.dg_ld;
+    b.tb_ld = p.tb_ld;
     b.dh0 = dh0 ? dh0 + l * lstride : nullptr;
     b.dc0 = dc0 ? dc0 + l * lstride : nullptr;
     if (b.persistent) RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
@@ -651,32 +723,46 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
       b.s_begin = 0;
       b.s_end = T + 1;
       ProfScope ps(h, s, K_BWD);
-      RNN_TRY(dev(rnn_launch_bwd(b, h->mode, bf, p.bwd.cfg, p.bwd.grid, s)));
+      RNN_TRY(dev(rnn_launch_bwd(b, h->mode, bf, p.bwd.cfg, p.bwd.grid, p.bwd.lds, s)));
     } else {
       for (int st = 0; st <= T; ++st) {
         b.s_begin = st;
         b.s_end = st + 1;
         ProfScope ps(h, s, K_BWD);
-        RNN_TRY(dev(rnn_launch_bwd(b, h->mode, bf, p.bwd.cfg, p.bwd.grid, s)));
+        RNN_TRY(dev(rnn_launch_bwd(b, h->mode, bf, p.bwd.cfg, p.bwd.grid, p.bwd.lds, s)));
       }
     }
-    // dX_l = dG_i W_ih  (both directions in one product, K = D*G*H)
-    GemmParams g{};
+    // dX_l = dG_i W_ih  (both directions in one product, K = D*G*H); B = W_ih^T
     const int I_l = in_width(h, l);
+    void* wT = at<void>(ws, p.off_scr);
+    {
+      TransposeParams tp{};
+      tp.src = layer_w(h, W, RNN_W_IH, l);
+      tp.ld_src = I_l;
+      tp.alt_r0 = tp.alt_r1 = 0;
+      tp.out = wT;
+      tp.ld_out = p.dg_ld;
+      tp.R = (int)dgh;
+      tp.C = I_l;
+      ProfScope ps(h, s, K_PREP);
+      RNN_TRY(dev(rnn_launch_transpose(tp, bf, bf, s)));
+    }
+    GemmParams g{};
     g.M = T * B;
     g.N = I_l;
     g.K = (int)dgh;
-    g.A[0] = b.dgi;
-    g.lda = (long long)dgh;
-    g.B[0] = layer_w(h, W, RNN_W_IH, l);
-    g.ldb = I_l;
+    g.A[0] = b.dg;
+    g.lda = p.dg_ld;
+    g.B[0] = wT;
+    g.ldb = p.dg_ld;
     g.n_ones = -1;
     g.C[0] = (l == 0) ? dx : dyslot(l - 1);
     g.ldc = I_l;
-    g.a_vec = (dgh % 4 == 0);
-    g.b_vec = (I_l % (bf ? 8 : 4) == 0);
+    g.a_vec = 1;
+    g.b_vec = 1;
+    g.split_k = 1;
     ProfScope ps(h, s, K_GEMM_DX);
-    RNN_TRY(dev(rnn_launch_gemm(g, bf, bf, 1, 1, EPI_STORE, 1, s)));
+    RNN_TRY(dev(rnn_launch_gemm(g, bf, EPI_STORE, 1, s)));
   }
   h->seq_stage = 2;
   return RNN_STATUS_SUCCESS;
@@ -703,56 +789,87 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
   auto yl = [&](int l) -> const float* {
     return l == h->L - 1 ? y : at<float>(wsm, p.off_yin + p.yin_slot * (size_t)l);
   };
+  (void)lstride;
   char* dWb = reinterpret_cast<char*>(dW);
+  const size_t TB = (size_t)T * B;
+  const size_t es = bf ? 2 : 4;
+  int Imax = h->I;
+  for (int l = 1; l < h->L; ++l) Imax = std::max(Imax, in_width(h, l));
+  const size_t Ipad = (size_t)ceil_div(Imax, 8) * 8;
+  char* scr = at<char>(wsm, p.off_scr);
+  void* xT = scr;
+  char* hT = scr + align_up(Ipad * p.tb_ld * es);
+  float* part = reinterpret_cast<float*>(hT + align_up((size_t)h->D * h->H * p.tb_ld * es));
   for (int l = 0; l < h->L; ++l) {
     const int I_l = in_width(h, l);
     const float* X = (l == 0) ? x : yl(l - 1);
-    const float* dgi = at<float>(wsm, p.off_dgi + p.dg_layer * l);
-    const float* dghp = h->mode == RNN_GRU ? at<float>(wsm, p.off_dgh + p.dg_layer * l) : dgi;
+    const char* dgT = at<char>(wsm, p.off_dgT + p.dgT_layer * l);
+    const char* dghT = h->mode == RNN_GRU ? at<char>(wsm, p.off_dghT + p.dgT_layer * l) : dgT;
+    {  // X^T [I_l][T*B] and H_prev^T [D][H][T*B] (shifted one step, h0 at the start)
+      ProfScope ps(h, s, K_PREP);
+      TransposeParams tp{};
+      tp.src = X;
+      tp.ld_src = I_l;
+      tp.out = xT;
+      tp.ld_out = p.tb_ld;
+      tp.R = (int)TB;
+      tp.C = I_l;
+      RNN_TRY(dev(rnn_launch_transpose(tp, 0, bf, s)));
+      for (int d = 0; d < h->D; ++d) {
+        TransposeParams th{};
+        th.src = yl(l) + (size_t)d * h->H;
+        th.ld_src = (long long)h->D * h->H;
+        th.shift = d == 0 ? -B : B;
+        th.alt = h0 ? h0 + l * lstride + (size_t)d * B * h->H : nullptr;
+        th.ld_alt = h->H;
+        th.alt_r0 = d == 0 ? 0 : (T - 1) * B;
+        th.alt_r1 = th.alt_r0 + B;
+        th.out = hT + (size_t)d * h->H * p.tb_ld * es;
+        th.ld_out = p.tb_ld;
+        th.R = (int)TB;
+        th.C = h->H;
+        RNN_TRY(dev(rnn_launch_transpose(th, 0, bf, s)));
+      }
+    }
     {  // dW_ih | db_ih = dG_i^T [X | 1]
       GemmParams g{};
       g.M = dgh;
       g.N = I_l + 1;
-      g.K = T * B;
-      g.A[0] = dgi;
-      g.lda = dgh;
-      g.B[0] = X;
-      g.ldb = I_l;
-      g.b_alt_k0[0] = g.b_alt_k1[0] = 0;
+      g.K = (int)TB;
+      g.A[0] = dgT;
+      g.lda = p.tb_ld;
+      g.B[0] = xT;
+      g.ldb = p.tb_ld;
       g.n_ones = I_l;
       g.C[0] = reinterpret_cast<float*>(dWb + h->off[1][RNN_W_IH][l]);
       g.ldc = I_l;
       g.cbias[0] = reinterpret_cast<float*>(dWb + h->off[1][RNN_B_IH][l]);
-      g.a_vec = (dgh % 4 == 0);
-      g.b_vec = (I_l % 4 == 0) && ((uintptr_t)X % 16 == 0);
+      g.a_vec = g.b_vec = 1;
+      g.split_k = gemm_split(h, g.M, g.N, g.K, 1);
+      g.partial = part;
       ProfScope ps(h, s, K_GEMM_DW);
-      RNN_TRY(dev(rnn_launch_gemm(g, bf, 0, 0, 1, EPI_DW, 1, s)));
+      RNN_TRY(dev(rnn_launch_gemm(g, bf, EPI_DW, 1, s)));
     }
     {  // dW_hh | db_hh = dG_h^T [H_prev | 1], per direction
       GemmParams g{};
       g.M = GH;
       g.N = h->H + 1;
-      g.K = T * B;
-      g.lda = dgh;
-      g.ldb = (long long)h->D * h->H;
-      g.ld_alt = h->H;
+      g.K = (int)TB;
+      g.lda = p.tb_ld;
+      g.ldb = p.tb_ld;
       g.n_ones = h->H;
       g.ldc = h->H;
       for (int d = 0; d < h->D; ++d) {
-        g.A[d] = dghp + (size_t)d * GH;
-        g.B[d] = yl(l) + (size_t)d * h->H;
-        g.b_shift[d] = d == 0 ? -B : B;
-        g.b_alt_k0[d] = d == 0 ? 0 : (T - 1) * B;
-        g.b_alt_k1[d] = g.b_alt_k0[d] + B;
-        g.b_alt[d] = h0 ? h0 + l * lstride + (size_t)d * B * h->H : nullptr;
+        g.A[d] = dghT + (size_t)d * GH * p.tb_ld * es;
+        g.B[d] = hT + (size_t)d * h->H * p.tb_ld * es;
         g.C[d] = reinterpret_cast<float*>(dWb + h->off[1][RNN_W_HH][l]) + (size_t)d * GH * h->H;
         g.cbias[d] = reinterpret_cast<float*>(dWb + h->off[1][RNN_B_HH][l]) + (size_t)d * GH;
       }
-      g.a_vec = (dgh % 4 == 0) && (GH % 4 == 0);
-      g.b_vec = ((h->D * h->H) % 4 == 0) && (h->H % 4 == 0) && ((uintptr_t)yl(l) % 16 == 0) &&
-                (!h0 || (uintptr_t)h0 % 16 == 0);
+      g.a_vec = g.b_vec = 1;
+      g.split_k = gemm_split(h, g.M, g.N, g.K, h->D);
+      g.partial = part;
       ProfScope ps(h, s, K_GEMM_DW);
-      RNN_TRY(dev(rnn_launch_gemm(g, bf, 0, 0, 1, EPI_DW, h->D, s)));
+      RNN_TRY(dev(rnn_launch_gemm(g, bf, EPI_DW, h->D, s)));
     }
   }
   return RNN_STATUS_SUCCESS;

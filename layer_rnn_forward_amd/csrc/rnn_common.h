@@ -23,27 +23,23 @@ __host__ __device__ constexpr int gates_of(int mode) {
 }
 
 // ------------------------------------------------------------------ GEMM
-// C[m, n] = sum_k A(m, k) * B(k, n)   (batched over blockIdx.z < 2)
-//   A fp32: a_kmajor ? A[m*lda + k] : A[k*lda + m]
-//   B (fp32 or bf16): b_kn ? B[k*ldb + n] : B[n*ldb + k]
-//   B rows may be remapped (KN only): row k reads row k + b_shift, except
-//   rows in [b_alt_k0, b_alt_k1) which read b_alt[(k - b_alt_k0)*ld_alt + n]
-//   (zero if b_alt is null).  Column n == n_ones of B is all ones.
+// C[m, n] = sum_k A[m*lda + k] * B[n*ldb + k]   (batched over blockIdx.z < 2)
+// A and B in the compute type (bf16 or fp32), both K-contiguous.  Row n_ones
+// of B is all ones (it yields the bias gradient), or -1.
 // Epilogue: EPI_STORE  C[m*ldc + n] = acc
 //           EPI_BIAS   C[m*ldc + n] = acc + bias1[n] + bias2[n] (bias2 skipped
 //                      for columns whose gate (n % gh) / hh == bias2_skip_gate)
 //           EPI_DW     n == n_ones ? cbias[m] = acc : C[m*ldc + n] = acc
+// split_k > 1 (EPI_DW only): fp32 partials [batch][split][M][N] in `partial`,
+// summed in split order by a second kernel.
 enum Epi { EPI_STORE = 0, EPI_BIAS = 1, EPI_DW = 2 };
 
 struct GemmParams {
   int M, N, K;
-  const float* A[2];
+  const void* A[2];
   long long lda;
   const void* B[2];
   long long ldb;
-  int b_shift[2], b_alt_k0[2], b_alt_k1[2];
-  const float* b_alt[2];
-  long long ld_alt;
   int n_ones;
   float* C[2];
   long long ldc;
@@ -52,6 +48,24 @@ struct GemmParams {
   const float* bias2;
   int bias2_skip_gate, gh, hh;
   int a_vec, b_vec;   // 1: 16-byte vector loads are legal (aligned bases and strides)
+  int split_k;
+  float* partial;
+};
+
+// Row-gather transpose: out[c * ld_out + r] = src_row(r)[c] for r < R, c < C,
+// where src_row(r) = src + (r + shift) * ld_src, except rows r in
+// [alt_r0, alt_r1) which read alt + (r - alt_r0) * ld_alt (zeros if alt is
+// null).  Converts the element type on the way.
+struct TransposeParams {
+  const void* src;
+  long long ld_src;
+  int shift;
+  const void* alt;
+  long long ld_alt;
+  int alt_r0, alt_r1;
+  void* out;
+  long long ld_out;
+  int R, C;
 };
 
 // ------------------------------------------------------------- recurrence
@@ -66,6 +80,7 @@ struct FwdParams {
   int slice;              // bytes of one producer's slice in a ring entry (multiple of 128)
   long long ring_step;    // bytes of one ring entry (nwg * slice)
   long long ring_group;   // bytes of one group's ring (entries * ring_step)
+  int stage;              // 1: copy each consumed ring entry into LDS first
   int s_begin, s_end;     // global steps [s_begin, s_end); -1 is the prologue
   int s_total;            // T + nlayers - 1
   int persistent, training, wavefront;
@@ -95,6 +110,7 @@ struct BwdParams {
   int nchunk, Bc, U, nwg;
   int slice;              // bytes of one producer's slice (Bc x G x U values, padded to 128)
   long long ring_step, ring_group;
+  int stage;              // 1: copy each consumed ring entry into LDS first
   int s_begin, s_end;     // processing steps; s == T is the final dh0 phase
   int persistent;
   const void* w_hh;       // layer block [D*G*H, H]
@@ -105,8 +121,11 @@ struct BwdParams {
   const float* dy;        // [T, B, D*H]
   const float* dhy;       // [D, B, H] or null
   const float* dcy;
-  float* dgi;             // [T*B, D*G*H]
-  float* dgh;             // GRU only: [T*B, D*G*H]
+  void* dg;               // dG_i [T*B, D*G*H] in the compute type (dX operand)
+  void* dgT;              // dG_i^T [D*G*H, T*B] (dW_ih operand)
+  void* dghT;             // GRU: dG_h^T [D*G*H, T*B] (dW_hh operand)
+  int dg_ld;              // row stride of dg (>= D*G*H)
+  int tb_ld;              // row stride of dgT / dghT (>= T*B)
   float* dh0;             // [D, B, H] or null
   float* dc0;
   float* st_dh;           // carries between stepped launches [D*nchunk... ] laid out [D][B][H]
@@ -128,16 +147,22 @@ struct RecConfig {
 };
 
 // Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
-hipError_t rnn_launch_gemm(const rnnk::GemmParams& p, int bf16_compute, int b_bf16, int a_kmajor,
-                           int b_kn, int epi, int batches, hipStream_t s);
+hipError_t rnn_launch_gemm(const rnnk::GemmParams& p, int bf16, int epi, int batches, hipStream_t s);
+// in_bf16 / out_bf16: element types of src (and alt) / out.
+hipError_t rnn_launch_transpose(const rnnk::TransposeParams& p, int in_bf16, int out_bf16, hipStream_t s);
+hipError_t rnn_launch_convert(const float* src, long long ld_src, void* dst, long long ld_dst, int rows,
+                              int cols, hipStream_t s);   // fp32 -> bf16 (round to nearest even)
+// lds: dynamic LDS bytes (the ring-entry staging buffer, 0 when not staging)
 hipError_t rnn_launch_fwd(const rnnk::FwdParams& p, int mode, int bf16, const RecConfig& c,
-                          int grid, hipStream_t s);
+                          int grid, size_t lds, hipStream_t s);
 hipError_t rnn_launch_bwd(const rnnk::BwdParams& p, int mode, int bf16, const RecConfig& c,
-                          int grid, hipStream_t s);
-hipError_t rnn_launch_fill(void* const* ptrs, const size_t* bytes, int n, hipStream_t s);
+                          int grid, size_t lds, hipStream_t s);
+// Fill ranges with 32-bit patterns (values null: zeros).  bytes: multiples of 4.
+hipError_t rnn_launch_fill(void* const* ptrs, const size_t* bytes, const uint32_t* values, int n,
+                           hipStream_t s);
 hipError_t rnn_copy_state(float* dst, const float* src, size_t n, hipStream_t s);
 // Maximum co-resident workgroups of the fwd/bwd kernel for this config (0 if unsupported).
-int rnn_fwd_max_resident(int mode, int bf16, const RecConfig& c);
-int rnn_bwd_max_resident(int mode, int bf16, const RecConfig& c);
+int rnn_fwd_max_resident(int mode, int bf16, const RecConfig& c, size_t lds);
+int rnn_bwd_max_resident(int mode, int bf16, const RecConfig& c, size_t lds);
 bool rnn_fwd_config_supported(int mode, int bf16, const RecConfig& c);
 bool rnn_bwd_config_supported(int mode, int bf16, const RecConfig& c);
