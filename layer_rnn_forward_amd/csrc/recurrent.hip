@@ -8,29 +8,35 @@
 // slice of the recurrent weights (and, in the wavefront, of the input weights)
 // in registers for the whole sweep -- the persistent-RNN idea discussed in the
 // TVM thread "Persist RNN Implementation" -- and per step:
-//   1. waits until every producer of the h it needs has published the step
-//      (per-workgroup flags, agent scope; GX for the step is prefetched first),
-//   2. multiplies the 16-row batch tiles of h_prev by its weight slice on MFMA
-//      (K split across the waves, partial tiles summed through LDS in a fixed
-//      order),
+//   1. each wave waits until the producers of the part of h it multiplies
+//      have published the step (per-workgroup flags, agent scope; GX for the
+//      step is prefetched first),
+//   2. multiplies the 16-row batch tiles of that part of h_prev by its weight
+//      slice on MFMA (K split across the waves, partial tiles summed through
+//      LDS in a fixed order),
 //   3. applies the cell equations to its units in the same kernel (fused
-//      point-wise step of the optimisation table), writes y, the training
-//      reserve and the next h into the other half of a ping-pong buffer,
+//      point-wise step of the optimisation table), writes the next h into the
+//      exchange ring, then y and the training reserve,
 //   4. publishes its flag.
 // Backward: the same structure walks time in reverse; each workgroup owns U
 // units, exchanges the recurrent gate gradients dG_h, computes
-// dh = dG_h W_hh for its units on MFMA, and applies the hand-derived BPTT
-// formulas to the reserved forward intermediates.
+// dh = dG_h W_hh for its units on MFMA (each wave first copies its part of
+// the exchanged dG_h into LDS with direct global->LDS loads), and applies the
+// hand-derived BPTT formulas to the reserved forward intermediates.
 //
 // Exchange protocol.  The vector one step produces (h, or dG_h) goes into a
 // ring with one entry per step, so no address is written twice within a
-// sweep.  Each producer owns whole 128-byte lines of an entry (its slice:
-// rows x units, zero-padded), writes them with agent-scope stores, waits for
-// their completion and then stores its step flag (agent scope).  A consumer
-// polls the flags with agent-scope loads and then reads the entry with plain
-// loads: no cache can hold a stale copy of a line that was never read before
-// its single writer completed, so no cache write-back or invalidation is
-// needed per step, and the workgroups of one XCD share the entry through L2.
+// sweep.  An entry is a sequence of granules: 16 bytes of consecutive units
+// (the A-fragment share of one lane in one MFMA: 8 bf16 or 4 fp32 values) for
+// every batch row, [row][16 bytes].  Producer pp owns the consecutive
+// granules of its units (per gate in the backward), padded so that its slice
+// covers whole 128-byte lines; it writes them with agent-scope stores, waits
+// for their completion and then stores its step flag (agent scope).  A wave
+// consumes a contiguous range of granules, polls only the flags of their
+// producers with agent-scope loads and then reads them with plain loads: no
+// cache can hold a stale copy of a line that was never read before its single
+// writer completed, so no cache write-back or invalidation is needed per
+// step, and the workgroups of one XCD share the entry through L2.
 // Every wait is bounded; an expired wait sets the error word and every
 // workgroup leaves the sweep.
 #include <type_traits>
@@ -80,39 +86,39 @@ __device__ __forceinline__ void ring_store(char* base, size_t off, float v) {
     __hip_atomic_store(reinterpret_cast<float*>(base + off), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wave 0 polls the flags of up to two groups (ranges of nwg workgroups); the
-// workgroup barrier follows.  Returns false (for every thread) if the bounded
-// wait expired or another workgroup reported an error.
-__device__ bool wait_groups(const unsigned* flags, unsigned* err, unsigned spin_limit,
-                            const int (&g)[2], int ng, int nwg, unsigned target, int* s_flag) {
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int lane = tid;
-    const int total = ng * nwg;
-    bool ok = false;
-    unsigned it = 0;
-    while (true) {
-      bool mine = true;
+// Bounded wait of one wave for the flags of two ranges of producers,
+// [a0, a0 + na) and [b0, b0 + nb) (flag indices), to reach `target`.
+// Returns false (uniformly over the wave) if the wait expired -- the error
+// word is then set -- or another workgroup reported an error.
+__device__ bool wave_wait(const unsigned* flags, unsigned* err, unsigned spin_limit, int a0, int na,
+                          int b0, int nb, unsigned target) {
+  const int lane = threadIdx.x & 63;
+  const int total = na + nb;
+  const int nper = (total + 63) / 64;   // flags per lane, uniform
+  unsigned it = 0;
+  while (true) {
+    // issue every flag load of this round before looking at any of them
+    unsigned v[kWaitPerLane];
 #pragma unroll
-      for (int i = 0; i < kWaitPerLane; ++i) {
-        const int idx = lane + 64 * i;
-        if (idx < total) {
-          const int gi = idx / nwg;
-          const int w = g[gi] * nwg + (idx - gi * nwg);
-          mine = mine && (flag_load(flags + (size_t)w * kFlagStride) >= target);
-        }
+    for (int i = 0; i < kWaitPerLane; ++i) {
+      const int idx = lane + 64 * i;
+      v[i] = target;
+      if (i < nper && idx < total) {
+        const int w = idx < na ? a0 + idx : b0 + (idx - na);
+        v[i] = flag_load(flags + (size_t)w * kFlagStride);
       }
-      if (__all(mine)) { ok = true; break; }
-      if (++it > spin_limit) { flag_store(err, 1u); break; }
-      if ((it & 31u) == 0 && flag_load(err) != 0u) break;
-      __builtin_amdgcn_s_sleep(1);
     }
-    if (lane == 0) *s_flag = ok ? 1 : 0;
+    bool mine = true;
+#pragma unroll
+    for (int i = 0; i < kWaitPerLane; ++i) mine = mine && v[i] >= target;
+    if (__all(mine)) return true;
+    if (++it > spin_limit) {
+      flag_store(err, 1u);
+      return false;
+    }
+    if ((it & 31u) == 0 && flag_load(err) != 0u) return false;
+    __builtin_amdgcn_s_sleep(1);
   }
-  __syncthreads();
-  const bool ok = *s_flag != 0;
-  __syncthreads();
-  return ok;
 }
 
 // Every wave waits for completion of its stores (the ring stores are agent
@@ -123,14 +129,17 @@ __device__ __forceinline__ void publish(unsigned* flags, unsigned v) {
   if (threadIdx.x == 0) flag_store(flags + (size_t)blockIdx.x * kFlagStride, v);
 }
 
-// MFMA over the K chunks this wave holds, A fragments (16 bytes per lane) from
-// `load(k0, row, valid)`; all loads of a batch are issued before its MFMAs.
-template <bool BF16, int NT, int MT, int KPW, int NW, class LoadF>
-__device__ __forceinline__ void mfma_sweep(f32x4 (&acc)[MT][NT], const uint4 (&wf)[KPW][NT],
-                                           int wave, int fr, int fq, int nch, int Bact,
-                                           LoadF load) {
-  constexpr int KC = kchunk<BF16>();
-  constexpr int PER = KC / 4;
+// MFMA over the granules this wave holds.  K chunk kk takes granules
+// 4*kk + fq of the wave's range (fq = lane / 16): a lane feeds one granule's
+// 16 bytes of row `row` as its A fragment, `load(gl, row)`, and the matching
+// weights sit in wf[kk].  Lanes past the end of the range re-read its last
+// granule (their weights are zero), and tile rows past the granule's padded
+// rows re-read its last row: no load leaves the granules the wave has waited
+// for, and such rows only feed output rows that are never used.  All loads of
+// a batch are issued before its MFMAs.
+template <bool BF16, int NT, int MT, int KPW, class LoadF>
+__device__ __forceinline__ void mfma_sweep(f32x4 (&acc)[MT][NT], const uint4 (&wf)[KPW][NT], int fr,
+                                           int fq, int nmine, int rmax, LoadF load) {
   constexpr int KB = KPW < 8 ? KPW : 8;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -138,17 +147,16 @@ __device__ __forceinline__ void mfma_sweep(f32x4 (&acc)[MT][NT], const uint4 (&w
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < KPW; kb += KB) {
+    if (kb * 4 >= nmine) break;   // uniform over the wave
     uint4 av[KB][MT];
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk) {
-      const int gc = wave + (kb + kk) * NW;
-      const int k0 = gc * KC + fq * PER;
+      const int gl = min((kb + kk) * 4 + fq, nmine - 1);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = mt * 16 + fr;
-        av[kk][mt] = load(k0, row, gc < nch && row < Bact);
-      }
+      for (int mt = 0; mt < MT; ++mt) av[kk][mt] = load(gl, min(mt * 16 + fr, rmax));
     }
+    // keep the whole batch of loads in flight before the first MFMA
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
@@ -158,15 +166,20 @@ __device__ __forceinline__ void mfma_sweep(f32x4 (&acc)[MT][NT], const uint4 (&w
   }
 }
 
-// Copy `bytes` (a multiple of 1024) of a ring entry into LDS with direct
-// global->LDS loads: each wave moves 1 KB per instruction (lane i -> +16*i);
-// nothing goes through registers, so the whole entry is in flight at once.
-__device__ __forceinline__ void stage_to_lds(char __attribute__((address_space(3)))* dst, const char* src,
-                                             int bytes, int wave, int nw, int lane) {
-  for (int c = wave; c < bytes / 1024; c += nw)
-    __builtin_amdgcn_global_load_lds(
-        (const void __attribute__((address_space(1)))*)(src + (size_t)c * 1024 + lane * 16),
-        (void __attribute__((address_space(3)))*)(dst + c * 1024), 16, 0, 0);
+// Copy granules [g0, g0 + n) of a ring entry to the same offsets in LDS with
+// direct global->LDS loads (lane i of an instruction moves 16 bytes to
+// M0 + 16*i); nothing passes through registers, so the whole range is in
+// flight at once.  The issuing wave waits for its own loads only.
+__device__ __forceinline__ void stage_granules(char __attribute__((address_space(3)))* lds, const char* src,
+                                               int g0, int n, int gran, int lane) {
+  const int n16 = n * (gran >> 4);
+  const int base = g0 * gran;
+  for (int c = 0; c < n16; c += 64)
+    if (c + lane < n16)
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(src + base + (size_t)(c + lane) * 16),
+          (void __attribute__((address_space(3)))*)(lds + base + c * 16), 16, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // ====================================================================== fwd
@@ -174,8 +187,7 @@ template <int MODE, bool BF16, int NT, int MT, int KPW, int NW>
 __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   constexpr int G = gates_of(MODE);
   constexpr int R = reserve_slots(MODE);
-  constexpr int KC = kchunk<BF16>();
-  constexpr int PER = KC / 4;
+  constexpr int PER = kchunk<BF16>() / 4;   // values per lane per MFMA (16 bytes)
   constexpr int NCOL = NT * 16;
   constexpr int NROW = MT * 16;
   constexpr int ES = BF16 ? 2 : 4;
@@ -183,7 +195,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   __shared__ float red[NW][NROW][NCOL + 1];
   __shared__ float sh_h[NROW * NCOL];
   __shared__ float sh_c[NROW * NCOL];
-  __shared__ int s_flag;
+  __shared__ int s_fail;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
@@ -204,10 +216,29 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   const bool inproj = p.wavefront && li > 0;
   const int GB = (MODE == MODE_GRU && inproj) ? 4 : G;   // column blocks
   const int I_l = p.in_l[li];
-  const int Kh = p.nwg * U;               // padded width of h (unit order)
-  const int Kx = inproj ? Kh : 0;         // the layer below's h in the wavefront
-  const int nch = (Kx + Kh + KC - 1) / KC;
   const int DC = p.D * p.nchunk;
+  const int gran = p.gran;
+  const int rmax = (gran >> 4) - 1;   // last (padded) row of a granule
+
+  // K in granules: [the layer below's h (wavefront) | own h], each in unit
+  // order, PER units per granule; this wave holds granules [g0, g1)
+  const int UJ = U / PER;
+  const int ngr_h = p.nwg * UJ;
+  const int xoff = inproj ? ngr_h : 0;
+  const int ngr = xoff + ngr_h;
+  const int g0 = (wave * ngr) / NW, g1 = ((wave + 1) * ngr) / NW;
+  const int nmine = g1 - g0;
+  // the producers those granules come from
+  int xa0 = 0, xn = 0, ha0 = 0, hn = 0;
+  if (nmine > 0 && g0 < xoff) {
+    xa0 = g0 / UJ;
+    xn = (min(g1, xoff) - 1) / UJ + 1 - xa0;
+  }
+  if (nmine > 0 && g1 > xoff) {
+    ha0 = (max(g0, xoff) - xoff) / UJ;
+    hn = (g1 - xoff - 1) / UJ + 1 - ha0;
+  }
+  const int xflag0 = (grp - DC) * p.nwg + xa0, hflag0 = grp * p.nwg + ha0;
 
   char* ring = reinterpret_cast<char*>(p.xch) + (size_t)grp * p.ring_group;
   const char* ring_below = inproj ? reinterpret_cast<const char*>(p.xch) + (size_t)(grp - DC) * p.ring_group : ring;
@@ -218,7 +249,10 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   uint4 wf[KPW][NT];
 #pragma unroll
   for (int kk = 0; kk < KPW; ++kk) {
-    const int gc = wave + kk * NW;
+    const int gl = kk * 4 + fq;
+    const int gg = g0 + gl;
+    const bool xpart = gg < xoff;
+    const int kbase = (xpart ? gg : gg - xoff) * PER;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       uint32_t v[PER];
@@ -226,7 +260,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
       for (int e = 0; e < PER; ++e) v[e] = 0u;
       const int n = nt * 16 + fr;
       const int gb = n / U, j = n - gb * U;
-      if (gc < nch && gb < GB && j < Uact) {
+      if (gl < nmine && gb < GB && j < Uact) {
         int gate = gb;
         bool use_x = true, use_h = true;
         if (MODE == MODE_GRU && inproj) {
@@ -237,12 +271,11 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         const size_t row = (size_t)d * GH + (size_t)gate * H + u0 + j;
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-          const int k = gc * KC + fq * PER + e;
-          if (k < Kx) {
+          const int k = kbase + e;
+          if (xpart) {
             if (use_x && k < I_l) v[e] = w_bits<BF16>(wih, row * I_l + k);
           } else {
-            const int kh = k - Kx;
-            if (use_h && kh < H) v[e] = w_bits<BF16>(whh, row * H + kh);
+            if (use_h && k < H) v[e] = w_bits<BF16>(whh, row * H + k);
           }
         }
       }
@@ -258,8 +291,9 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   const int qu = u0 + qj, qbg = b0 + qb;
   const size_t st_idx = (((size_t)li * D + d) * B + qbg) * H + qu;
   const size_t hx_idx = (((size_t)layer * D + d) * B + qbg) * H + qu;
-  const size_t my_off = (size_t)slice * p.slice + ((size_t)qb * U + qj) * ES;
+  const size_t my_off = (size_t)(slice * UJ + qj / PER) * gran + qb * 16 + (qj % PER) * ES;
 
+  if (tid == 0) s_fail = 0;
   if (p.s_begin < 0) {
     float hv = 0.f, cv = 0.f;
     if (qv) {
@@ -277,12 +311,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   }
   __syncthreads();
 
-  int wgroups[2] = {grp, grp};
-  int nwait = 1;
-  if (inproj) { wgroups[0] = grp - DC; wgroups[1] = grp; nwait = 2; }
-
   const size_t ystride_t = (size_t)B * D * H;
-  const int pslice = p.slice;
   for (int s = max(p.s_begin, 0); s < p.s_end; ++s) {
     const int t_rel = p.wavefront ? s - li : s;
     const bool active = t_rel >= 0 && t_rel < T;
@@ -316,23 +345,35 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     float bhn = 0.f;
     if (MODE == MODE_GRU && !inproj && qv) bhn = p.b_hh[li][(size_t)d * GH + 2 * H + qu];
 
-    if (p.persistent) {
-      if (!wait_groups(p.flags, p.err, p.spin_limit, wgroups, nwait, p.nwg, (unsigned)(s + 1), &s_flag))
-        return;
-    }
+    // each wave waits only for the producers of its own granules
     f32x4 acc[MT][NT];
-    const char* eh = ring + (size_t)s * p.ring_step;
-    const char* ex = ring_below + (size_t)s * p.ring_step;
-    mfma_sweep<BF16, NT, MT, KPW, NW>(acc, wf, wave, fr, fq, nch, Bact,
-        [&](int k0, int row, bool v) -> uint4 {
-          const bool xpart = k0 < Kx;
-          const int kk = xpart ? k0 : k0 - Kx;
-          v = v && kk < Kh;
-          const int pp = kk / U, j0 = kk - pp * U;
-          const char* a = (xpart ? ex : eh) + (v ? pp * pslice + (row * U + j0) * ES : 0);
-          const uint4 t4 = *reinterpret_cast<const uint4*>(a);
-          return v ? t4 : make_uint4(0u, 0u, 0u, 0u);
-        });
+    bool ok = true;
+    if (p.persistent) {
+      if (p.group_poll) {   // wave 0 waits for every producer, the others at the barrier
+        if (wave == 0 && !wave_wait(p.flags, p.err, p.spin_limit, (grp - DC) * p.nwg, inproj ? p.nwg : 0,
+                                    grp * p.nwg, p.nwg, (unsigned)(s + 1)) && lane == 0)
+          s_fail = 1;
+        __syncthreads();
+        ok = s_fail == 0;
+      } else {
+        ok = wave_wait(p.flags, p.err, p.spin_limit, xflag0, xn, hflag0, hn, (unsigned)(s + 1));
+      }
+    }
+    if (ok) {
+      const char* eh = ring + (size_t)s * p.ring_step;
+      const char* ex = ring_below + (size_t)s * p.ring_step;
+      mfma_sweep<BF16, NT, MT, KPW>(acc, wf, fr, fq, nmine, rmax, [&](int gl, int row) -> uint4 {
+        const int gg = g0 + gl;
+        const bool xpart = gg < xoff;
+        return *reinterpret_cast<const uint4*>((xpart ? ex : eh) + (xpart ? gg : gg - xoff) * gran + row * 16);
+      });
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (lane == 0) s_fail = 1;
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -340,8 +381,10 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[wave][mt * 16 + fq * 4 + r][nt * 16 + fr] = acc[mt][nt][r];
     __syncthreads();
+    if (s_fail) return;   // every wave leaves after the same barrier
 
     float hnew = 0.f;
+    float rv[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
     if (qv) {
       float pre[4];
 #pragma unroll
@@ -354,9 +397,6 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         pre[gb] = v;
       }
       const float hprev = sh_h[qb * NCOL + qj];
-      float* res = (p.training && R > 0)
-                       ? p.reserve[li] + (((size_t)d * T + t) * B + qbg) * R * H + qu
-                       : nullptr;
       if (MODE == MODE_LSTM) {
         const float ig = sigmoidf_(pre[0] + gxv[0]);
         const float fg = sigmoidf_(pre[1] + gxv[1]);
@@ -365,9 +405,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         const float cn = fg * sh_c[qb * NCOL + qj] + ig * gg;
         hnew = og * tanhf_(cn);
         sh_c[qb * NCOL + qj] = cn;
-        if (res) {
-          res[0] = ig; res[H] = fg; res[2 * H] = gg; res[3 * H] = og; res[4 * H] = cn;
-        }
+        rv[0] = ig; rv[1] = fg; rv[2] = gg; rv[3] = og; rv[4] = cn;
       } else if (MODE == MODE_GRU) {
         const float rg = sigmoidf_(pre[0] + gxv[0]);
         const float zg = sigmoidf_(pre[1] + gxv[1]);
@@ -376,7 +414,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         else { gin = gxv[2]; ghn = pre[2] + bhn; }
         const float ng = tanhf_(gin + rg * ghn);
         hnew = (1.f - zg) * ng + zg * hprev;
-        if (res) { res[0] = rg; res[H] = zg; res[2 * H] = ng; res[3 * H] = ghn; }
+        rv[0] = rg; rv[1] = zg; rv[2] = ng; rv[3] = ghn;
       } else {
         hnew = tanhf_(pre[0] + gxv[0]);
       }
@@ -384,7 +422,14 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     }
     // the exchange store first: it is what the other workgroups wait for
     if (qw) ring_store<BF16>(ring + (size_t)(s + 1) * p.ring_step, my_off, hnew);
-    if (qv) p.y[li][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = hnew;
+    if (qv) {
+      p.y[li][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = hnew;
+      if (p.training && R > 0) {
+        float* res = p.reserve[li] + (((size_t)d * T + t) * B + qbg) * R * H + qu;
+#pragma unroll
+        for (int r = 0; r < R; ++r) res[(size_t)r * H] = rv[r];
+      }
+    }
     if (p.persistent) publish(p.flags, (unsigned)(s + 2));
     __syncthreads();   // red and sh_* are reused by the next step
   }
@@ -405,8 +450,7 @@ template <int MODE, bool BF16, int NT, int MT, int KPW, int NW>
 __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   constexpr int G = gates_of(MODE);
   constexpr int R = reserve_slots(MODE);
-  constexpr int KC = kchunk<BF16>();
-  constexpr int PER = KC / 4;
+  constexpr int PER = kchunk<BF16>() / 4;
   constexpr int NCOL = NT * 16;
   constexpr int NROW = MT * 16;
   constexpr int ES = BF16 ? 2 : 4;
@@ -414,7 +458,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   __shared__ float red[NW][NROW][NCOL + 1];
   __shared__ float sh_dh[NROW * NCOL];
   __shared__ float sh_dc[NROW * NCOL];
-  __shared__ int s_flag;
+  __shared__ int s_fail;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
@@ -425,33 +469,46 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   const int d = grp / p.nchunk;
   const int U = p.U, H = p.H, D = p.D, B = p.B, T = p.T;
   const int GH = G * H;
-  const int Kh = p.nwg * U;
-  const int KP = G * Kh;
   const int u0 = slice * U;
   const int Uact = max(0, min(U, H - u0));
   const int b0 = c * p.Bc;
   const int Bact = min(p.Bc, B - b0);
-  const int nch = (KP + KC - 1) / KC;
+  const int gran = p.gran;
+  const int rmax = (gran >> 4) - 1;
+
+  // K in granules: producer slice pp holds (gate g, units pp*U + jb*PER ..)
+  // as granule pp*G*UJ + g*UJ + jb; this wave holds granules [g0, g1)
+  const int UJ = U / PER;
+  const int GU = G * UJ;
+  const int ngr = p.nwg * GU;
+  const int g0 = (wave * ngr) / NW, g1 = ((wave + 1) * ngr) / NW;
+  const int nmine = g1 - g0;
+  const int pa0 = g0 / GU;
+  const int pn = nmine > 0 ? (g1 - 1) / GU + 1 - pa0 : 0;
+  const int flag0 = grp * p.nwg + pa0;
 
   char* ring = reinterpret_cast<char*>(p.xch) + (size_t)grp * p.ring_group;
 
-  // ---- W_hh^T slice -> registers: B(k = g*Kh + uu, n = j) = W_hh[g*H + uu][u0 + j]
+  // ---- W_hh^T slice -> registers: B(k = (g, uu), n = j) = W_hh[g*H + uu][u0 + j]
   uint4 wf[KPW][NT];
 #pragma unroll
   for (int kk = 0; kk < KPW; ++kk) {
-    const int gc = wave + kk * NW;
+    const int gl = kk * 4 + fq;
+    const int gi = g0 + gl;
+    const int pp = gi / GU, rem = gi - pp * GU;
+    const int g = rem / UJ, jb = rem - g * UJ;
+    const int ubase = pp * U + jb * PER;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       uint32_t v[PER];
 #pragma unroll
       for (int e = 0; e < PER; ++e) v[e] = 0u;
       const int j = nt * 16 + fr;
-      if (gc < nch && j < Uact) {
+      if (gl < nmine && j < Uact) {
 #pragma unroll
         for (int e = 0; e < PER; ++e) {
-          const int k = gc * KC + fq * PER + e;
-          const int g = k / Kh, uu = k - g * Kh;
-          if (g < G && uu < H) v[e] = w_bits<BF16>(p.w_hh, ((size_t)d * GH + (size_t)g * H + uu) * H + u0 + j);
+          const int uu = ubase + e;
+          if (uu < H) v[e] = w_bits<BF16>(p.w_hh, ((size_t)d * GH + (size_t)g * H + uu) * H + u0 + j);
         }
       }
       wf[kk][nt] = pack_frag<BF16>(v);
@@ -464,7 +521,9 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   const bool qv = qw && qj < Uact;
   const int qu = u0 + qj, qbg = b0 + qb;
   const size_t sidx = ((size_t)d * B + qbg) * H + qu;   // [D][B][H] state index
-  const size_t my_off = (size_t)slice * p.slice + ((size_t)qb * G * U + qj) * ES;
+  // ring offset of gate 0 of (qb, qj); gate g is g*UJ granules further
+  const size_t my_off = (size_t)(slice * GU + qj / PER) * gran + qb * 16 + (qj % PER) * ES;
+  if (tid == 0) s_fail = 0;
   if (qv) {
     if (p.s_begin == 0) {
       sh_dh[qb * NCOL + qj] = p.dhy ? p.dhy[sidx] : 0.f;
@@ -476,10 +535,8 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   }
   __syncthreads();
 
-  const int wgroups[2] = {grp, grp};
   const size_t ystride_t = (size_t)B * D * H;
-  const int pslice = p.slice;
-  const int rs = (int)p.ring_step;
+  auto lds = (char __attribute__((address_space(3)))*)(dyn_lds);
   for (int s = p.s_begin; s < p.s_end; ++s) {
     const bool final_phase = (s == T);
     const int t = (d == 0) ? T - 1 - s : s;
@@ -507,33 +564,32 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
     if (s > 0) {
       f32x4 acc[MT][NT];
       const char* e = ring + (size_t)s * p.ring_step;
-      auto frag_off = [&](int k0, int row, bool& v) -> int {
-        const int g = k0 / Kh, uu = k0 - g * Kh;
-        v = v && g < G;
-        const int pp = uu / U, j0 = uu - pp * U;
-        return pp * pslice + ((row * G + g) * U + j0) * ES;
-      };
+      // each wave waits only for the producers of its own granules
+      bool ok = true;
       if (p.persistent) {
-        if (!wait_groups(p.flags, p.err, p.spin_limit, wgroups, 1, p.nwg, (unsigned)s, &s_flag)) return;
+        if (p.group_poll) {
+          if (wave == 0 && !wave_wait(p.flags, p.err, p.spin_limit, grp * p.nwg, p.nwg, 0, 0, (unsigned)s) &&
+              lane == 0)
+            s_fail = 1;
+          __syncthreads();
+          ok = s_fail == 0;
+        } else {
+          ok = wave_wait(p.flags, p.err, p.spin_limit, flag0, pn, 0, 0, (unsigned)s);
+        }
       }
-      if (p.stage) {
-        auto lds = (char __attribute__((address_space(3)))*)(dyn_lds);
-        stage_to_lds(lds, e, rs, wave, NW, lane);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        mfma_sweep<BF16, NT, MT, KPW, NW>(acc, wf, wave, fr, fq, nch, Bact,
-            [&](int k0, int row, bool v) -> uint4 {
-              const int off = frag_off(k0, row, v);
-              const uint4 t4 = lds_load16(lds + (v ? off : 0));
-              return v ? t4 : make_uint4(0u, 0u, 0u, 0u);
-            });
+      if (ok && p.stage) {
+        stage_granules(lds, e, g0, nmine, gran, lane);
+        mfma_sweep<BF16, NT, MT, KPW>(acc, wf, fr, fq, nmine, rmax,
+            [&](int gl, int row) -> uint4 { return lds_load16(lds + (g0 + gl) * gran + row * 16); });
+      } else if (ok) {
+        mfma_sweep<BF16, NT, MT, KPW>(acc, wf, fr, fq, nmine, rmax,
+            [&](int gl, int row) -> uint4 { return *reinterpret_cast<const uint4*>(e + (g0 + gl) * gran + row * 16); });
       } else {
-        mfma_sweep<BF16, NT, MT, KPW, NW>(acc, wf, wave, fr, fq, nch, Bact,
-            [&](int k0, int row, bool v) -> uint4 {
-              const int off = frag_off(k0, row, v);
-              const uint4 t4 = *reinterpret_cast<const uint4*>(e + (v ? off : 0));
-              return v ? t4 : make_uint4(0u, 0u, 0u, 0u);
-            });
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (lane == 0) s_fail = 1;
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -542,6 +598,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) red[wave][mt * 16 + fq * 4 + r][nt * 16 + fr] = acc[mt][nt][r];
       __syncthreads();
+      if (s_fail) return;   // every wave leaves after the same barrier
       if (qv) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) dhrec += red[w][qb][qj];
@@ -592,7 +649,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
       if (qw) {
         char* en = ring + (size_t)(s + 1) * p.ring_step;
 #pragma unroll
-        for (int g = 0; g < G; ++g) ring_store<BF16>(en, my_off + (size_t)g * U * ES, dgh[g]);
+        for (int g = 0; g < G; ++g) ring_store<BF16>(en, my_off + (size_t)g * UJ * gran, dgh[g]);
       }
       if (qv) {
         // gate gradients for the dX product ([T*B, D*G*H]) and, transposed
@@ -688,11 +745,22 @@ struct BwdK {
 #define RNN_BWD_CONFIGS(X, M, BF) \
   X(M, BF, 1, 1, 8, 4)            \
   X(M, BF, 1, 2, 8, 4)            \
+  X(M, BF, 1, 1, 16, 4)           \
   X(M, BF, 1, 2, 16, 4)           \
+  X(M, BF, 1, 1, 32, 4)           \
   X(M, BF, 1, 2, 32, 4)           \
+  X(M, BF, 1, 1, 16, 8)           \
   X(M, BF, 1, 2, 16, 8)           \
   X(M, BF, 1, 2, 32, 8)           \
-  X(M, BF, 1, 1, 32, 8)
+  X(M, BF, 1, 1, 32, 8)           \
+  RNN_BWD_WIDE_##BF(X, M)
+
+// 64 K chunks per wave: fp32 only (the bf16 fragments would not fit the
+// register file of one wave)
+#define RNN_BWD_WIDE_false(X, M) \
+  X(M, false, 1, 1, 64, 4)       \
+  X(M, false, 1, 2, 64, 4)
+#define RNN_BWD_WIDE_true(X, M)
 
 int max_resident(const void* f, int nthr, size_t lds) {
   int per_cu = 0;

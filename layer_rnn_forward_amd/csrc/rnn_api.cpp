@@ -42,6 +42,7 @@ struct ProfPending {
 // Recurrent launch plan for one sweep kind.
 struct SweepPlan {
   RecConfig cfg{};
+  int nchunk = 0, Bc = 0;   // batch chunks of Bc rows
   int U = 0, nwg = 0, groups = 0, grid = 0;
   bool persistent = false;
   size_t lds = 0;   // dynamic LDS for staging ring entries (0: fragments read from global)
@@ -49,8 +50,7 @@ struct SweepPlan {
 
 struct Plan {
   int T = 0, B = 0, training = 0;
-  int Bc = 0, nchunk = 0;
-  int fslice = 0, bslice = 0;
+  int fslice = 0, bslice = 0, fgran = 0, bgran = 0;
   size_t fring_step = 0, fring_group = 0, bring_step = 0, bring_group = 0;
   bool wavefront = false;
   SweepPlan fwd, bwd;
@@ -116,8 +116,9 @@ void layout_weights(rnn_desc* h) {
 const RecConfig kFwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 1, 16, 4}, {1, 2, 16, 4}, {2, 1, 8, 4},
                               {2, 2, 8, 4},  {2, 1, 16, 4}, {2, 2, 16, 4}, {4, 1, 8, 8},  {4, 2, 8, 8},
                               {1, 2, 32, 4}, {1, 2, 16, 8}, {2, 2, 16, 8}, {4, 2, 16, 8}};
-const RecConfig kBwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 2, 16, 4}, {1, 2, 32, 4},
-                              {1, 2, 16, 8}, {1, 2, 32, 8}, {1, 1, 32, 8}};
+const RecConfig kBwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 1, 16, 4}, {1, 2, 16, 4},
+                              {1, 1, 32, 4}, {1, 2, 32, 4}, {1, 1, 64, 4}, {1, 2, 64, 4},
+                              {1, 1, 16, 8}, {1, 2, 16, 8}, {1, 2, 32, 8}, {1, 1, 32, 8}};
 
 // Units per workgroup are a multiple of the per-lane MFMA k run (8 bf16 / 4
 // fp32 values, 16 bytes) so that every A fragment of the exchange comes from
@@ -128,8 +129,6 @@ int unit_quantum(const rnn_desc* h) { return h->wtype == RNN_W_BF16 ? 8 : 4; }
 // `target_wgs` workgroups, the gate columns of U units fit the MFMA tiles, the
 // K chunks fit the registers, and each epilogue thread owns one (row, unit).
 bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepPlan* sp) {
-  const int bf = h->wtype == RNN_W_BF16;
-  const int KC = bf ? 32 : 16;
   const int Q = unit_quantum(h);
   const int GB = (h->mode == RNN_GRU && inproj) ? 4 : h->G;
   const int target_wgs = std::max(1, env_int("RNN_FWD_TARGET_WGS", 128));
@@ -139,12 +138,11 @@ bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepP
   U = std::max(Q, std::min(U, ceil_div(h->H, Q) * Q));
   for (int tryU = U; tryU >= Q; tryU -= Q) {
     const int nwg = ceil_div(h->H, tryU);
-    const int Kh = nwg * tryU;
-    const int nch = ceil_div((inproj ? 2 : 1) * Kh, KC);
+    const int ngr = (inproj ? 2 : 1) * nwg * (tryU / Q);   // K granules
     for (const RecConfig& c : kFwdCfgs) {
       if (c.mt != mt) continue;
       if (GB * tryU > 16 * c.nt || Bc * tryU > 64 * c.nwaves) continue;
-      if (nch > c.kpw * c.nwaves) continue;
+      if (ceil_div(ceil_div(ngr, c.nwaves), 4) > c.kpw) continue;
       sp->cfg = c;
       sp->U = tryU;
       sp->nwg = nwg;
@@ -157,18 +155,16 @@ bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepP
 }
 
 bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, SweepPlan* sp) {
-  const int bf = h->wtype == RNN_W_BF16;
-  const int KC = bf ? 32 : 16;
   const int Q = unit_quantum(h);
   int U = ceil_div(std::max(1, env_int("RNN_BWD_UNITS", 8)), Q) * Q;
   U = std::max(Q, std::min(U, ceil_div(h->H, Q) * Q));
   for (int tryU = U; tryU >= Q; tryU -= Q) {
     const int nwg = ceil_div(h->H, tryU);
-    const int nch = ceil_div(h->G * nwg * tryU, KC);
+    const int ngr = h->G * nwg * (tryU / Q);   // K granules
     for (const RecConfig& c : kBwdCfgs) {
-      if (c.mt != mt) continue;
+      if (c.mt != mt || (c.kpw > 32 && h->wtype == RNN_W_BF16)) continue;
       if (tryU > 16 * c.nt || Bc * tryU > 64 * c.nwaves) continue;
-      if (nch > c.kpw * c.nwaves) continue;
+      if (ceil_div(ceil_div(ngr, c.nwaves), 4) > c.kpw) continue;
       sp->cfg = c;
       sp->U = tryU;
       sp->nwg = nwg;
@@ -199,42 +195,24 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   const int bf = h->wtype == RNN_W_BF16;
   const size_t es = bf ? 2 : 4;
   const int Bq = std::max(B, 1);
-  p.nchunk = ceil_div(Bq, 32);
-  p.Bc = ceil_div(Bq, p.nchunk);
-  const int mt = ceil_div(p.Bc, 16);
-  p.wavefront = (h->D == 1 && h->L > 1 && h->L <= kMaxLayersPerLaunch &&
-                 env_int("RNN_NO_WAVEFRONT", 0) == 0);
-  const int fl = p.wavefront ? h->L : 1;
-  if (!plan_fwd(h, mt, p.Bc, fl * h->D * p.nchunk, p.wavefront, &p.fwd) ||
-      !plan_bwd(h, mt, p.Bc, h->D * p.nchunk, &p.bwd)) {
-    p.status = RNN_STATUS_UNSUPPORTED;
-    return p;
-  }
-  // wavefront: every workgroup polls its own and the layer below's flags
-  if (p.wavefront && 2 * p.fwd.nwg > kMaxWaitFlags) p.wavefront = false;
-  if (!p.wavefront && p.fwd.groups != h->D * p.nchunk) {
-    if (!plan_fwd(h, mt, p.Bc, h->D * p.nchunk, false, &p.fwd)) {
-      p.status = RNN_STATUS_UNSUPPORTED;
-      return p;
-    }
-  }
-  if (p.fwd.nwg > kMaxWaitFlags || p.bwd.nwg > kMaxWaitFlags) {
-    p.status = RNN_STATUS_UNSUPPORTED;
-    return p;
-  }
-  // exchange rings: one entry per step, one 128-byte-aligned slice per
-  // producer, entries padded to 1 KB (the LDS staging granule)
-  const int s_total = T + (p.wavefront ? h->L : 1) - 1;
-  p.fslice = (int)(((size_t)p.Bc * p.fwd.U * es + 127) / 128 * 128);
-  p.fring_step = ((size_t)p.fwd.nwg * p.fslice + 1023) / 1024 * 1024;
-  p.fring_group = align_up(p.fring_step * (size_t)(s_total + 1));
-  p.bslice = (int)(((size_t)p.Bc * h->G * p.bwd.U * es + 127) / 128 * 128);
-  p.bring_step = ((size_t)p.bwd.nwg * p.bslice + 1023) / 1024 * 1024;
-  p.bring_group = align_up(p.bring_step * (size_t)(T + 1));
-
+  auto chunk = [&](int max_bc, SweepPlan& sp) {
+    max_bc = std::max(1, std::min(32, max_bc));
+    sp.nchunk = ceil_div(Bq, max_bc);
+    sp.Bc = ceil_div(Bq, sp.nchunk);
+  };
+  const int Q = unit_quantum(h);
+  // rows of a granule: the batch chunk, padded so that a producer's slice
+  // (granules_per_slice granules of rows x 16 bytes) is whole 128-byte lines
+  auto padded_rows = [&](int Bc, int granules_per_slice) {
+    int rows = Bc;
+    while ((granules_per_slice * rows) % 8 != 0) ++rows;
+    return rows;
+  };
   const int sched = h->sched;
   const bool allow_stage = env_int("RNN_NO_STAGE", 0) == 0;
-  auto decide = [&](SweepPlan& sp, bool fwd, size_t stage_bytes) {
+  // co-residency: returns whether every workgroup of the sweep fits on the
+  // GPU at once (with LDS staging if it fits, else without)
+  auto fit = [&](SweepPlan& sp, bool fwd, size_t stage_bytes) {
     auto res = [&](size_t lds) {
       return fwd ? rnn_fwd_max_resident(h->mode, bf, sp.cfg, lds)
                  : rnn_bwd_max_resident(h->mode, bf, sp.cfg, lds);
@@ -245,14 +223,69 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
     if (!lds) maxres = res(0);
     sp.lds = lds;
     const bool fits = maxres >= sp.grid && maxres > 0;
-    if (sched == RNN_SCHED_STEPPED) sp.persistent = false;
-    else if (sched == RNN_SCHED_PERSISTENT) {
-      sp.persistent = true;
-      if (!fits) p.status = RNN_STATUS_NOT_CORESIDENT;
-    } else sp.persistent = fits;
+    sp.persistent = sched == RNN_SCHED_PERSISTENT || (sched == RNN_SCHED_AUTO && fits);
+    return fits;
   };
-  decide(p.fwd, true, 0);   // the forward reads its fragments straight from the ring
-  if (training) decide(p.bwd, false, p.bring_step);
+
+  // ---- forward sweep: batch chunks of up to 32 rows
+  chunk(env_int("RNN_FWD_MAX_BC", 32), p.fwd);
+  p.wavefront = (h->D == 1 && h->L > 1 && h->L <= kMaxLayersPerLaunch &&
+                 env_int("RNN_NO_WAVEFRONT", 0) == 0);
+  const int fl = p.wavefront ? h->L : 1;
+  const int fmt = ceil_div(p.fwd.Bc, 16);
+  if (!plan_fwd(h, fmt, p.fwd.Bc, fl * h->D * p.fwd.nchunk, p.wavefront, &p.fwd)) {
+    p.status = RNN_STATUS_UNSUPPORTED;
+    return p;
+  }
+  // wavefront: every workgroup polls its own and the layer below's flags
+  if (p.wavefront && 2 * p.fwd.nwg > kMaxWaitFlags) p.wavefront = false;
+  if (!p.wavefront && p.fwd.groups != h->D * p.fwd.nchunk) {
+    if (!plan_fwd(h, fmt, p.fwd.Bc, h->D * p.fwd.nchunk, false, &p.fwd)) {
+      p.status = RNN_STATUS_UNSUPPORTED;
+      return p;
+    }
+  }
+  if (p.fwd.nwg > kMaxWaitFlags) {
+    p.status = RNN_STATUS_UNSUPPORTED;
+    return p;
+  }
+  // exchange rings: one entry per step, entries padded to 1 KB
+  const int s_total = T + (p.wavefront ? h->L : 1) - 1;
+  p.fgran = padded_rows(p.fwd.Bc, p.fwd.U / Q) * 16;
+  p.fslice = (p.fwd.U / Q) * p.fgran;
+  p.fring_step = ((size_t)p.fwd.nwg * p.fslice + 1023) / 1024 * 1024;
+  p.fring_group = align_up(p.fring_step * (size_t)(s_total + 1));
+  // the forward reads its fragments straight from the ring
+  if (!fit(p.fwd, true, 0) && sched == RNN_SCHED_PERSISTENT) p.status = RNN_STATUS_NOT_CORESIDENT;
+
+  // ---- backward sweep: batch chunks of up to 16 rows (one MFMA row tile,
+  // half the exchanged bytes per workgroup) when that many workgroups fit
+  // at once, else up to 32
+  if (training) {
+    auto plan_b = [&](int max_bc) {
+      chunk(max_bc, p.bwd);
+      if (!plan_bwd(h, ceil_div(p.bwd.Bc, 16), p.bwd.Bc, h->D * p.bwd.nchunk, &p.bwd) ||
+          p.bwd.nwg > kMaxWaitFlags)
+        return false;
+      p.bgran = padded_rows(p.bwd.Bc, h->G * p.bwd.U / Q) * 16;
+      p.bslice = h->G * (p.bwd.U / Q) * p.bgran;
+      p.bring_step = ((size_t)p.bwd.nwg * p.bslice + 1023) / 1024 * 1024;
+      p.bring_group = align_up(p.bring_step * (size_t)(T + 1));
+      return true;
+    };
+    const int bmax = std::max(1, std::min(32, env_int("RNN_BWD_MAX_BC", 16)));
+    bool ok = plan_b(bmax);
+    bool fits = ok && fit(p.bwd, false, p.bring_step);
+    if ((!ok || !fits) && bmax < 32 && Bq > bmax) {
+      ok = plan_b(32);
+      fits = ok && fit(p.bwd, false, p.bring_step);
+    }
+    if (!ok) {
+      p.status = RNN_STATUS_UNSUPPORTED;
+      return p;
+    }
+    if (!fits && sched == RNN_SCHED_PERSISTENT) p.status = RNN_STATUS_NOT_CORESIDENT;
+  }
 
   const size_t TB = (size_t)T * B;
   const size_t dgh = (size_t)h->D * h->G * h->H;
@@ -487,11 +520,13 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   f.B = B;
   f.H = h->H;
   f.D = h->D;
-  f.nchunk = p.nchunk;
-  f.Bc = p.Bc;
+  f.nchunk = p.fwd.nchunk;
+  f.Bc = p.fwd.Bc;
   f.U = p.fwd.U;
   f.nwg = p.fwd.nwg;
   f.slice = p.fslice;
+  f.gran = p.fgran;
+  f.group_poll = env_int("RNN_GROUP_POLL", 0);
   f.ring_step = (long long)p.fring_step;
   f.ring_group = (long long)p.fring_group;
   f.stage = p.fwd.lds > 0 ? 1 : 0;
@@ -511,7 +546,7 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   auto run_sweep = [&](int nlayers) -> rnn_status_t {
     f.nlayers = nlayers;
     f.s_total = T + nlayers - 1;
-    const int grid = p.fwd.nwg * nlayers * h->D * p.nchunk;
+    const int grid = p.fwd.nwg * nlayers * h->D * p.fwd.nchunk;
     if (f.persistent) RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
     if (f.persistent) {
       f.s_begin = -1;
@@ -687,11 +722,13 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
   b.B = B;
   b.H = h->H;
   b.D = h->D;
-  b.nchunk = p.nchunk;
-  b.Bc = p.Bc;
+  b.nchunk = p.bwd.nchunk;
+  b.Bc = p.bwd.Bc;
   b.U = p.bwd.U;
   b.nwg = p.bwd.nwg;
   b.slice = p.bslice;
+  b.gran = p.bgran;
+  b.group_poll = env_int("RNN_GROUP_POLL", 0);
   b.ring_step = (long long)p.bring_step;
   b.ring_group = (long long)p.bring_group;
   b.stage = p.bwd.lds > 0 ? 1 : 0;

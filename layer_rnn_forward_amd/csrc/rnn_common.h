@@ -78,9 +78,11 @@ struct FwdParams {
   int nchunk, Bc;         // batch chunks of Bc rows
   int U, nwg;             // units per workgroup, workgroups per group
   int slice;              // bytes of one producer's slice in a ring entry (multiple of 128)
+  int gran;               // bytes of one granule: padded rows x 16 (U/PER granules per slice)
   long long ring_step;    // bytes of one ring entry (nwg * slice)
   long long ring_group;   // bytes of one group's ring (entries * ring_step)
   int stage;              // 1: copy each consumed ring entry into LDS first
+  int group_poll;         // 1: one wave polls every producer; 0: each wave its own
   int s_begin, s_end;     // global steps [s_begin, s_end); -1 is the prologue
   int s_total;            // T + nlayers - 1
   int persistent, training, wavefront;
@@ -108,9 +110,11 @@ struct FwdParams {
 struct BwdParams {
   int T, B, H, D;
   int nchunk, Bc, U, nwg;
-  int slice;              // bytes of one producer's slice (Bc x G x U values, padded to 128)
+  int slice;              // bytes of one producer's slice (G*U/PER granules, a multiple of 128)
+  int gran;               // bytes of one granule: padded rows x 16
   long long ring_step, ring_group;
   int stage;              // 1: copy each consumed ring entry into LDS first
+  int group_poll;         // 1: one wave polls every producer; 0: each wave its own
   int s_begin, s_end;     // processing steps; s == T is the final dh0 phase
   int persistent;
   const void* w_hh;       // layer block [D*G*H, H]
