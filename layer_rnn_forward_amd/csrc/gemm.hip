@@ -10,12 +10,25 @@
 //
 // One layout only: C[m, n] = sum_k A[m, k] * B[n, k], both operands
 // K-contiguous, both in the compute type (bf16 with fp32 accumulation, or
-// fp32).  Tile 128x128, K step 32 (fp32) / 64 (bf16), 256 threads as 2x2
-// waves of 64x64 built from 16x16 MFMA tiles; operands staged through
-// double-buffered LDS with 16-byte loads and stores.  Tiles are numbered
-// m-major and dealt to the 8 XCDs in contiguous runs so that the tiles sharing
-// an A row-block share an L2.  Optional split-K writes fp32 partials that a
-// second kernel sums in a fixed order (deterministic).
+// fp32).  Tile 128x128, K step 32 (fp32) / 64 (bf16) -- 128 bytes of every
+// tile row per step -- 256 threads as 2x2 waves of 64x64 built from 16x16
+// MFMA tiles.  Tiles are numbered m-major and dealt to the 8 XCDs in
+// contiguous runs so that the tiles sharing an A row-block share an L2.
+// Optional split-K writes fp32 partials that a second kernel sums in a fixed
+// order (deterministic).
+//
+// Two kernels share that structure:
+//  * gemm_lds_kernel, used whenever every operand row is 16-byte aligned and
+//    K is a whole number of 16-byte vectors: operands go straight from global
+//    memory into LDS (global_load_lds, no register staging) through a
+//    two-stage pipeline, in an XOR-swizzled layout (16-byte slot s of row r
+//    holds k-vector s ^ (r & 7)) so that the fragment reads of 8 consecutive
+//    rows hit distinct banks.  Addressing is branch-free: rows past M re-read
+//    the last row of A, rows past N and the ones row of the bias gradient
+//    read a 16-byte ones vector (results of rows past M or N are not
+//    stored), and vectors past K read a 16-byte zero vector.
+//  * gemm_nt_kernel, the general fallback (any alignment and K), staging
+//    through registers with element-wise edge handling.
 #include <type_traits>
 
 #include "device_util.h"
@@ -61,6 +74,60 @@ __device__ __forceinline__ uint4 ones_vec(int k, int K) {
     else v[e] = (k + e < K) ? 1.f : 0.f;
   }
   return *reinterpret_cast<const uint4*>(v);
+}
+
+// Store one wave's 64x64 accumulator tile (rows mw0.., columns nw0..): the
+// fp32 split-K partial, or C with the epilogue EPI.
+template <int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const f32x4 (&acc)[4][4], int z,
+                                              int split, int mw0, int nw0, int fr, int fq) {
+  const int M = p.M, N = p.N;
+  if (p.split_k > 1) {
+    float* part = p.partial + ((size_t)z * p.split_k + split) * (size_t)M * N;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int n = nw0 + nt * 16 + fr;
+        if (n >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mw0 + mt * 16 + fq * 4 + r;
+          if (m < M) part[(size_t)m * N + n] = acc[mt][nt][r];
+        }
+      }
+    return;
+  }
+  float* __restrict__ C = p.C[z];
+  float badd[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (EPI == EPI_BIAS) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = min(nw0 + nt * 16 + fr, N - 1);
+      float b = p.bias1 ? p.bias1[n] : 0.f;
+      if (p.bias2 && ((n % p.gh) / p.hh) != p.bias2_skip_gate) b += p.bias2[n];
+      badd[nt] = b;
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int n = nw0 + nt * 16 + fr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mw0 + mt * 16 + fq * 4 + r;
+        if (m >= M || n >= N) continue;
+        const float v = acc[mt][nt][r];
+        if constexpr (EPI == EPI_DW) {
+          if (n == p.n_ones) p.cbias[z][m] = v;
+          else C[(long long)m * p.ldc + n] = v;
+        } else {
+          C[(long long)m * p.ldc + n] = v + badd[nt];
+        }
+      }
+    }
+  }
 }
 
 template <bool BF16, int EPI>
@@ -158,50 +225,132 @@ __global__ __launch_bounds__(NTHR) void gemm_nt_kernel(const GemmParams p) {
     __syncthreads();
   }
 
-  // --- epilogue
-  if (nsplit > 1) {
-    // fp32 partial tile for the fixed-order reduction
-    float* part = p.partial + ((size_t)z * nsplit + split) * (size_t)M * N;
+  gemm_epilogue<EPI>(p, acc, z, split, m0 + wm, n0 + wn, fr, fq);
+}
+
+// --------------------------------------------------------------- fast path
+constexpr int kRowBytes = 128;                  // bytes of one tile row per K step
+constexpr int kStageBytes = BM * kRowBytes;     // one operand, one stage
+constexpr int kStages = 2;
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ uint4 lds_read16(const lds_char* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <bool BF16, int EPI>
+__global__ __launch_bounds__(NTHR) void gemm_lds_kernel(const GemmParams p) {
+  using T = typename Cfg<BF16>::T;
+  constexpr int BK = Cfg<BF16>::BK, EPV = Cfg<BF16>::EPV;
+  static_assert(BK * sizeof(T) == kRowBytes, "one K step is 128 bytes of a row");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStages * kStageBytes];
+  lds_char* const lds = (lds_char*)smem;
+
+  const int z = blockIdx.z;
+  const int M = p.M, N = p.N, K = p.K;
+  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const int nsplit = p.split_k;
+  const int total = tm * tn * nsplit;
+  const int bid = blockIdx.x;
+  const int per = (total + 7) / 8;
+  const int lin = (bid % 8) * per + bid / 8;
+  if (lin >= total) return;
+  const int split = lin % nsplit;
+  const int tile = lin / nsplit;
+  const int m0 = (tile / tn) * BM, n0 = (tile % tn) * BN;
+  const int kper = ((K + nsplit - 1) / nsplit + BK - 1) / BK * BK;
+  const int kbeg = split * kper, kend = min(K, kbeg + kper);
+  const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int fr = lane & 15, fq = lane >> 4;
+
+  // ---- loader: instruction j of wave w fills rows 8*(4j + w) .. +7 of a
+  // stage (64 lanes x 16 bytes); lane l takes row 8*(4j+w) + l/8, slot l%8,
+  // i.e. k-vector (l%8) ^ (row & 7)
+  const char* zero = reinterpret_cast<const char*>(p.zero16);
+  const char* ones = reinterpret_cast<const char*>(p.ones16);
+  const char* arow[4];
+  const char* brow[4];
+  int kvo[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int n = n0 + wn + nt * 16 + fr;
-        if (n >= N) continue;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm + mt * 16 + fq * 4 + r;
-          if (m < M) part[(size_t)m * N + n] = acc[mt][nt][r];
-        }
-      }
-    return;
+  for (int j = 0; j < 4; ++j) {
+    const int r = 8 * (4 * j + wave) + (lane >> 3);
+    kvo[j] = (((lane & 7) ^ (r & 7)) * EPV);
+    arow[j] = reinterpret_cast<const char*>(reinterpret_cast<const T*>(p.A[z]) +
+                                            (long long)min(m0 + r, M - 1) * p.lda);
+    // the ones row reads the ones vector, and so do rows past N (B may have
+    // no real row to re-read when its last row is the ones row)
+    const int n = n0 + r;
+    brow[j] = (n == p.n_ones || n >= N)
+                  ? nullptr
+                  : reinterpret_cast<const char*>(reinterpret_cast<const T*>(p.B[z]) + (long long)n * p.ldb);
   }
-  float* __restrict__ C = p.C[z];
+  auto issue = [&](int st, int k0) {
+    lds_char* sa = lds + st * kStageBytes;
+    lds_char* sb = lds + (kStages + st) * kStageBytes;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int n = n0 + wn + nt * 16 + fr;
-      if (n >= N) continue;
-      float badd = 0.f;
-      if constexpr (EPI == EPI_BIAS) {
-        badd = p.bias1 ? p.bias1[n] : 0.f;
-        if (p.bias2 && ((n % p.gh) / p.hh) != p.bias2_skip_gate) badd += p.bias2[n];
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm + mt * 16 + fq * 4 + r;
-        if (m >= M) continue;
-        const float v = acc[mt][nt][r];
-        if constexpr (EPI == EPI_DW) {
-          if (n == p.n_ones) p.cbias[z][m] = v;
-          else C[(long long)m * p.ldc + n] = v;
-        } else {
-          C[(long long)m * p.ldc + n] = v + badd;
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int k = k0 + kvo[j];
+      const bool kv = k < kend;
+      const char* ga = kv ? arow[j] + (size_t)k * sizeof(T) : zero;
+      const char* gb = kv ? (brow[j] ? brow[j] + (size_t)k * sizeof(T) : ones) : zero;
+      const int off = (4 * j + wave) * 1024;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)ga,
+                                       (void __attribute__((address_space(3)))*)(sa + off), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gb,
+                                       (void __attribute__((address_space(3)))*)(sb + off), 16, 0, 0);
     }
+  };
+
+  // fragment offsets: row r, k-vector v sits at r*128 + ((v ^ (r & 7)) * 16);
+  // for the rows a lane reads, r & 7 == fr & 7
+  constexpr int CH = BK * (int)sizeof(T) / 64;   // MFMA chunks (4 vectors) per step
+  int fo[CH];
+#pragma unroll
+  for (int ch = 0; ch < CH; ++ch) fo[ch] = fr * kRowBytes + (((ch * 4 + fq) ^ (fr & 7)) * 16);
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nk > 0) issue(0, kbeg);
+  if (nk > 1) issue(1, kbeg + BK);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    // this thread's loads of stage kt are complete once at most the next
+    // stage's 8 remain outstanding; the barrier extends that to all threads
+    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x3F70 | 8);   // vmcnt(8)
+    else __builtin_amdgcn_s_waitcnt(0x3F70);                   // vmcnt(0)
+    // a bare barrier: __syncthreads() would also wait for the next stage's
+    // loads (its fence drains every outstanding memory operation)
+    __builtin_amdgcn_s_barrier();
+    const lds_char* sa = lds + st * kStageBytes + wm * kRowBytes;
+    const lds_char* sb = lds + (kStages + st) * kStageBytes + wn * kRowBytes;
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch) {
+      uint4 af[4], bfr[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) af[t] = lds_read16(sa + t * 16 * kRowBytes + fo[ch]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bfr[t] = lds_read16(sb + t * 16 * kRowBytes + fo[ch]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_chunk<BF16>(af[mt], bfr[nt], acc[mt][nt]);
+    }
+    // every wave is done reading stage st before it is refilled
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < nk) issue(st, kbeg + (kt + 2) * BK);
   }
+  gemm_epilogue<EPI>(p, acc, z, split, m0 + wm, n0 + wn, fr, fq);
 }
 
 // Fixed-order sum of the split-K partials, then the dW epilogue.
@@ -222,7 +371,10 @@ template <bool BF16, int EPI>
 hipError_t launch_one(const GemmParams& p, int batches, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.split_k;
   const int grid = (tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_nt_kernel<BF16, EPI>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
+  const bool fast = p.a_vec && p.b_vec && p.zero16 && (p.n_ones < 0 || p.ones16) &&
+                    p.K % Cfg<BF16>::EPV == 0 && !p.force_general;
+  if (fast) hipLaunchKernelGGL((gemm_lds_kernel<BF16, EPI>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
+  else hipLaunchKernelGGL((gemm_nt_kernel<BF16, EPI>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.split_k <= 1) return e;
   size_t mn = (size_t)p.M * p.N;

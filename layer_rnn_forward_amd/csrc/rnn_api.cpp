@@ -423,6 +423,27 @@ rnn_status_t fill(rnn_desc* h, hipStream_t s, std::initializer_list<std::pair<vo
   return dev(rnn_launch_fill(ps.data(), ns.data(), vs.data(), (int)ps.size(), s));
 }
 
+// The 256-byte head of the workspace: the error word and zeros in [0, 128),
+// 16-byte constant vectors for the GEMMs after it: bf16 ones at 128, fp32
+// ones at 192.
+constexpr size_t kZero16 = 64, kOnesBf16 = 128, kOnesF32 = 192;
+rnn_status_t fill_head(rnn_desc* h, hipStream_t s, void* head) {
+  char* c = reinterpret_cast<char*>(head);
+  void* ptrs[3] = {c, c + kOnesBf16, c + kOnesF32};
+  size_t bytes[3] = {kOnesBf16, 64, 64};
+  uint32_t vals[3] = {0u, 0x3f803f80u, 0x3f800000u};
+  ProfScope ps_(h, s, K_FILL);
+  return dev(rnn_launch_fill(ptrs, bytes, vals, 3, s));
+}
+
+// Constant vectors and the kernel choice of a GEMM on this workspace.
+void gemm_consts(const rnn_desc* h, GemmParams& g, const void* ws, size_t off_head) {
+  const char* c = reinterpret_cast<const char*>(ws) + off_head;
+  g.zero16 = c + kZero16;
+  g.ones16 = c + (h->wtype == RNN_W_BF16 ? kOnesBf16 : kOnesF32);
+  g.force_general = env_int("RNN_GEMM_GENERAL", 0);
+}
+
 
 unsigned spin_limit() {
   const int v = env_int("RNN_SPIN_LIMIT", 1 << 20);
@@ -473,6 +494,7 @@ rnn_status_t gemm_input(rnn_desc* h, hipStream_t s, const Plan& p, int l, const 
   g.hh = h->H;
   g.split_k = 1;
   ProfScope ps(h, s, K_GEMM_IN);
+  gemm_consts(h, g, ws, p.off_err);
   return dev(rnn_launch_gemm(g, bf, EPI_BIAS, 1, s));
 }
 
@@ -497,7 +519,7 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
   if (h->seq_ws == ws) h->seq_stage = 0;
 
-  RNN_TRY(fill(h, s, {{at<void>(ws, p.off_err), 256}}));
+  RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err)));
   const size_t nstate = (size_t)h->L * h->D * B * h->H;
   if (T == 0 || B == 0) {
     if (hy) RNN_TRY(dev(rnn_copy_state(hy, h0, nstate, s)));
@@ -702,7 +724,7 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
   Plan p = make_plan(h, T, B, 1);
   if (p.status != RNN_STATUS_SUCCESS) return p.status;
   if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
-  RNN_TRY(fill(h, s, {{at<void>(ws, p.off_err), 256}}));
+  RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err)));
   const size_t nstate = (size_t)h->L * h->D * B * h->H;
   if (T == 0 || B == 0) {
     if (dh0) RNN_TRY(dev(rnn_copy_state(dh0, dhy, nstate, s)));
@@ -799,6 +821,7 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
     g.b_vec = 1;
     g.split_k = 1;
     ProfScope ps(h, s, K_GEMM_DX);
+    gemm_consts(h, g, ws, p.off_err);
     RNN_TRY(dev(rnn_launch_gemm(g, bf, EPI_STORE, 1, s)));
   }
   h->seq_stage = 2;
@@ -885,6 +908,7 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
       g.split_k = gemm_split(h, g.M, g.N, g.K, 1);
       g.partial = part;
       ProfScope ps(h, s, K_GEMM_DW);
+      gemm_consts(h, g, ws, p.off_err);
       RNN_TRY(dev(rnn_launch_gemm(g, bf, EPI_DW, 1, s)));
     }
     {  // dW_hh | db_hh = dG_h^T [H_prev | 1], per direction
@@ -906,6 +930,7 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
       g.split_k = gemm_split(h, g.M, g.N, g.K, h->D);
       g.partial = part;
       ProfScope ps(h, s, K_GEMM_DW);
+      gemm_consts(h, g, ws, p.off_err);
       RNN_TRY(dev(rnn_launch_gemm(g, bf, EPI_DW, h->D, s)));
     }
   }

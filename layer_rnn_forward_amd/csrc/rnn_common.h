@@ -50,6 +50,9 @@ struct GemmParams {
   int a_vec, b_vec;   // 1: 16-byte vector loads are legal (aligned bases and strides)
   int split_k;
   float* partial;
+  const void* zero16;  // 16 bytes of zeros (device), or null: general kernel only
+  const void* ones16;  // 16 bytes of ones in the compute type (device)
+  int force_general;   // 1: always use the general kernel
 };
 
 // Row-gather transpose: out[c * ld_out + r] = src_row(r)[c] for r < R, c < C,
