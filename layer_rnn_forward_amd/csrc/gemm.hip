@@ -21,7 +21,9 @@
 //  * gemm_lds_kernel, used whenever every operand row is 16-byte aligned and
 //    K is a whole number of 16-byte vectors: operands go straight from global
 //    memory into LDS (global_load_lds, no register staging) through a
-//    two-stage pipeline, in an XOR-swizzled layout (16-byte slot s of row r
+//    multi-stage pipeline (one barrier per K step; the loads of step k+NS-1
+//    are issued as soon as every wave has finished step k-1), tiles visited
+//    in groups of 8 tile rows for L2 reuse, in an XOR-swizzled layout (16-byte slot s of row r
 //    holds k-vector s ^ (r & 7)) so that the fragment reads of 8 consecutive
 //    rows hit distinct banks.  Addressing is branch-free: rows past M re-read
 //    the last row of A, rows past N and the ones row of the bias gradient
@@ -231,7 +233,6 @@ __global__ __launch_bounds__(NTHR) void gemm_nt_kernel(const GemmParams p) {
 // --------------------------------------------------------------- fast path
 constexpr int kRowBytes = 128;                  // bytes of one tile row per K step
 constexpr int kStageBytes = BM * kRowBytes;     // one operand, one stage
-constexpr int kStages = 2;
 
 typedef __attribute__((address_space(3))) char lds_char;
 
@@ -241,12 +242,16 @@ __device__ __forceinline__ uint4 lds_read16(const lds_char* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <bool BF16, int EPI>
+// NS: pipeline stages (LDS 32 KB each); GM: tiles are visited in groups of GM
+// tile rows, column by column inside a group, so that the workgroups running
+// at the same time on one XCD share few A and B row blocks (0: row-major).
+template <bool BF16, int EPI, int NS, int GM>
 __global__ __launch_bounds__(NTHR) void gemm_lds_kernel(const GemmParams p) {
   using T = typename Cfg<BF16>::T;
   constexpr int BK = Cfg<BF16>::BK, EPV = Cfg<BF16>::EPV;
+  constexpr int kStages = NS;
   static_assert(BK * sizeof(T) == kRowBytes, "one K step is 128 bytes of a row");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * kStageBytes];
   lds_char* const lds = (lds_char*)smem;
 
   const int z = blockIdx.z;
@@ -259,8 +264,15 @@ __global__ __launch_bounds__(NTHR) void gemm_lds_kernel(const GemmParams p) {
   const int lin = (bid % 8) * per + bid / 8;
   if (lin >= total) return;
   const int split = lin % nsplit;
-  const int tile = lin / nsplit;
-  const int m0 = (tile / tn) * BM, n0 = (tile % tn) * BN;
+  int tile = lin / nsplit;
+  int mi = tile / tn, ni = tile % tn;
+  if (GM > 0) {
+    const int g = tile / (GM * tn), in = tile - g * GM * tn;
+    const int gm = min(GM, tm - g * GM);
+    mi = g * GM + in % gm;
+    ni = in / gm;
+  }
+  const int m0 = mi * BM, n0 = ni * BN;
   const int kper = ((K + nsplit - 1) / nsplit + BK - 1) / BK * BK;
   const int kbeg = split * kper, kend = min(K, kbeg + kper);
   const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
@@ -320,17 +332,25 @@ __global__ __launch_bounds__(NTHR) void gemm_lds_kernel(const GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nk > 0) issue(0, kbeg);
-  if (nk > 1) issue(1, kbeg + BK);
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < nk) issue(i, kbeg + i * BK);
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    // this thread's loads of stage kt are complete once at most the next
-    // stage's 8 remain outstanding; the barrier extends that to all threads
-    if (kt + 1 < nk) __builtin_amdgcn_s_waitcnt(0x3F70 | 8);   // vmcnt(8)
-    else __builtin_amdgcn_s_waitcnt(0x3F70);                   // vmcnt(0)
-    // a bare barrier: __syncthreads() would also wait for the next stage's
-    // loads (its fence drains every outstanding memory operation)
+    const int st = kt % NS;
+    // this thread's loads of step kt are complete once only those of the
+    // steps issued after it (8 each) remain outstanding, and its LDS reads of
+    // step kt-1 once lgkmcnt is 0; the barrier extends both to all threads.
+    // A bare barrier: __syncthreads() would also wait for the later steps'
+    // loads (its fence drains every memory operation).
+    const int ahead = min(nk - 1 - kt, NS - 2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (NS >= 4 && ahead >= 2) __builtin_amdgcn_s_waitcnt(0x3070 | 16);   // vmcnt(16) lgkmcnt(0)
+    else if (NS >= 3 && ahead == 1) __builtin_amdgcn_s_waitcnt(0x3070 | 8);
+    else __builtin_amdgcn_s_waitcnt(0x3070);                              // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // every wave has finished step kt-1, so its buffer can be refilled
+    if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kbeg + (kt + NS - 1) * BK);
     const lds_char* sa = lds + st * kStageBytes + wm * kRowBytes;
     const lds_char* sb = lds + (kStages + st) * kStageBytes + wn * kRowBytes;
 #pragma unroll
@@ -345,10 +365,6 @@ __global__ __launch_bounds__(NTHR) void gemm_lds_kernel(const GemmParams p) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_chunk<BF16>(af[mt], bfr[nt], acc[mt][nt]);
     }
-    // every wave is done reading stage st before it is refilled
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    if (kt + 2 < nk) issue(st, kbeg + (kt + 2) * BK);
   }
   gemm_epilogue<EPI>(p, acc, z, split, m0 + wm, n0 + wn, fr, fq);
 }
@@ -373,7 +389,9 @@ hipError_t launch_one(const GemmParams& p, int batches, hipStream_t s) {
   const int grid = (tiles + 7) / 8 * 8;
   const bool fast = p.a_vec && p.b_vec && p.zero16 && (p.n_ones < 0 || p.ones16) &&
                     p.K % Cfg<BF16>::EPV == 0 && !p.force_general;
-  if (fast) hipLaunchKernelGGL((gemm_lds_kernel<BF16, EPI>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
+  // two stages (64 KB of LDS, two workgroups per CU) measured faster than
+  // three or four with one workgroup per CU; groups of 8 tile rows
+  if (fast) hipLaunchKernelGGL((gemm_lds_kernel<BF16, EPI, 2, 8>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
   else hipLaunchKernelGGL((gemm_nt_kernel<BF16, EPI>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.split_k <= 1) return e;

@@ -15,9 +15,10 @@
 //      slice on MFMA (K split across the waves, partial tiles summed through
 //      LDS in a fixed order),
 //   3. applies the cell equations to its units in the same kernel (fused
-//      point-wise step of the optimisation table), writes the next h into the
-//      exchange ring, then y and the training reserve,
-//   4. publishes its flag.
+//      point-wise step of the optimisation table) and writes the next h into
+//      the exchange ring,
+//   4. publishes its flag, then writes y and the training reserve (read only
+//      by later kernels, so off the critical path).
 // Backward: the same structure walks time in reverse; each workgroup owns U
 // units, exchanges the recurrent gate gradients dG_h, computes
 // dh = dG_h W_hh for its units on MFMA (each wave first copies its part of
@@ -119,6 +120,14 @@ __device__ bool wave_wait(const unsigned* flags, unsigned* err, unsigned spin_li
     if ((it & 31u) == 0 && flag_load(err) != 0u) return false;
     __builtin_amdgcn_s_sleep(1);
   }
+}
+
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
+// does not wait for the wave's outstanding global loads and stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Every wave waits for completion of its stores (the ring stores are agent
@@ -311,6 +320,29 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   }
   __syncthreads();
 
+  // biases that stay in the pre-activations over all steps: the input
+  // projection's when it is computed here (wavefront layers above the first),
+  // and GRU's b_hn otherwise
+  float bconst[4] = {0.f, 0.f, 0.f, 0.f};
+  float bhn = 0.f;
+  if (qv) {
+    const float* bi = p.b_ih[li] + (size_t)d * GH + qu;
+    const float* bh = p.b_hh[li] + (size_t)d * GH + qu;
+    if (inproj) {
+      if (MODE == MODE_GRU) {
+        bconst[0] = bi[0] + bh[0];
+        bconst[1] = bi[H] + bh[H];
+        bconst[2] = bi[2 * H];   // b_in (x part of n)
+        bconst[3] = bh[2 * H];   // b_hn (h part of n)
+      } else {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) bconst[gi] = bi[(size_t)gi * H] + bh[(size_t)gi * H];
+      }
+    } else if (MODE == MODE_GRU) {
+      bhn = bh[2 * H];
+    }
+  }
+
   const size_t ystride_t = (size_t)B * D * H;
   for (int s = max(p.s_begin, 0); s < p.s_end; ++s) {
     const int t_rel = p.wavefront ? s - li : s;
@@ -321,29 +353,14 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
       continue;
     }
 
-    // input part of the pre-activations (independent of other workgroups)
-    float gxv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (qv) {
-      if (!inproj) {
-        const float* g = p.gx + ((size_t)t * B + qbg) * D * GH + (size_t)d * GH + qu;
+    // input part of the pre-activations (independent of other workgroups):
+    // issued now, first used in the epilogue, so its latency overlaps the wait
+    float gxl[4] = {0.f, 0.f, 0.f, 0.f};
+    if (qv && !inproj) {
+      const float* g = p.gx + ((size_t)t * B + qbg) * D * GH + (size_t)d * GH + qu;
 #pragma unroll
-        for (int gi = 0; gi < G; ++gi) gxv[gi] = g[(size_t)gi * H];
-      } else {
-        const float* bi = p.b_ih[li] + (size_t)d * GH + qu;
-        const float* bh = p.b_hh[li] + (size_t)d * GH + qu;
-        if (MODE == MODE_GRU) {
-          gxv[0] = bi[0] + bh[0];
-          gxv[1] = bi[H] + bh[H];
-          gxv[2] = bi[2 * H];   // b_in (x part of n)
-          gxv[3] = bh[2 * H];   // b_hn (h part of n)
-        } else {
-#pragma unroll
-          for (int gi = 0; gi < G; ++gi) gxv[gi] = bi[(size_t)gi * H] + bh[(size_t)gi * H];
-        }
-      }
+      for (int gi = 0; gi < G; ++gi) gxl[gi] = g[(size_t)gi * H];
     }
-    float bhn = 0.f;
-    if (MODE == MODE_GRU && !inproj && qv) bhn = p.b_hh[li][(size_t)d * GH + 2 * H + qu];
 
     // each wave waits only for the producers of its own granules
     f32x4 acc[MT][NT];
@@ -380,12 +397,15 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[wave][mt * 16 + fq * 4 + r][nt * 16 + fr] = acc[mt][nt][r];
-    __syncthreads();
+    lds_barrier();
     if (s_fail) return;   // every wave leaves after the same barrier
 
     float hnew = 0.f;
     float rv[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
     if (qv) {
+      float gxv[4];
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) gxv[gi] = inproj ? bconst[gi] : gxl[gi];
       float pre[4];
 #pragma unroll
       for (int gb = 0; gb < 4; ++gb) {
@@ -420,8 +440,10 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
       }
       sh_h[qb * NCOL + qj] = hnew;
     }
-    // the exchange store first: it is what the other workgroups wait for
+    // only the exchange store precedes the flag; y and the reserve are read
+    // by later kernels, so they are written after it, off the critical path
     if (qw) ring_store<BF16>(ring + (size_t)(s + 1) * p.ring_step, my_off, hnew);
+    if (p.persistent) publish(p.flags, (unsigned)(s + 2));
     if (qv) {
       p.y[li][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = hnew;
       if (p.training && R > 0) {
@@ -430,8 +452,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         for (int r = 0; r < R; ++r) res[(size_t)r * H] = rv[r];
       }
     }
-    if (p.persistent) publish(p.flags, (unsigned)(s + 2));
-    __syncthreads();   // red and sh_* are reused by the next step
+    lds_barrier();   // red and sh_* are reused by the next step
   }
 
   if (qv) {
@@ -597,7 +618,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) red[wave][mt * 16 + fq * 4 + r][nt * 16 + fr] = acc[mt][nt][r];
-      __syncthreads();
+      lds_barrier();
       if (s_fail) return;   // every wave leaves after the same barrier
       if (qv) {
 #pragma unroll
@@ -605,13 +626,13 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
       }
     }
 
+    float dgi[4] = {0.f, 0.f, 0.f, 0.f}, dgh[4] = {0.f, 0.f, 0.f, 0.f};
     if (final_phase) {
       if (qv) {
         if (p.dh0) p.dh0[sidx] = dhrec + sh_dh[qb * NCOL + qj];
         if (MODE == MODE_LSTM && p.dc0) p.dc0[sidx] = sh_dc[qb * NCOL + qj];
       }
     } else {
-      float dgi[4] = {0.f, 0.f, 0.f, 0.f}, dgh[4] = {0.f, 0.f, 0.f, 0.f};
       if (qv) {
         const float dh = dhrec + dyv + sh_dh[qb * NCOL + qj];
         float ncarry = 0.f;
@@ -645,30 +666,30 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
         }
         sh_dh[qb * NCOL + qj] = ncarry;
       }
-      // the exchange stores first: they are what the other workgroups wait for
+      // only the exchange stores precede the flag
       if (qw) {
         char* en = ring + (size_t)(s + 1) * p.ring_step;
 #pragma unroll
         for (int g = 0; g < G; ++g) ring_store<BF16>(en, my_off + (size_t)g * UJ * gran, dgh[g]);
       }
-      if (qv) {
-        // gate gradients for the dX product ([T*B, D*G*H]) and, transposed
-        // ([D*G*H, T*B]), for the weight-gradient products
-        using X = XT<BF16>;
-        const size_t rowi = (size_t)t * B + qbg;
-        const size_t col0 = (size_t)d * GH + qu;
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const size_t col = col0 + (size_t)g * H;
-          const X vi = to_x<BF16>(dgi[g]);
-          reinterpret_cast<X*>(p.dg)[rowi * p.dg_ld + col] = vi;
-          reinterpret_cast<X*>(p.dgT)[col * p.tb_ld + rowi] = vi;
-          if (MODE == MODE_GRU) reinterpret_cast<X*>(p.dghT)[col * p.tb_ld + rowi] = to_x<BF16>(dgh[g]);
-        }
-      }
     }
     if (p.persistent && !final_phase) publish(p.flags, (unsigned)(s + 1));
-    __syncthreads();   // red and sh_* are reused by the next step
+    if (!final_phase && qv) {
+      // gate gradients for the dX product ([T*B, D*G*H]) and, transposed
+      // ([D*G*H, T*B]), for the weight-gradient products (later kernels)
+      using X = XT<BF16>;
+      const size_t rowi = (size_t)t * B + qbg;
+      const size_t col0 = (size_t)d * GH + qu;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const size_t col = col0 + (size_t)g * H;
+        const X vi = to_x<BF16>(dgi[g]);
+        reinterpret_cast<X*>(p.dg)[rowi * p.dg_ld + col] = vi;
+        reinterpret_cast<X*>(p.dgT)[col * p.tb_ld + rowi] = vi;
+        if (MODE == MODE_GRU) reinterpret_cast<X*>(p.dghT)[col * p.tb_ld + rowi] = to_x<BF16>(dgh[g]);
+      }
+    }
+    lds_barrier();   // red and sh_* are reused by the next step
   }
   if (qv && p.s_end <= T) {
     p.st_dh[sidx] = sh_dh[qb * NCOL + qj];
