@@ -390,8 +390,12 @@ hipError_t launch_one(const GemmParams& p, int batches, hipStream_t s) {
   const bool fast = p.a_vec && p.b_vec && p.zero16 && (p.n_ones < 0 || p.ones16) &&
                     p.K % Cfg<BF16>::EPV == 0 && !p.force_general;
   // two stages (64 KB of LDS, two workgroups per CU) measured faster than
-  // three or four with one workgroup per CU; groups of 8 tile rows
-  if (fast) hipLaunchKernelGGL((gemm_lds_kernel<BF16, EPI, 2, 8>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
+  // three or four with one workgroup per CU; groups of 8 tile rows helped the
+  // single-pass products and not the split-K weight gradients
+  if (fast && p.split_k == 1)
+    hipLaunchKernelGGL((gemm_lds_kernel<BF16, EPI, 2, 8>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
+  else if (fast)
+    hipLaunchKernelGGL((gemm_lds_kernel<BF16, EPI, 2, 0>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
   else hipLaunchKernelGGL((gemm_nt_kernel<BF16, EPI>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.split_k <= 1) return e;
