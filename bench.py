@@ -196,6 +196,25 @@ def main():
     R.rnn_set_profiling(run.h, False)
     assert R.rnn_device_status(run.h, run.ws) == 0
 
+    # latency floor of the recurrence: the forward sweep's launch with only
+    # its exchange (flag waits, ring stores, flags), no arithmetic
+    exchange = None
+    try:
+        R.rnn_set_profiling(run.h, True)
+        for _ in range(max(3, args.steps // 4)):
+            R.rnn_exchange_floor(run.h, w.T, w.B, run.ws_inf)
+        n_p, ms_p = R.rnn_profile_read(run.h, R.KERNEL_NAMES.index("exchange_probe"))
+        R.rnn_set_profiling(run.h, False)
+        assert R.rnn_device_status(run.h, run.ws_inf) == 0
+        steps_per_sweep = w.T + (w.layers - 1 if w.dirs == 1 and w.layers > 1 else 0)
+        floor = 1000.0 * ms_p / n_p / steps_per_sweep
+        fwd_step = kern["recurrent_fwd"]["avg_us"] / steps_per_sweep
+        exchange = {"floor_us_per_step": round(floor, 3), "recurrent_fwd_us_per_step": round(fwd_step, 3),
+                    "floor_fraction_of_step": round(floor / fwd_step, 4)}
+    except R.RNNError as e:   # the sweep could not run persistently
+        R.rnn_set_profiling(run.h, False)
+        exchange = {"error": str(e)}
+
     T_ms = float(np.mean(step_ms))
     value = F_train / (T_ms * 1e-3) / 1e9
     peak = PEAK_TFLOPS[w.wtype]
@@ -242,6 +261,7 @@ def main():
         "train_step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
         "kernels": kern,
         "roofline": roof,
+        "exchange_floor": exchange,
     }
     if not args.no_fp32 and w.wtype == "bf16":
         w32 = synth.WORKLOADS.get(args.workload.replace("bf16", "f32"))

@@ -168,6 +168,19 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
                                   const float* h0, const float* y, const void* ws,
                                   size_t ws_bytes, float* dW);
 
+/* Diagnostic: the latency floor of the persistent forward sweep.  Runs the
+ * launch rnn_forward_inference would use for its first recurrent sweep (same
+ * grid, same per-step waits on the producers' flags, same exchange-ring
+ * stores and flag publication: the step-wise grid synchronisation of the
+ * persistent-RNN design discussed in the TVM thread "Persist RNN
+ * Implementation") with no weights, arithmetic or outputs, so that its time
+ * divided by the steps is the cost of the exchange alone.  Writes only the
+ * workspace (at least rnn_workspace_size(h, T, B, 0) bytes); invalidates a
+ * pending training sequence on it.  Timed like the other launches by
+ * rnn_set_profiling (kernel id 7).  Errors: as rnn_forward_inference, and
+ * NOT_CORESIDENT when the sweep could not run persistently. */
+rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, void* ws, size_t ws_bytes);
+
 /* Synchronise `stream` and report whether a kernel that used `ws` hit an
  * expired bounded wait since the workspace was last handed to a compute
  * call: RNN_STATUS_SUCCESS or RNN_STATUS_DEVICE_TIMEOUT (or DEVICE if the
@@ -178,7 +191,8 @@ rnn_status_t rnn_device_status(rnn_handle_t h, void* stream, const void* ws, siz
  * every launch (off by default; adds one event pair per launch).  Kernel ids:
  * 0 input-projection GEMM, 1 recurrent forward sweep, 2 recurrent backward
  * sweep, 3 dX GEMM, 4 dW GEMMs, 5 workspace fill, 6 operand preparation
- * (bf16 conversion and transposes for the GEMMs).  rnn_profile_read
+ * (bf16 conversion and transposes for the GEMMs), 7 exchange probe
+ * (rnn_exchange_floor).  rnn_profile_read
  * synchronises, accumulates the elapsed times of finished launches and
  * returns the launch count and total milliseconds for `kernel` since the last
  * reset (rnn_set_profiling(h, 1) resets). */

@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     rnn_forward_inference,
     rnn_forward_training,
     rnn_backward_data,
+    rnn_exchange_floor,
     rnn_backward_weights,
     rnn_device_status,
     rnn_set_profiling,

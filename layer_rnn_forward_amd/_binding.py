@@ -11,7 +11,8 @@ import torch
 MODES = {"rnn_tanh": 0, "lstm": 1, "gru": 2}
 WTYPES = {"f32": 0, "bf16": 1}
 SCHED_AUTO, SCHED_PERSISTENT, SCHED_STEPPED = 0, 1, 2
-KERNEL_NAMES = ["gemm_input", "recurrent_fwd", "recurrent_bwd", "gemm_dx", "gemm_dw", "fill", "prep"]
+KERNEL_NAMES = ["gemm_input", "recurrent_fwd", "recurrent_bwd", "gemm_dx", "gemm_dw", "fill", "prep",
+                "exchange_probe"]
 STATUS_DEVICE_TIMEOUT = -7
 
 _LIB = None
@@ -52,6 +53,7 @@ def load_library():
         "rnn_backward_data": [vp, vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz],
         "rnn_backward_weights": [vp, vp, i, i, vp, vp, vp, vp, sz, vp],
         "rnn_device_status": [vp, vp, vp, sz],
+        "rnn_exchange_floor": [vp, vp, i, i, vp, sz],
         "rnn_set_profiling": [vp, i],
         "rnn_profile_read": [vp, i, ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_double)],
     }
@@ -187,6 +189,12 @@ def rnn_device_status(h, ws) -> int:
     if s not in (0, STATUS_DEVICE_TIMEOUT):
         raise RNNError(s, "rnn_device_status")
     return s
+
+
+def rnn_exchange_floor(h, T, B, ws):
+    """Run the forward sweep's exchange alone (same launch, no arithmetic)."""
+    _check(load_library().rnn_exchange_floor(h.ptr, _stream(), T, B, _ptr(ws, "ws", None), _nbytes(ws)),
+           "rnn_exchange_floor")
 
 
 def rnn_set_profiling(h, enable: bool):

@@ -256,6 +256,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
 
   // ---- weight slice -> registers (B operand fragments)
   uint4 wf[KPW][NT];
+  const bool live = !p.probe;   // the exchange probe skips every use of weights and outputs
 #pragma unroll
   for (int kk = 0; kk < KPW; ++kk) {
     const int gl = kk * 4 + fq;
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
       for (int e = 0; e < PER; ++e) v[e] = 0u;
       const int n = nt * 16 + fr;
       const int gb = n / U, j = n - gb * U;
-      if (gl < nmine && gb < GB && j < Uact) {
+      if (live && gl < nmine && gb < GB && j < Uact) {
         int gate = gb;
         bool use_x = true, use_h = true;
         if (MODE == MODE_GRU && inproj) {
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   if (tid == 0) s_fail = 0;
   if (p.s_begin < 0) {
     float hv = 0.f, cv = 0.f;
-    if (qv) {
+    if (qv && live) {
       hv = p.h0 ? p.h0[hx_idx] : 0.f;
       cv = (MODE == MODE_LSTM && p.c0) ? p.c0[hx_idx] : 0.f;
       sh_h[qb * NCOL + qj] = hv;
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     const int first = p.wavefront ? li : 0;
     if (qw) ring_store<BF16>(ring + (size_t)first * p.ring_step, my_off, hv);
     if (p.persistent) publish(p.flags, 1u);
-  } else if (qv) {
+  } else if (qv && live) {
     sh_h[qb * NCOL + qj] = p.st_h[st_idx];
     if (MODE == MODE_LSTM) sh_c[qb * NCOL + qj] = p.st_c[st_idx];
   }
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   // and GRU's b_hn otherwise
   float bconst[4] = {0.f, 0.f, 0.f, 0.f};
   float bhn = 0.f;
-  if (qv) {
+  if (qv && live) {
     const float* bi = p.b_ih[li] + (size_t)d * GH + qu;
     const float* bh = p.b_hh[li] + (size_t)d * GH + qu;
     if (inproj) {
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     // input part of the pre-activations (independent of other workgroups):
     // issued now, first used in the epilogue, so its latency overlaps the wait
     float gxl[4] = {0.f, 0.f, 0.f, 0.f};
-    if (qv && !inproj) {
+    if (qv && live && !inproj) {
       const float* g = p.gx + ((size_t)t * B + qbg) * D * GH + (size_t)d * GH + qu;
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) gxl[gi] = g[(size_t)gi * H];
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         ok = wave_wait(p.flags, p.err, p.spin_limit, xflag0, xn, hflag0, hn, (unsigned)(s + 1));
       }
     }
-    if (ok) {
+    if (ok && live) {
       const char* eh = ring + (size_t)s * p.ring_step;
       const char* ex = ring_below + (size_t)s * p.ring_step;
       mfma_sweep<BF16, NT, MT, KPW>(acc, wf, fr, fq, nmine, rmax, [&](int gl, int row) -> uint4 {
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (lane == 0) s_fail = 1;
+      if (!ok && lane == 0) s_fail = 1;
     }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -402,7 +403,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
 
     float hnew = 0.f;
     float rv[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-    if (qv) {
+    if (qv && live) {
       float gxv[4];
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) gxv[gi] = inproj ? bconst[gi] : gxl[gi];
@@ -444,7 +445,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     // by later kernels, so they are written after it, off the critical path
     if (qw) ring_store<BF16>(ring + (size_t)(s + 1) * p.ring_step, my_off, hnew);
     if (p.persistent) publish(p.flags, (unsigned)(s + 2));
-    if (qv) {
+    if (qv && live) {
       p.y[li][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = hnew;
       if (p.training && R > 0) {
         float* res = p.reserve[li] + (((size_t)d * T + t) * B + qbg) * R * H + qu;
@@ -455,7 +456,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     lds_barrier();   // red and sh_* are reused by the next step
   }
 
-  if (qv) {
+  if (qv && live) {
     if (p.s_end >= p.s_total) {
       if (p.hy) p.hy[hx_idx] = sh_h[qb * NCOL + qj];
       if (MODE == MODE_LSTM && p.cy) p.cy[hx_idx] = sh_c[qb * NCOL + qj];

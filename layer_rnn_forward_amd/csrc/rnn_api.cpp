@@ -32,7 +32,8 @@ int env_int(const char* name, int dflt) {
   return std::atoi(v);
 }
 
-enum KernelId { K_GEMM_IN = 0, K_FWD = 1, K_BWD = 2, K_GEMM_DX = 3, K_GEMM_DW = 4, K_FILL = 5, K_PREP = 6, K_NKERNELS = 7 };
+enum KernelId { K_GEMM_IN = 0, K_FWD = 1, K_BWD = 2, K_GEMM_DX = 3, K_GEMM_DW = 4, K_FILL = 5, K_PREP = 6,
+                K_PROBE = 7, K_NKERNELS = 8 };
 
 struct ProfPending {
   hipEvent_t a, b;
@@ -139,6 +140,8 @@ bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepP
   for (int tryU = U; tryU >= Q; tryU -= Q) {
     const int nwg = ceil_div(h->H, tryU);
     const int ngr = (inproj ? 2 : 1) * nwg * (tryU / Q);   // K granules
+    // (measured: four waves with two load batches beat eight waves with one
+    // for the fp32 DS2 forward, so the list order, fewer waves first, stands)
     for (const RecConfig& c : kFwdCfgs) {
       if (c.mt != mt) continue;
       if (GB * tryU > 16 * c.nt || Bc * tryU > 64 * c.nwaves) continue;
@@ -626,6 +629,50 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   return RNN_STATUS_SUCCESS;
 }
 
+// The forward sweep's launch with only its exchange: the same grid, waits,
+// ring stores and flags, no weights, arithmetic or outputs.
+rnn_status_t exchange_probe_impl(rnn_desc* h, void* stream, int T, int B, void* ws, size_t ws_bytes) {
+  RNN_TRY(check_common(h, T, B, ws, ws_bytes));
+  if (!ws) return RNN_STATUS_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  Plan p = make_plan(h, T, B, 0);
+  if (p.status != RNN_STATUS_SUCCESS) return p.status;
+  if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
+  if (!p.fwd.persistent) return RNN_STATUS_NOT_CORESIDENT;
+  if (h->seq_ws == ws) h->seq_stage = 0;
+  RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err)));
+  if (T == 0 || B == 0) return RNN_STATUS_SUCCESS;
+  FwdParams f{};
+  f.T = T;
+  f.B = B;
+  f.H = h->H;
+  f.D = h->D;
+  f.nchunk = p.fwd.nchunk;
+  f.Bc = p.fwd.Bc;
+  f.U = p.fwd.U;
+  f.nwg = p.fwd.nwg;
+  f.slice = p.fslice;
+  f.gran = p.fgran;
+  f.ring_step = (long long)p.fring_step;
+  f.ring_group = (long long)p.fring_group;
+  f.persistent = 1;
+  f.probe = 1;
+  f.wavefront = p.wavefront ? 1 : 0;
+  f.nlayers = p.wavefront ? h->L : 1;
+  f.s_total = T + f.nlayers - 1;
+  f.s_begin = -1;
+  f.s_end = f.s_total;
+  for (int l = 0; l < f.nlayers; ++l) f.in_l[l] = in_width(h, l);
+  f.xch = at<void>(ws, p.off_xch);
+  f.flags = at<unsigned>(ws, p.off_flags);
+  f.err = at<unsigned>(ws, p.off_err);
+  f.spin_limit = spin_limit();
+  const int grid = p.fwd.nwg * f.nlayers * h->D * p.fwd.nchunk;
+  RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
+  ProfScope ps(h, s, K_PROBE);
+  return dev(rnn_launch_fwd(f, h->mode, h->wtype == RNN_W_BF16, p.fwd.cfg, grid, p.fwd.lds, s));
+}
+
 }  // namespace
 
 // ================================================================== C ABI
@@ -935,6 +982,10 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
     }
   }
   return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, void* ws, size_t ws_bytes) {
+  return exchange_probe_impl(h, stream, T, B, ws, ws_bytes);
 }
 
 rnn_status_t rnn_device_status(rnn_handle_t h, void* stream, const void* ws, size_t ws_bytes) {

@@ -89,6 +89,7 @@ struct FwdParams {
   int s_begin, s_end;     // global steps [s_begin, s_end); -1 is the prologue
   int s_total;            // T + nlayers - 1
   int persistent, training, wavefront;
+  int probe;              // 1: exchange only (waits, ring stores, flags); no weights, math or outputs
   int first_layer;        // index of layer 0 of this launch in the network
   const void* w_ih[kMaxLayersPerLaunch];   // layer block [D*G*H, I_l]
   const void* w_hh[kMaxLayersPerLaunch];   // layer block [D*G*H, H]

@@ -216,3 +216,33 @@ def test_forced_wait_timeout_is_reported():
                        timeout=120, cwd=str(__import__("pathlib").Path(__file__).parents[1]))
     assert r.returncode == 0, r.stderr
     assert "STATUS -7" in r.stdout or "STATUS 0" in r.stdout, r.stdout
+
+
+@pytest.mark.parametrize("mode,L,D,wtype", [("lstm", 1, 1, "bf16"), ("gru", 1, 2, "f32"),
+                                            ("rnn_tanh", 3, 1, "bf16"), ("lstm", 2, 2, "f32")])
+def test_exchange_floor_probe(mode, L, D, wtype):
+    """rnn_exchange_floor runs the forward sweep's launch with its exchange
+    only: it completes without a device timeout, touches nothing but the
+    workspace, and a forward pass on the same workspace afterwards gives
+    bitwise the same outputs as before it."""
+    T, B, I, H = 12, 6, 24, 40
+    _announce("exchange_floor", mode, L, D, wtype)
+    case = _case(mode, L, D, T, B, I, H, wtype, seed=21)
+    h = R.rnn_create(mode, L, D, I, H, wtype)
+    W = R.pack_weights(h, case["params"])
+    need = R.rnn_workspace_size(h, T, B, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    x = torch.as_tensor(case["x"], dtype=torch.float64).float().cuda()
+    y1 = torch.zeros((T, B, D * H), device="cuda")
+    y2 = torch.full((T, B, D * H), 7.0, device="cuda")
+    R.rnn_forward_inference(h, T, B, x, None, None, W, y1, None, None, ws)
+    R.rnn_exchange_floor(h, T, B, ws)
+    assert R.rnn_device_status(h, ws) == 0
+    R.rnn_forward_inference(h, T, B, x, None, None, W, y2, None, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(R.RNNError) as e:
+        R.rnn_exchange_floor(h, T, B, small)
+    assert e.value.status == -3
+    R.rnn_destroy(h)
