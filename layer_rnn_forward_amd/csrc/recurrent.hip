@@ -145,11 +145,11 @@ __device__ __forceinline__ void publish(unsigned* flags, unsigned v) {
 // granule (their weights are zero), and tile rows past the granule's padded
 // rows re-read its last row: no load leaves the granules the wave has waited
 // for, and such rows only feed output rows that are never used.  All loads of
-// a batch are issued before its MFMAs.
-template <bool BF16, int NT, int MT, int KPW, class LoadF>
+// a batch (at most KBMAX chunks) are issued before its MFMAs.
+template <bool BF16, int NT, int MT, int KPW, int KBMAX = 8, class LoadF>
 __device__ __forceinline__ void mfma_sweep(f32x4 (&acc)[MT][NT], const uint4 (&wf)[KPW][NT], int fr,
                                            int fq, int nmine, int rmax, LoadF load) {
-  constexpr int KB = KPW < 8 ? KPW : 8;
+  constexpr int KB = KPW < KBMAX ? KPW : KBMAX;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -380,8 +380,14 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     if (ok && live) {
       const char* eh = ring + (size_t)s * p.ring_step;
       const char* ex = ring_below + (size_t)s * p.ring_step;
-      mfma_sweep<BF16, NT, MT, KPW>(acc, wf, fr, fq, nmine, rmax, [&](int gl, int row) -> uint4 {
-        const int gg = g0 + gl;
+      // the fragment offsets are recomputed every step (a few VALU
+      // operations) instead of being held in registers across the sweep
+      int g0s = g0;
+      asm volatile("" : "+v"(g0s));
+      // eight waves share the register file two per SIMD: smaller batches
+      constexpr int KBD = NW >= 8 ? 4 : 8;
+      mfma_sweep<BF16, NT, MT, KPW, KBD>(acc, wf, fr, fq, nmine, rmax, [&](int gl, int row) -> uint4 {
+        const int gg = g0s + gl;
         const bool xpart = gg < xoff;
         return *reinterpret_cast<const uint4*>((xpart ? ex : eh) + (xpart ? gg : gg - xoff) * gran + row * 16);
       });
@@ -601,10 +607,14 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
       }
       if (ok && p.stage) {
         stage_granules(lds, e, g0, nmine, gran, lane);
-        mfma_sweep<BF16, NT, MT, KPW>(acc, wf, fr, fq, nmine, rmax,
+        // (batches of 32 LDS fragments measured no faster than 8, and 8 keep
+        // the register count low enough for two workgroups per CU)
+        constexpr int KBL = NW >= 8 ? 4 : 8;
+        mfma_sweep<BF16, NT, MT, KPW, KBL>(acc, wf, fr, fq, nmine, rmax,
             [&](int gl, int row) -> uint4 { return lds_load16(lds + (g0 + gl) * gran + row * 16); });
       } else if (ok) {
-        mfma_sweep<BF16, NT, MT, KPW>(acc, wf, fr, fq, nmine, rmax,
+        constexpr int KBD = NW >= 8 ? 4 : 8;
+        mfma_sweep<BF16, NT, MT, KPW, KBD>(acc, wf, fr, fq, nmine, rmax,
             [&](int gl, int row) -> uint4 { return *reinterpret_cast<const uint4*>(e + (g0 + gl) * gran + row * 16); });
       } else {
 #pragma unroll
@@ -757,6 +767,8 @@ struct BwdK {
   X(M, BF, 2, 2, 8, 4)            \
   X(M, BF, 2, 1, 16, 4)           \
   X(M, BF, 2, 2, 16, 4)           \
+  X(M, BF, 4, 1, 4, 8)            \
+  X(M, BF, 4, 2, 4, 8)            \
   X(M, BF, 4, 1, 8, 8)            \
   X(M, BF, 4, 2, 8, 8)            \
   X(M, BF, 1, 2, 32, 4)           \

@@ -115,7 +115,8 @@ void layout_weights(rnn_desc* h) {
 
 // Candidate kernel configurations, in order of preference.
 const RecConfig kFwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 1, 16, 4}, {1, 2, 16, 4}, {2, 1, 8, 4},
-                              {2, 2, 8, 4},  {2, 1, 16, 4}, {2, 2, 16, 4}, {4, 1, 8, 8},  {4, 2, 8, 8},
+                              {2, 2, 8, 4},  {2, 1, 16, 4}, {2, 2, 16, 4}, {4, 1, 4, 8},  {4, 2, 4, 8},
+                              {4, 1, 8, 8},  {4, 2, 8, 8},
                               {1, 2, 32, 4}, {1, 2, 16, 8}, {2, 2, 16, 8}, {4, 2, 16, 8}};
 const RecConfig kBwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 1, 16, 4}, {1, 2, 16, 4},
                               {1, 1, 32, 4}, {1, 2, 32, 4}, {1, 1, 64, 4}, {1, 2, 64, 4},
@@ -132,7 +133,7 @@ int unit_quantum(const rnn_desc* h) { return h->wtype == RNN_W_BF16 ? 8 : 4; }
 bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepPlan* sp) {
   const int Q = unit_quantum(h);
   const int GB = (h->mode == RNN_GRU && inproj) ? 4 : h->G;
-  const int target_wgs = std::max(1, env_int("RNN_FWD_TARGET_WGS", 128));
+  const int target_wgs = std::max(1, env_int("RNN_FWD_TARGET_WGS", 256));
   int U = ceil_div(ceil_div(h->H * std::max(1, groups), target_wgs), Q) * Q;
   const int Uenv = env_int("RNN_FWD_UNITS", 0);
   if (Uenv > 0) U = ceil_div(Uenv, Q) * Q;
@@ -159,7 +160,7 @@ bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepP
 
 bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, SweepPlan* sp) {
   const int Q = unit_quantum(h);
-  int U = ceil_div(std::max(1, env_int("RNN_BWD_UNITS", 8)), Q) * Q;
+  int U = ceil_div(std::max(1, env_int("RNN_BWD_UNITS", 16)), Q) * Q;
   U = std::max(Q, std::min(U, ceil_div(h->H, Q) * Q));
   for (int tryU = U; tryU >= Q; tryU -= Q) {
     const int nwg = ceil_div(h->H, tryU);
