@@ -46,6 +46,17 @@ the input of layer ``l > 0`` is ``y_{l-1}``, the concatenation
 ``d = 0`` and ``h_0`` for ``d = 1`` (shapes ``(num_layers*num_directions,
 batch, hidden)`` from the hx/cx/hy/cy question in oneDNN issue #218).
 
+Variable-length (packed) batches (the packed-sequence question of oneDNN
+issue #218 asks for them; the pages fix no semantics, so the plainest
+reading -- the one PyTorch's packed sequences have -- is taken): row ``b``
+has ``lengths[b]`` valid steps ``t < lengths[b]``; at the other steps its
+state is carried unchanged (``h``, and ``c`` for LSTM) and its output is 0.
+Direction 0 thus stops at ``t = lengths[b] - 1`` and direction 1 starts
+there, so ``hy`` is the state after the last valid step of each direction.
+In the backward pass such a step passes ``dh`` (and ``dc``) through
+unchanged, ignores ``dy`` there, and contributes nothing to ``dx``, ``dW``
+or ``db``.
+
 Backward (the pages only say forward results are reused by the backward
 pass, MXNet page "Operator Registration"; the chain rule below is derived by
 hand and pinned by central finite differences): see :func:`backward`.
@@ -132,8 +143,15 @@ def _check_params(mode, params, num_layers, num_dirs, input_size, hidden):
             assert p["b_hh"].shape == (G * hidden,)
 
 
+def _valid_rows(lengths, t, B):
+    """``[B, 1]`` boolean mask of the rows for which step ``t`` is valid."""
+    if lengths is None:
+        return np.ones((B, 1), dtype=bool)
+    return (t < np.asarray(lengths))[:, None]
+
+
 def forward(mode, x, params, h0=None, c0=None, num_dirs=1, gru_variant="pytorch",
-            keep=False):
+            keep=False, lengths=None):
     """Stacked, optionally bidirectional forward pass in fp64.
 
     ``x`` ``[T, B, I]`` (TNC, the layout named in the oneDNN issue's
@@ -143,7 +161,9 @@ def forward(mode, x, params, h0=None, c0=None, num_dirs=1, gru_variant="pytorch"
     Returns ``(y, hy, cy, cache)``: ``y [T, B, D*H]`` of the top layer,
     ``hy``/``cy`` ``[L*D, B, H]`` (``cy`` is ``None`` unless LSTM) and, if
     ``keep``, the per-step intermediates the backward pass reuses (the MXNet
-    page's "reserved workspace"), else ``None``.
+    page's "reserved workspace"), else ``None``.  ``lengths`` (``[B]`` ints
+    in ``[0, T]``, or ``None`` for all ``T``) gives each row's number of
+    valid steps (module docstring).
     """
     x = np.asarray(x, dtype=np.float64)
     T, B, I = x.shape
@@ -158,7 +178,11 @@ def forward(mode, x, params, h0=None, c0=None, num_dirs=1, gru_variant="pytorch"
         c0 = np.zeros((L * D, B, H)) if c0 is None else np.asarray(c0, np.float64)
     hy = np.zeros((L * D, B, H))
     cy = np.zeros((L * D, B, H)) if mode == "lstm" else None
-    cache = {"layer_inputs": [], "steps": {}, "gru_variant": gru_variant} if keep else None
+    if lengths is not None:
+        lengths = np.asarray(lengths, dtype=np.int64)
+        assert lengths.shape == (B,) and np.all((lengths >= 0) & (lengths <= T)), lengths
+    cache = ({"layer_inputs": [], "steps": {}, "gru_variant": gru_variant, "lengths": lengths}
+             if keep else None)
 
     layer_in = x
     for l in range(L):
@@ -171,10 +195,16 @@ def forward(mode, x, params, h0=None, c0=None, num_dirs=1, gru_variant="pytorch"
             c = c0[l * D + d] if mode == "lstm" else None
             order = range(T) if d == 0 else range(T - 1, -1, -1)
             for t in order:
-                h_prev = h
+                h_prev, c_prev = h, c
                 h, c, saved = cell_forward(mode, layer_in[t], h_prev, c, p, gru_variant)
-                y_l[t, :, d * H:(d + 1) * H] = h
+                valid = _valid_rows(lengths, t, B)
+                if lengths is not None:   # rows past their length keep their state
+                    h = np.where(valid, h, h_prev)
+                    if mode == "lstm":
+                        c = np.where(valid, c, c_prev)
+                y_l[t, :, d * H:(d + 1) * H] = np.where(valid, h, 0.0)
                 if keep:
+                    saved["valid"] = valid
                     saved["h_prev"] = h_prev
                     cache["steps"][(l, d, t)] = saved
             hy[l * D + d] = h
@@ -212,7 +242,9 @@ def backward(mode, params, cache, dy, dhy=None, dcy=None, num_dirs=1):
     Then ``dh_prev = dG_h W_hh (+ dh*z for GRU)``, ``dX_l[t] += dG_i W_ih``,
     ``dW_ih += dG_i^T x_t``, ``dW_hh += dG_h^T h_prev``,
     ``db_ih += sum_b dG_i``, ``db_hh += sum_b dG_h``.  ``dX_l`` is
-    ``dY_{l-1}``; ``dX_0`` is ``dx``.
+    ``dY_{l-1}``; ``dX_0`` is ``dx``.  For the rows of a step past their
+    length (the forward's ``lengths``) ``dY`` is ignored, ``dG_i = dG_h = 0``
+    and ``dh``, ``dc`` pass through unchanged.
     """
     if cache is None:
         raise ValueError("backward needs the cache of forward(..., keep=True)")
@@ -244,7 +276,9 @@ def backward(mode, params, cache, dy, dhy=None, dcy=None, num_dirs=1):
             for t in order:
                 s = cache["steps"][(l, d, t)]
                 h_prev = s["h_prev"]
-                dh = dh + dY[t, :, d * H:(d + 1) * H]
+                valid = s["valid"]
+                dh_carried, dc_carried = dh, dc
+                dh = dh + np.where(valid, dY[t, :, d * H:(d + 1) * H], 0.0)
                 direct = 0.0
                 if mode == "rnn_tanh":
                     da = dh * (1.0 - s["h"] ** 2)
@@ -271,6 +305,12 @@ def backward(mode, params, cache, dy, dhy=None, dcy=None, num_dirs=1):
                     dG_i = np.concatenate([da_r, da_z, da_n], axis=1)
                     dG_h = np.concatenate([da_r, da_z, da_n * r], axis=1)
                     direct = dh * z
+                if cache["lengths"] is not None:   # rows past their length
+                    dG_i = np.where(valid, dG_i, 0.0)
+                    dG_h = np.where(valid, dG_h, 0.0)
+                    direct = np.where(valid, direct, dh_carried)
+                    if mode == "lstm":
+                        dc = np.where(valid, dc, dc_carried)
                 dX[t] += dG_i @ p["w_ih"]
                 g["w_ih"] += dG_i.T @ layer_in[t]
                 g["w_hh"] += dG_h.T @ h_prev

@@ -181,10 +181,13 @@ def _torch_module(mode, I, H, L, D):
     return torch.nn.RNN(nonlinearity="tanh", **kw)
 
 
-def check_against_torch(orc, mode, L, D, T=4, B=3, I=5, H=6, seed=11):
+def check_against_torch(orc, mode, L, D, T=4, B=3, I=5, H=6, seed=11, lengths=None):
     """Normwise error of the oracle's forward outputs and all gradients
     against ``torch.nn`` in float64 on the CPU (same equations; PyTorch is
-    the implementation the oneDNN issue names for the GRU flavour)."""
+    the implementation the oneDNN issue names for the GRU flavour).  With
+    ``lengths`` (all >= 1, torch's packed sequences reject empty rows) the
+    torch module runs on ``pack_padded_sequence`` input and its output is
+    padded back with zeros."""
     case = rand_case(mode, L, D, T, B, I, H, seed)
     params = case["params"]
     m = _torch_module(mode, I, H, L, D)
@@ -198,18 +201,24 @@ def check_against_torch(orc, mode, L, D, T=4, B=3, I=5, H=6, seed=11):
                     getattr(m, tname).copy_(torch.from_numpy(params[l][d][name]))
     x = torch.from_numpy(case["x"]).requires_grad_(True)
     h0 = torch.from_numpy(case["h0"]).requires_grad_(True)
+    xin = x
+    if lengths is not None:
+        xin = torch.nn.utils.rnn.pack_padded_sequence(
+            x, torch.as_tensor(lengths, dtype=torch.int64), enforce_sorted=False)
     if mode == "lstm":
         c0 = torch.from_numpy(case["c0"]).requires_grad_(True)
-        out, (hn, cn) = m(x, (h0, c0))
+        out, (hn, cn) = m(xin, (h0, c0))
     else:
-        out, hn = m(x, h0)
+        out, hn = m(xin, h0)
+    if lengths is not None:
+        out, _ = torch.nn.utils.rnn.pad_packed_sequence(out, total_length=T)
     loss = (out * torch.from_numpy(case["dy"])).sum() + (hn * torch.from_numpy(case["dhy"])).sum()
     if mode == "lstm":
         loss = loss + (cn * torch.from_numpy(case["dcy"])).sum()
     loss.backward()
 
     y, hy, cy, cache = orc.forward(mode, case["x"], params, h0=case["h0"], c0=case["c0"],
-                                   num_dirs=D, keep=True)
+                                   num_dirs=D, keep=True, lengths=lengths)
     errs = [normwise(y, out.detach().numpy()), normwise(hy, hn.detach().numpy())]
     if mode == "lstm":
         errs.append(normwise(cy, cn.detach().numpy()))
@@ -228,21 +237,23 @@ def check_against_torch(orc, mode, L, D, T=4, B=3, I=5, H=6, seed=11):
 
 
 # --------------------------------------------------------- finite differences
-def _loss(orc, mode, case, D):
+def _loss(orc, mode, case, D, lengths=None):
     y, hy, cy, _ = orc.forward(mode, case["x"], case["params"], h0=case["h0"], c0=case["c0"],
-                               num_dirs=D)
+                               num_dirs=D, lengths=lengths)
     v = float(np.sum(y * case["dy"]) + np.sum(hy * case["dhy"]))
     if mode == "lstm":
         v += float(np.sum(cy * case["dcy"]))
     return v
 
 
-def check_finite_differences(orc, mode, L, D, T=3, B=2, I=3, H=4, seed=5, eps=1e-6):
+def check_finite_differences(orc, mode, L, D, T=3, B=2, I=3, H=4, seed=5, eps=1e-6,
+                             lengths=None):
     """Worst normwise error of every analytic gradient against central
-    differences of the scalar loss ``sum(y*dy) + sum(hy*dhy) + sum(cy*dcy)``."""
+    differences of the scalar loss ``sum(y*dy) + sum(hy*dhy) + sum(cy*dcy)``
+    (optionally with per-row sequence lengths)."""
     case = rand_case(mode, L, D, T, B, I, H, seed)
     _, _, _, cache = orc.forward(mode, case["x"], case["params"], h0=case["h0"], c0=case["c0"],
-                                 num_dirs=D, keep=True)
+                                 num_dirs=D, keep=True, lengths=lengths)
     dx, dh0, dc0, dparams = orc.backward(mode, case["params"], cache, case["dy"],
                                          dhy=case["dhy"], dcy=case["dcy"], num_dirs=D)
 
@@ -253,9 +264,9 @@ def check_finite_differences(orc, mode, L, D, T=3, B=2, I=3, H=4, seed=5, eps=1e
             idx = it.multi_index
             old = arr[idx]
             arr[idx] = old + eps
-            lp = _loss(orc, mode, case, D)
+            lp = _loss(orc, mode, case, D, lengths)
             arr[idx] = old - eps
-            lm = _loss(orc, mode, case, D)
+            lm = _loss(orc, mode, case, D, lengths)
             arr[idx] = old
             g[idx] = (lp - lm) / (2 * eps)
         return g
@@ -267,4 +278,49 @@ def check_finite_differences(orc, mode, L, D, T=3, B=2, I=3, H=4, seed=5, eps=1e
         for d in range(D):
             for name in ("w_ih", "w_hh", "b_ih", "b_hh"):
                 errs.append(normwise(dparams[l][d][name], fd(case["params"][l][d][name])))
+    return max(errs)
+
+
+# ------------------------------------------------------------ packed batches
+def check_packed_truncation(orc, mode, L, D, lengths, T=5, I=3, H=4, seed=17):
+    """Worst normwise error between a batch with per-row lengths and, row by
+    row, the plain (unmasked) pass over that row's sequence cut to its
+    length: outputs, final states, dx, dh0, dc0 and the weight gradients
+    (the batched gradient is the sum of the rows').  Rows of length 0 must
+    return h0 / dhy unchanged and zeros elsewhere."""
+    B = len(lengths)
+    case = rand_case(mode, L, D, T, B, I, H, seed)
+    P = case["params"]
+    y, hy, cy, cache = orc.forward(mode, case["x"], P, h0=case["h0"], c0=case["c0"],
+                                   num_dirs=D, keep=True, lengths=lengths)
+    dx, dh0, dc0, dp = orc.backward(mode, P, cache, case["dy"], dhy=case["dhy"], dcy=case["dcy"],
+                                    num_dirs=D)
+    errs = []
+    acc = [[{k: np.zeros_like(v) for k, v in P[l][d].items()} for d in range(D)] for l in range(L)]
+    for b, n in enumerate(lengths):
+        sl = slice(b, b + 1)
+        st = lambda a: None if a is None else a[:, sl]
+        if n == 0:
+            errs += [float(np.max(np.abs(y[:, b]))), float(np.max(np.abs(dx[:, b]))),
+                     normwise(hy[:, b], case["h0"][:, b]), normwise(dh0[:, b], case["dhy"][:, b])]
+            if mode == "lstm":
+                errs += [normwise(cy[:, b], case["c0"][:, b]), normwise(dc0[:, b], case["dcy"][:, b])]
+            continue
+        yr, hyr, cyr, cr = orc.forward(mode, case["x"][:n, sl], P, h0=st(case["h0"]), c0=st(case["c0"]),
+                                       num_dirs=D, keep=True)
+        dxr, dh0r, dc0r, dpr = orc.backward(mode, P, cr, case["dy"][:n, sl], dhy=st(case["dhy"]),
+                                            dcy=st(case["dcy"]), num_dirs=D)
+        errs += [normwise(y[:n, b], yr[:, 0]), float(np.max(np.abs(y[n:, b]), initial=0.0)),
+                 normwise(hy[:, b], hyr[:, 0]), normwise(dx[:n, b], dxr[:, 0]),
+                 float(np.max(np.abs(dx[n:, b]), initial=0.0)), normwise(dh0[:, b], dh0r[:, 0])]
+        if mode == "lstm":
+            errs += [normwise(cy[:, b], cyr[:, 0]), normwise(dc0[:, b], dc0r[:, 0])]
+        for l in range(L):
+            for d in range(D):
+                for k in acc[l][d]:
+                    acc[l][d][k] += dpr[l][d][k]
+    for l in range(L):
+        for d in range(D):
+            for k in acc[l][d]:
+                errs.append(normwise(dp[l][d][k], acc[l][d][k]))
     return max(errs)

@@ -55,8 +55,12 @@ MUTANTS = [
      ["gru"]),
     ("bptt_dx_missing", "dX[t] += dG_i @ p[\"w_ih\"]", "dX[t] += 0.0 * (dG_i @ p[\"w_ih\"])",
      ["lstm"]),
-    ("bptt_dy_not_added", "dh = dh + dY[t, :, d * H:(d + 1) * H]",
-     "dh = dh + dY[t, :, 0:H]", ["rnn_tanh"]),
+    ("bptt_dy_not_added", "np.where(valid, dY[t, :, d * H:(d + 1) * H], 0.0)",
+     "np.where(valid, dY[t, :, 0:H], 0.0)", ["rnn_tanh"]),
+    ("packed_state_not_held", "h = np.where(valid, h, h_prev)", "h = np.where(valid, h, h)",
+     ["gru"]),
+    ("packed_bwd_no_passthrough", "direct = np.where(valid, direct, dh_carried)",
+     "direct = np.where(valid, direct, 0.0)", ["rnn_tanh"]),
 ]
 
 
@@ -77,6 +81,8 @@ def _pins_fail(mod, modes):
             checks.append(lambda mode=mode, L=L, D=D: oc.check_against_torch(mod, mode, L, D) > 1e-11)
             checks.append(lambda mode=mode, L=L, D=D:
                           oc.check_finite_differences(mod, mode, L, D, T=2, B=2, I=3, H=2) > 1e-6)
+            checks.append(lambda mode=mode, L=L, D=D:
+                          oc.check_against_torch(mod, mode, L, D, lengths=[4, 1, 3]) > 1e-11)
     for chk in checks:
         try:
             if chk():

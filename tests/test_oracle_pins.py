@@ -51,6 +51,34 @@ def test_finite_differences(mode, L, D):
     assert oc.check_finite_differences(orc, mode, L, D) < 1e-6
 
 
+# ------------------------------------------------------- variable lengths
+@pytest.mark.parametrize("mode,L,D", list(itertools.product(MODES, (1, 2), (1, 2))))
+def test_packed_matches_torch_nn_float64(mode, L, D):
+    """torch.nn on pack_padded_sequence input (rows of lengths 4, 1, 3)."""
+    assert oc.check_against_torch(orc, mode, L, D, lengths=[4, 1, 3]) < 1e-11
+
+
+@pytest.mark.parametrize("mode,L,D", list(itertools.product(MODES, (1, 2), (1, 2))))
+def test_packed_rows_equal_truncated_sequences(mode, L, D):
+    assert oc.check_packed_truncation(orc, mode, L, D, lengths=[5, 0, 2, 3]) < 1e-13
+
+
+@pytest.mark.parametrize("mode,D", list(itertools.product(MODES, (1, 2))))
+def test_packed_finite_differences(mode, D):
+    assert oc.check_finite_differences(orc, mode, 2, D, lengths=[1, 3]) < 1e-6
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_full_lengths_equal_unpacked(mode):
+    case = oc.rand_case(mode, 2, 2, 4, 3, 3, 5, seed=3)
+    a = orc.forward(mode, case["x"], case["params"], h0=case["h0"], c0=case["c0"], num_dirs=2)
+    b = orc.forward(mode, case["x"], case["params"], h0=case["h0"], c0=case["c0"], num_dirs=2,
+                    lengths=[4, 4, 4])
+    for u, v in zip(a[:3], b[:3]):
+        if u is not None:
+            assert np.array_equal(u, v)
+
+
 # ------------------------------------------------------------------ invariants
 @pytest.mark.parametrize("mode", MODES)
 def test_reverse_direction_is_time_reversed_forward(mode):
