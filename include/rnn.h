@@ -95,6 +95,24 @@ rnn_status_t rnn_destroy(rnn_handle_t h);
  * Results are bitwise identical across schedules. */
 rnn_status_t rnn_set_schedule(rnn_handle_t h, rnn_schedule_t s);
 
+/* Variable-length (packed) batches: the packed-sequence question of oneDNN
+ * issue #218, with the semantics of PyTorch's packed sequences (the pages
+ * fix none).  `lengths` is a DEVICE pointer to int32 [B] (B of every later
+ * compute call) giving each batch row's number of valid steps; values are
+ * clamped to [0, T].  Row b is processed only at steps t < lengths[b]: at the
+ * other steps its state (h, and c for LSTM) is carried unchanged and its y is
+ * 0, so direction 0 stops and direction 1 starts at t = lengths[b] - 1 and
+ * hy/cy are the states after each direction's last valid step.  The backward
+ * pass ignores dy at those steps, passes dh/dc through them, and gives zero dx
+ * there; dW/db collect only valid steps.  Rows of length 0 return h0/c0 and
+ * dhy/dcy unchanged.  NULL (the default) means every row has T steps.  The
+ * pointer is stored in the handle (the caller keeps the buffer alive and
+ * unchanged while calls that use it run) and applies to the compute calls
+ * that follow; rnn_backward_data and rnn_backward_weights return
+ * BAD_CALL_ORDER if it changed since the rnn_forward_training they follow.
+ * Errors: INVALID_ARG for a NULL handle. */
+rnn_status_t rnn_set_sequence_lengths(rnn_handle_t h, const int* lengths);
+
 /* Bytes of the packed weight buffer (grad = 0: matrices in the handle's
  * wtype, biases fp32) or of the packed weight-gradient buffer (grad = 1: all
  * fp32). */

@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     rnn_create,
     rnn_destroy,
     rnn_set_schedule,
+    rnn_set_sequence_lengths,
     rnn_weights_size,
     rnn_weight_offset,
     rnn_workspace_size,

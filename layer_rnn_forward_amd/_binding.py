@@ -45,6 +45,7 @@ def load_library():
         "rnn_create": [ctypes.POINTER(vp), i, i, i, i, i, i],
         "rnn_destroy": [vp],
         "rnn_set_schedule": [vp, i],
+        "rnn_set_sequence_lengths": [vp, vp],
         "rnn_weights_size": [vp, i, psz],
         "rnn_weight_offset": [vp, i, i, i, i, psz, psz],
         "rnn_workspace_size": [vp, i, i, i, psz],
@@ -84,6 +85,7 @@ class Handle:
         self.mode, self.L, self.D = mode, num_layers, num_dirs
         self.I, self.H, self.wtype = input_size, hidden_size, wtype
         self.G = {"rnn_tanh": 1, "lstm": 4, "gru": 3}[mode]
+        self.lengths = None
 
     def __del__(self):
         try:
@@ -132,6 +134,15 @@ def rnn_destroy(h: Handle):
 
 def rnn_set_schedule(h: Handle, sched: int):
     _check(load_library().rnn_set_schedule(h.ptr, int(sched)), "rnn_set_schedule")
+
+
+def rnn_set_sequence_lengths(h: Handle, lengths):
+    """Per-row valid step counts (int32 device tensor [B]) for the calls that
+    follow, or None for full-length rows.  The handle keeps a reference so the
+    tensor outlives its use."""
+    _check(load_library().rnn_set_sequence_lengths(h.ptr, _ptr(lengths, "lengths", torch.int32)),
+           "rnn_set_sequence_lengths")
+    h.lengths = lengths
 
 
 def rnn_weights_size(h: Handle, grad: int = 0) -> int:

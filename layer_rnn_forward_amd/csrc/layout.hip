@@ -34,7 +34,14 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TransposeParams p)
     const int r = r0 + rl, c = c0 + tx;
     float v = 0.f;
     if (r < p.R && c < p.C) {
-      if (r >= p.alt_r0 && r < p.alt_r1) {
+      int lb = -1;   // alt row of a row whose successor is past its length
+      if (p.lengths) {
+        const int t = r / p.len_B, b = r - t * p.len_B;
+        if (t + 1 >= min(max(p.lengths[b], 0), p.len_T)) lb = b;
+      }
+      if (lb >= 0) {
+        if (p.alt) v = ld_elem<IN_BF>(p.alt, (size_t)lb * p.ld_alt + c);
+      } else if (r >= p.alt_r0 && r < p.alt_r1) {
         if (p.alt) v = ld_elem<IN_BF>(p.alt, (size_t)(r - p.alt_r0) * p.ld_alt + c);
       } else {
         v = ld_elem<IN_BF>(p.src, (size_t)((long long)(r + p.shift) * p.ld_src) + c);

@@ -302,6 +302,8 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   const size_t st_idx = (((size_t)li * D + d) * B + qbg) * H + qu;
   const size_t hx_idx = (((size_t)layer * D + d) * B + qbg) * H + qu;
   const size_t my_off = (size_t)(slice * UJ + qj / PER) * gran + qb * 16 + (qj % PER) * ES;
+  // valid steps of this row (t < qlen); past them the state is carried and y is 0
+  const int qlen = (p.lengths && qv && live) ? min(max(p.lengths[qbg], 0), T) : T;
 
   if (tid == 0) s_fail = 0;
   if (p.s_begin < 0) {
@@ -424,12 +426,14 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         pre[gb] = v;
       }
       const float hprev = sh_h[qb * NCOL + qj];
+      const bool tv = t < qlen;
       if (MODE == MODE_LSTM) {
         const float ig = sigmoidf_(pre[0] + gxv[0]);
         const float fg = sigmoidf_(pre[1] + gxv[1]);
         const float gg = tanhf_(pre[2] + gxv[2]);
         const float og = sigmoidf_(pre[3] + gxv[3]);
-        const float cn = fg * sh_c[qb * NCOL + qj] + ig * gg;
+        const float cprev = sh_c[qb * NCOL + qj];
+        const float cn = tv ? fg * cprev + ig * gg : cprev;
         hnew = og * tanhf_(cn);
         sh_c[qb * NCOL + qj] = cn;
         rv[0] = ig; rv[1] = fg; rv[2] = gg; rv[3] = og; rv[4] = cn;
@@ -445,6 +449,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
       } else {
         hnew = tanhf_(pre[0] + gxv[0]);
       }
+      if (!tv) hnew = hprev;
       sh_h[qb * NCOL + qj] = hnew;
     }
     // only the exchange store precedes the flag; y and the reserve are read
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     if (qw) ring_store<BF16>(ring + (size_t)(s + 1) * p.ring_step, my_off, hnew);
     if (p.persistent) publish(p.flags, (unsigned)(s + 2));
     if (qv && live) {
-      p.y[li][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = hnew;
+      p.y[li][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = t < qlen ? hnew : 0.f;
       if (p.training && R > 0) {
         float* res = p.reserve[li] + (((size_t)d * T + t) * B + qbg) * R * H + qu;
 #pragma unroll
@@ -549,6 +554,8 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   const bool qv = qw && qj < Uact;
   const int qu = u0 + qj, qbg = b0 + qb;
   const size_t sidx = ((size_t)d * B + qbg) * H + qu;   // [D][B][H] state index
+  // valid steps of this row (t < qlen); every step without lengths
+  const int qlen = (p.lengths && qv) ? min(max(p.lengths[qbg], 0), T) : T;
   // ring offset of gate 0 of (qb, qj); gate g is g*UJ granules further
   const size_t my_off = (size_t)(slice * GU + qj / PER) * gran + qb * 16 + (qj % PER) * ES;
   if (tid == 0) s_fail = 0;
@@ -576,7 +583,8 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
 #pragma unroll
       for (int r = 0; r < R; ++r) rv[r] = res[(size_t)r * H];
       const int tp = (d == 0) ? t - 1 : t + 1;
-      const bool has_prev = tp >= 0 && tp < T;
+      // the previous state is h0 / c0 at the row's first step
+      const bool has_prev = tp >= 0 && tp < qlen;
       if (MODE == MODE_LSTM) {
         if (has_prev) prevv = p.reserve[(((size_t)d * T + tp) * B + qbg) * R * H + 4 * (size_t)H + qu];
         else prevv = p.c0 ? p.c0[sidx] : 0.f;
@@ -645,9 +653,14 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
       }
     } else {
       if (qv) {
-        const float dh = dhrec + dyv + sh_dh[qb * NCOL + qj];
-        float ncarry = 0.f;
-        if (MODE == MODE_LSTM) {
+        // a step past the row's length passes dh (and dc) through and
+        // ignores dy; its gate gradients stay zero
+        const bool tv = t < qlen;
+        const float dh = dhrec + (tv ? dyv : 0.f) + sh_dh[qb * NCOL + qj];
+        float ncarry = dh;
+        if (!tv) {
+        } else if (MODE == MODE_LSTM) {
+          ncarry = 0.f;
           const float ig = rv[0], fg = rv[1], gg = rv[2], og = rv[3], cc = rv[4];
           const float tau = tanhf_(cc);
           const float d_o = dh * tau;
@@ -672,6 +685,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
           dgh[2] = dan * rg;
           ncarry = dh * zg;
         } else {
+          ncarry = 0.f;
           dgi[0] = dh * (1.f - hcur * hcur);
           dgh[0] = dgi[0];
         }

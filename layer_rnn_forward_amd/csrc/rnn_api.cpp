@@ -76,11 +76,13 @@ struct Plan {
 struct rnn_desc {
   int mode = 0, L = 0, D = 0, I = 0, H = 0, wtype = 0, G = 0;
   int sched = RNN_SCHED_AUTO;
+  const int* lengths = nullptr;   // device [B] valid steps per row, or null
   size_t wbytes = 0, dwbytes = 0;
   std::vector<size_t> off[2][4];  // [grad][which] per layer block offset
   // pending training sequence
   int seq_stage = 0, seq_T = -1, seq_B = -1;
   const void* seq_ws = nullptr;
+  const int* seq_lengths = nullptr;
   // profiling
   int prof = 0;
   std::vector<ProfPending> pending;
@@ -533,6 +535,7 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
       h->seq_T = T;
       h->seq_B = B;
       h->seq_ws = ws;
+      h->seq_lengths = h->lengths;
     }
     return RNN_STATUS_SUCCESS;
   }
@@ -558,6 +561,7 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   f.stage = p.fwd.lds > 0 ? 1 : 0;
   f.persistent = p.fwd.persistent ? 1 : 0;
   f.training = training;
+  f.lengths = h->lengths;
   f.h0 = h0;
   f.c0 = c0;
   f.hy = hy;
@@ -626,6 +630,7 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
     h->seq_T = T;
     h->seq_B = B;
     h->seq_ws = ws;
+    h->seq_lengths = h->lengths;
   }
   return RNN_STATUS_SUCCESS;
 }
@@ -709,6 +714,12 @@ rnn_status_t rnn_destroy(rnn_handle_t h) {
   return RNN_STATUS_SUCCESS;
 }
 
+rnn_status_t rnn_set_sequence_lengths(rnn_handle_t h, const int* lengths) {
+  if (!h) return RNN_STATUS_INVALID_ARG;
+  h->lengths = lengths;
+  return RNN_STATUS_SUCCESS;
+}
+
 rnn_status_t rnn_set_schedule(rnn_handle_t h, rnn_schedule_t s) {
   if (!h || (s != RNN_SCHED_AUTO && s != RNN_SCHED_PERSISTENT && s != RNN_SCHED_STEPPED))
     return RNN_STATUS_INVALID_ARG;
@@ -766,7 +777,8 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
   if (h->mode != RNN_LSTM && (dcy || dc0 || c0)) return RNN_STATUS_INVALID_ARG;
   if (!W || !ws) return RNN_STATUS_INVALID_ARG;
   if (T > 0 && B > 0 && (!y || !dy || !dx)) return RNN_STATUS_INVALID_ARG;
-  if (h->seq_stage < 1 || h->seq_ws != ws || h->seq_T != T || h->seq_B != B)
+  if (h->seq_stage < 1 || h->seq_ws != ws || h->seq_T != T || h->seq_B != B ||
+      h->seq_lengths != h->lengths)
     return RNN_STATUS_BAD_CALL_ORDER;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   Plan p = make_plan(h, T, B, 1);
@@ -803,6 +815,7 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
   b.ring_group = (long long)p.bring_group;
   b.stage = p.bwd.lds > 0 ? 1 : 0;
   b.persistent = p.bwd.persistent ? 1 : 0;
+  b.lengths = h->lengths;
   b.st_dh = at<float>(ws, p.off_st);
   b.st_dc = at<float>(ws, p.off_st + p.st_bytes / 2);
   b.xch = at<void>(ws, p.off_xch);
@@ -882,7 +895,8 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
   RNN_TRY(check_common(h, T, B, ws, ws_bytes));
   if (!ws || !dW) return RNN_STATUS_INVALID_ARG;
   if (T > 0 && B > 0 && (!x || !y)) return RNN_STATUS_INVALID_ARG;
-  if (h->seq_stage < 2 || h->seq_ws != ws || h->seq_T != T || h->seq_B != B)
+  if (h->seq_stage < 2 || h->seq_ws != ws || h->seq_T != T || h->seq_B != B ||
+      h->seq_lengths != h->lengths)
     return RNN_STATUS_BAD_CALL_ORDER;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   Plan p = make_plan(h, T, B, 1);
@@ -936,6 +950,11 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
         th.ld_out = p.tb_ld;
         th.R = (int)TB;
         th.C = h->H;
+        if (d == 1) {   // a row's first reverse step starts from h0
+          th.lengths = h->lengths;
+          th.len_B = B;
+          th.len_T = T;
+        }
         RNN_TRY(dev(rnn_launch_transpose(th, 0, bf, s)));
       }
     }

@@ -69,6 +69,11 @@ struct TransposeParams {
   void* out;
   long long ld_out;
   int R, C;
+  // with lengths: row r = t*len_B + b also reads alt row b whenever
+  // t + 1 >= the row's length clamped to [0, len_T] (a reverse-direction
+  // step whose successor is past the row's end starts from h0)
+  const int* lengths;
+  int len_B, len_T;
 };
 
 // ------------------------------------------------------------- recurrence
@@ -90,6 +95,7 @@ struct FwdParams {
   int s_total;            // T + nlayers - 1
   int persistent, training, wavefront;
   int probe;              // 1: exchange only (waits, ring stores, flags); no weights, math or outputs
+  const int* lengths;     // [B] valid steps per row (clamped to [0, T]), or null: all T
   int first_layer;        // index of layer 0 of this launch in the network
   const void* w_ih[kMaxLayersPerLaunch];   // layer block [D*G*H, I_l]
   const void* w_hh[kMaxLayersPerLaunch];   // layer block [D*G*H, H]
@@ -121,6 +127,7 @@ struct BwdParams {
   int group_poll;         // 1: one wave polls every producer; 0: each wave its own
   int s_begin, s_end;     // processing steps; s == T is the final dh0 phase
   int persistent;
+  const int* lengths;     // [B] valid steps per row (clamped to [0, T]), or null: all T
   const void* w_hh;       // layer block [D*G*H, H]
   const float* reserve;   // [D][T][B][R][H]
   const float* y;         // layer output [T, B, D*H]

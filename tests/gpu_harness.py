@@ -25,13 +25,16 @@ def to_dev(a, dtype=torch.float32):
 
 
 def run_gpu(mode, L, D, case, wtype="f32", sched=R.SCHED_AUTO, training=True, backward=True,
-            pass_state=True, pass_grads=True, repeat=1):
-    """Returns a dict of numpy results from the library (fp32 -> fp64)."""
+            pass_state=True, pass_grads=True, repeat=1, lengths=None):
+    """Returns a dict of numpy results from the library (fp32 -> fp64).
+    ``lengths``: per-row valid steps (list of ints) or None."""
     x = case["x"]
     T, B, I = x.shape
     H = case["params"][0][0]["w_hh"].shape[1]
     h = R.rnn_create(mode, L, D, I, H, wtype)
     R.rnn_set_schedule(h, sched)
+    if lengths is not None:
+        R.rnn_set_sequence_lengths(h, torch.as_tensor(lengths, dtype=torch.int32, device="cuda"))
     W = R.pack_weights(h, case["params"])
     ws = torch.empty(R.rnn_workspace_size(h, T, B, 1 if training else 0), dtype=torch.uint8,
                      device="cuda")
@@ -74,11 +77,11 @@ def run_gpu(mode, L, D, case, wtype="f32", sched=R.SCHED_AUTO, training=True, ba
     return out
 
 
-def run_oracle(mode, L, D, case, backward=True, pass_state=True, pass_grads=True):
+def run_oracle(mode, L, D, case, backward=True, pass_state=True, pass_grads=True, lengths=None):
     h0 = case["h0"] if pass_state else None
     c0 = case["c0"] if (pass_state and mode == "lstm") else None
     y, hy, cy, cache = orc.forward(mode, case["x"], case["params"], h0=h0, c0=c0, num_dirs=D,
-                                   keep=backward)
+                                   keep=backward, lengths=lengths)
     out = {"y": y, "hy": hy}
     if mode == "lstm":
         out["cy"] = cy
