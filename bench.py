@@ -162,6 +162,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fp32", action="store_true")
+    ap.add_argument("--no-small-batch", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
@@ -274,6 +275,16 @@ def main():
                                    "ms_per_step": round(float(np.mean(s_ms)), 4),
                                    "fwd_ms": round(float(np.median(f_ms)), 4),
                                    "pct_mfma_peak": round(100.0 * v32 / (PEAK_TFLOPS["f32"] * 1000), 4)}
+    if not args.no_small_batch and w.layers == 1:
+        # serving-size batches: forward-inference latency of the same layer
+        import dataclasses
+        sb = {}
+        for Bs in (1, 2, 4):
+            rs = Runner(dataclasses.replace(w, B=Bs), torch, R, synth)
+            f_ms, _ = rs.timed(rs.fwd, max(5, args.steps // 2), args.warmup)
+            med = float(np.median(f_ms))
+            sb[str(Bs)] = {"fwd_ms": round(med, 4), "us_per_step": round(1000.0 * med / w.T, 3)}
+        out["small_batch_fwd"] = sb
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
     print(json.dumps(out))

@@ -246,3 +246,15 @@ def test_exchange_floor_probe(mode, L, D, wtype):
         R.rnn_exchange_floor(h, T, B, small)
     assert e.value.status == -3
     R.rnn_destroy(h)
+
+
+@pytest.mark.parametrize("mode,B", list(itertools.product(MODES, (1, 2, 4))))
+def test_serving_batches(mode, B):
+    """Serving-size batches (1, 2, 4 rows) at the full hidden width of the
+    DS2 shape, bf16 weights, both directions."""
+    T, I, H = 24, 64, 800
+    _announce("serving", mode, B)
+    case = _case(mode, 1, 2, T, B, I, H, "bf16", seed=31)
+    g = run_gpu(mode, 1, 2, case, "bf16")
+    o = run_oracle(mode, 1, 2, case)
+    check(compare(g, o, mode, 1, 2), *TOL["bf16"])
