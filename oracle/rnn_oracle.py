@@ -215,8 +215,7 @@ def forward(mode, x, params, h0=None, c0=None, num_dirs=1, gru_variant="pytorch"
 
 
 def backward(mode, params, cache, dy, dhy=None, dcy=None, num_dirs=1):
-    """Backward through time for :func:`forward` (PyTorch/cuDNN GRU flavour
-    only).
+    """Backward through time for :func:`forward` (every GRU flavour).
 
     Gradients of the scalar ``sum(y*dy) + sum(hy*dhy) + sum(cy*dcy)``.
     Returns ``(dx, dh0, dc0, dparams)`` with ``dparams[l][d]`` holding
@@ -238,6 +237,15 @@ def backward(mode, params, cache, dy, dhy=None, dcy=None, num_dirs=1):
       ``da_n = dn * (1 - n^2)``; ``da_r = da_n * gh_n * r(1-r)``;
       ``da_z = dz * z(1-z)``; ``dG_i = [da_r, da_z, da_n]``;
       ``dG_h = [da_r, da_z, da_n * r]``; plus the direct term ``dh * z``.
+    * GRU, TensorFlow / original-paper flavours (``n`` reads ``(r * h_prev)
+      W_hn^T``): ``dn = dh * (1 - z)``, ``dz = dh * (h_prev - n)``, direct
+      ``dh * z`` (TensorFlow) or ``dn = dh * z``, ``dz = dh * (n - h_prev)``,
+      direct ``dh * (1 - z)`` (paper); ``da_n = dn * (1 - n^2)``;
+      ``d_rh = da_n W_hn`` (the gradient of ``r * h_prev``); ``dr = d_rh *
+      h_prev``; ``da_r = dr * r(1-r)``; ``da_z = dz * z(1-z)``;
+      ``dG_i = dG_h = [da_r, da_z, da_n]``, where the n block of ``W_hh``
+      multiplies ``r * h_prev`` (so ``dW_hn = da_n^T (r * h_prev)``) and the
+      direct term gains ``d_rh * r``.
 
     Then ``dh_prev = dG_h W_hh (+ dh*z for GRU)``, ``dX_l[t] += dG_i W_ih``,
     ``dW_ih += dG_i^T x_t``, ``dW_hh += dG_h^T h_prev``,
@@ -248,8 +256,7 @@ def backward(mode, params, cache, dy, dhy=None, dcy=None, num_dirs=1):
     """
     if cache is None:
         raise ValueError("backward needs the cache of forward(..., keep=True)")
-    if cache["gru_variant"] != "pytorch":
-        raise NotImplementedError("backward covers the PyTorch/cuDNN GRU flavour only")
+    variant = cache["gru_variant"]
     L = len(params)
     D = num_dirs
     dy = np.asarray(dy, np.float64)
@@ -295,6 +302,19 @@ def backward(mode, params, cache, dy, dhy=None, dcy=None, num_dirs=1):
                         [d_i * i * (1.0 - i), d_f * f * (1.0 - f),
                          d_g * (1.0 - gg ** 2), d_o * o * (1.0 - o)], axis=1)
                     dc = dc * f
+                elif variant in ("tf", "paper"):   # gru, n reads (r * h_prev) W_hn^T
+                    r, z, n = s["r"], s["z"], s["n"]
+                    if variant == "tf":
+                        dn, dz, direct = dh * (1.0 - z), dh * (h_prev - n), dh * z
+                    else:
+                        dn, dz, direct = dh * z, dh * (n - h_prev), dh * (1.0 - z)
+                    da_n = dn * (1.0 - n ** 2)
+                    w_hn = p["w_hh"][2 * H:]
+                    d_rh = da_n @ w_hn
+                    da_r = d_rh * h_prev * r * (1.0 - r)
+                    da_z = dz * z * (1.0 - z)
+                    dG_i = dG_h = np.concatenate([da_r, da_z, da_n], axis=1)
+                    direct = direct + d_rh * r
                 else:  # gru, PyTorch/cuDNN flavour
                     r, z, n, gh_n = s["r"], s["z"], s["n"], s["gh_n"]
                     dn = dh * (1.0 - z)
@@ -313,10 +333,15 @@ def backward(mode, params, cache, dy, dhy=None, dcy=None, num_dirs=1):
                         dc = np.where(valid, dc, dc_carried)
                 dX[t] += dG_i @ p["w_ih"]
                 g["w_ih"] += dG_i.T @ layer_in[t]
-                g["w_hh"] += dG_h.T @ h_prev
                 g["b_ih"] += dG_i.sum(axis=0)
                 g["b_hh"] += dG_h.sum(axis=0)
-                dh = dG_h @ p["w_hh"] + direct
+                if mode == "gru" and variant in ("tf", "paper"):
+                    g["w_hh"][:2 * H] += dG_h[:, :2 * H].T @ h_prev
+                    g["w_hh"][2 * H:] += dG_h[:, 2 * H:].T @ (s["r"] * h_prev)
+                    dh = dG_h[:, :2 * H] @ p["w_hh"][:2 * H] + direct
+                else:
+                    g["w_hh"] += dG_h.T @ h_prev
+                    dh = dG_h @ p["w_hh"] + direct
             dh0[l * D + d] = dh
             if mode == "lstm":
                 dc0[l * D + d] = dc

@@ -237,9 +237,9 @@ def check_against_torch(orc, mode, L, D, T=4, B=3, I=5, H=6, seed=11, lengths=No
 
 
 # --------------------------------------------------------- finite differences
-def _loss(orc, mode, case, D, lengths=None):
+def _loss(orc, mode, case, D, lengths=None, gru_variant="pytorch"):
     y, hy, cy, _ = orc.forward(mode, case["x"], case["params"], h0=case["h0"], c0=case["c0"],
-                               num_dirs=D, lengths=lengths)
+                               num_dirs=D, lengths=lengths, gru_variant=gru_variant)
     v = float(np.sum(y * case["dy"]) + np.sum(hy * case["dhy"]))
     if mode == "lstm":
         v += float(np.sum(cy * case["dcy"]))
@@ -247,13 +247,13 @@ def _loss(orc, mode, case, D, lengths=None):
 
 
 def check_finite_differences(orc, mode, L, D, T=3, B=2, I=3, H=4, seed=5, eps=1e-6,
-                             lengths=None):
+                             lengths=None, gru_variant="pytorch"):
     """Worst normwise error of every analytic gradient against central
     differences of the scalar loss ``sum(y*dy) + sum(hy*dhy) + sum(cy*dcy)``
-    (optionally with per-row sequence lengths)."""
+    (optionally with per-row sequence lengths, or another GRU flavour)."""
     case = rand_case(mode, L, D, T, B, I, H, seed)
     _, _, _, cache = orc.forward(mode, case["x"], case["params"], h0=case["h0"], c0=case["c0"],
-                                 num_dirs=D, keep=True, lengths=lengths)
+                                 num_dirs=D, keep=True, lengths=lengths, gru_variant=gru_variant)
     dx, dh0, dc0, dparams = orc.backward(mode, case["params"], cache, case["dy"],
                                          dhy=case["dhy"], dcy=case["dcy"], num_dirs=D)
 
@@ -264,9 +264,9 @@ def check_finite_differences(orc, mode, L, D, T=3, B=2, I=3, H=4, seed=5, eps=1e
             idx = it.multi_index
             old = arr[idx]
             arr[idx] = old + eps
-            lp = _loss(orc, mode, case, D, lengths)
+            lp = _loss(orc, mode, case, D, lengths, gru_variant)
             arr[idx] = old - eps
-            lm = _loss(orc, mode, case, D, lengths)
+            lm = _loss(orc, mode, case, D, lengths, gru_variant)
             arr[idx] = old
             g[idx] = (lp - lm) / (2 * eps)
         return g

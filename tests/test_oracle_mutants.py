@@ -57,6 +57,11 @@ MUTANTS = [
      ["lstm"]),
     ("bptt_dy_not_added", "np.where(valid, dY[t, :, d * H:(d + 1) * H], 0.0)",
      "np.where(valid, dY[t, :, 0:H], 0.0)", ["rnn_tanh"]),
+    ("gru_tf_bptt_no_rh_direct", "direct = direct + d_rh * r", "direct = direct", ["gru_tf"]),
+    ("gru_tf_dW_hn_uses_h", 'g["w_hh"][2 * H:] += dG_h[:, 2 * H:].T @ (s["r"] * h_prev)',
+     'g["w_hh"][2 * H:] += dG_h[:, 2 * H:].T @ h_prev', ["gru_tf"]),
+    ("gru_paper_dz_sign", "dn, dz, direct = dh * z, dh * (n - h_prev), dh * (1.0 - z)",
+     "dn, dz, direct = dh * z, dh * (h_prev - n), dh * (1.0 - z)", ["gru_paper"]),
     ("packed_state_not_held", "h = np.where(valid, h, h_prev)", "h = np.where(valid, h, h)",
      ["gru"]),
     ("packed_bwd_no_passthrough", "direct = np.where(valid, direct, dh_carried)",
@@ -77,6 +82,11 @@ def _pins_fail(mod, modes):
               lambda: oc.check_closed_forms(mod) > 1e-11,
               lambda: oc.check_bptt_closed_forms(mod) > 1e-12]
     for mode in modes:
+        if mode.startswith("gru_"):   # another GRU flavour: finite differences only
+            v = mode[4:]
+            checks.append(lambda v=v: oc.check_finite_differences(mod, "gru", 1, 2, T=3, B=2, I=3, H=2,
+                                                                  gru_variant=v) > 1e-6)
+            continue
         for L, D in ((2, 2), (1, 1)):
             checks.append(lambda mode=mode, L=L, D=D: oc.check_against_torch(mod, mode, L, D) > 1e-11)
             checks.append(lambda mode=mode, L=L, D=D:

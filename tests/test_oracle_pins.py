@@ -51,6 +51,14 @@ def test_finite_differences(mode, L, D):
     assert oc.check_finite_differences(orc, mode, L, D) < 1e-6
 
 
+@pytest.mark.parametrize("variant,L,D", list(itertools.product(("tf", "paper"), (1, 2), (1, 2))))
+def test_gru_flavour_finite_differences(variant, L, D):
+    """Backward of the TensorFlow and original-paper GRU flavours (n reads
+    (r*h) W_hn^T) against central differences, with and without lengths."""
+    assert oc.check_finite_differences(orc, "gru", L, D, gru_variant=variant) < 1e-6
+    assert oc.check_finite_differences(orc, "gru", L, D, gru_variant=variant, lengths=[1, 3]) < 1e-6
+
+
 # ------------------------------------------------------- variable lengths
 @pytest.mark.parametrize("mode,L,D", list(itertools.product(MODES, (1, 2), (1, 2))))
 def test_packed_matches_torch_nn_float64(mode, L, D):
