@@ -17,6 +17,13 @@
  *    (num_layers*num_directions, batch, hidden); TNC input layout.
  *  - Keras issue #3692 "Exposing Cudnn v5 RNN models": the descriptor
  *    CudnnLSTM(num_layers, num_units, input_size).
+ *  - The GRU flavours of oneDNN issue #218 ("GRU flavours": PyTorch/cuDNN,
+ *    TensorFlow, and the original paper).  The TensorFlow and paper flavours
+ *    need r for every unit before the n product, so their recurrent sweeps
+ *    exchange twice per step and run only as persistent launches: with
+ *    RNN_SCHED_STEPPED, or when the sweep's workgroups cannot all be resident,
+ *    their compute calls return RNN_STATUS_NOT_CORESIDENT.  Layers always
+ *    run one after another (no layer wavefront).
  *
  * General rules for every call
  *  - Every call returns rnn_status_t: 0 on success, a negative code otherwise.
@@ -51,9 +58,13 @@ typedef struct rnn_desc* rnn_handle_t;
 typedef int rnn_status_t;
 
 typedef enum {
-  RNN_TANH = 0, /* h' = tanh(W_ih x + b_ih + W_hh h + b_hh) */
-  RNN_LSTM = 1, /* gates i, f, g, o in this memory order */
-  RNN_GRU = 2   /* gates r, z, n; n = tanh(W_in x + b_in + r*(W_hn h + b_hn)) */
+  RNN_TANH = 0,      /* h' = tanh(W_ih x + b_ih + W_hh h + b_hh) */
+  RNN_LSTM = 1,      /* gates i, f, g, o in this memory order */
+  RNN_GRU = 2,       /* gates r, z, n; n = tanh(W_in x + b_in + r*(W_hn h + b_hn)),
+                        h' = (1-z)*n + z*h (PyTorch / cuDNN flavour) */
+  RNN_GRU_TF = 3,    /* gates r, z, n; n = tanh(W_in x + b_in + W_hn (r*h) + b_hn),
+                        h' = (1-z)*n + z*h (TensorFlow flavour) */
+  RNN_GRU_PAPER = 4  /* as RNN_GRU_TF with h' = (1-z)*h + z*n (original-paper flavour) */
 } rnn_mode_t;
 
 typedef enum { RNN_W_F32 = 0, RNN_W_BF16 = 1 } rnn_wtype_t;

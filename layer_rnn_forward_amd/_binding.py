@@ -8,7 +8,7 @@ import os
 import numpy as np
 import torch
 
-MODES = {"rnn_tanh": 0, "lstm": 1, "gru": 2}
+MODES = {"rnn_tanh": 0, "lstm": 1, "gru": 2, "gru_tf": 3, "gru_paper": 4}
 WTYPES = {"f32": 0, "bf16": 1}
 SCHED_AUTO, SCHED_PERSISTENT, SCHED_STEPPED = 0, 1, 2
 KERNEL_NAMES = ["gemm_input", "recurrent_fwd", "recurrent_bwd", "gemm_dx", "gemm_dw", "fill", "prep",
@@ -84,7 +84,7 @@ class Handle:
         self.ptr = ptr
         self.mode, self.L, self.D = mode, num_layers, num_dirs
         self.I, self.H, self.wtype = input_size, hidden_size, wtype
-        self.G = {"rnn_tanh": 1, "lstm": 4, "gru": 3}[mode]
+        self.G = {"rnn_tanh": 1, "lstm": 4, "gru": 3, "gru_tf": 3, "gru_paper": 3}[mode]
         self.lengths = None
 
     def __del__(self):

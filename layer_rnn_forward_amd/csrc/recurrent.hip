@@ -43,153 +43,12 @@
 #include <type_traits>
 
 #include "device_util.h"
+#include "recurrent_util.h"
 #include "rnn_common.h"
 
 using namespace rnnk;
 
 namespace {
-
-template <bool BF16>
-using XT = typename std::conditional<BF16, uint16_t, float>::type;
-
-template <bool BF16>
-__device__ __forceinline__ XT<BF16> to_x(float v) {
-  if constexpr (BF16) return f2bf(v); else return v;
-}
-template <bool BF16>
-__device__ __forceinline__ uint32_t w_bits(const void* base, size_t idx) {
-  if constexpr (BF16) return reinterpret_cast<const uint16_t*>(base)[idx];
-  else return __float_as_uint(reinterpret_cast<const float*>(base)[idx]);
-}
-// Pack PER values (bits) into a 16-byte fragment.
-template <bool BF16>
-__device__ __forceinline__ uint4 pack_frag(const uint32_t (&v)[BF16 ? 8 : 4]) {
-  if constexpr (BF16)
-    return make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
-  else
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-extern __shared__ __attribute__((aligned(16))) char dyn_lds[];
-
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 lds_load16(const char __attribute__((address_space(3)))* p) {
-  const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)p;
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-template <bool BF16>
-__device__ __forceinline__ void ring_store(char* base, size_t off, float v) {
-  if (v != v) v = __uint_as_float(0x7FC00000u);   // canonical NaN: never the sentinel
-  if constexpr (BF16)
-    __hip_atomic_store(reinterpret_cast<uint16_t*>(base + off), f2bf(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    __hip_atomic_store(reinterpret_cast<float*>(base + off), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Bounded wait of one wave for the flags of two ranges of producers,
-// [a0, a0 + na) and [b0, b0 + nb) (flag indices), to reach `target`.
-// Returns false (uniformly over the wave) if the wait expired -- the error
-// word is then set -- or another workgroup reported an error.
-__device__ bool wave_wait(const unsigned* flags, unsigned* err, unsigned spin_limit, int a0, int na,
-                          int b0, int nb, unsigned target) {
-  const int lane = threadIdx.x & 63;
-  const int total = na + nb;
-  const int nper = (total + 63) / 64;   // flags per lane, uniform
-  unsigned it = 0;
-  while (true) {
-    // issue every flag load of this round before looking at any of them
-    unsigned v[kWaitPerLane];
-#pragma unroll
-    for (int i = 0; i < kWaitPerLane; ++i) {
-      const int idx = lane + 64 * i;
-      v[i] = target;
-      if (i < nper && idx < total) {
-        const int w = idx < na ? a0 + idx : b0 + (idx - na);
-        v[i] = flag_load(flags + (size_t)w * kFlagStride);
-      }
-    }
-    bool mine = true;
-#pragma unroll
-    for (int i = 0; i < kWaitPerLane; ++i) mine = mine && v[i] >= target;
-    if (__all(mine)) return true;
-    if (++it > spin_limit) {
-      flag_store(err, 1u);
-      return false;
-    }
-    if ((it & 31u) == 0 && flag_load(err) != 0u) return false;
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
-
-// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
-// does not wait for the wave's outstanding global loads and stores.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Every wave waits for completion of its stores (the ring stores are agent
-// scope), then one thread publishes the flag.
-__device__ __forceinline__ void publish(unsigned* flags, unsigned v) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) flag_store(flags + (size_t)blockIdx.x * kFlagStride, v);
-}
-
-// MFMA over the granules this wave holds.  K chunk kk takes granules
-// 4*kk + fq of the wave's range (fq = lane / 16): a lane feeds one granule's
-// 16 bytes of row `row` as its A fragment, `load(gl, row)`, and the matching
-// weights sit in wf[kk].  Lanes past the end of the range re-read its last
-// granule (their weights are zero), and tile rows past the granule's padded
-// rows re-read its last row: no load leaves the granules the wave has waited
-// for, and such rows only feed output rows that are never used.  All loads of
-// a batch (at most KBMAX chunks) are issued before its MFMAs.
-template <bool BF16, int NT, int MT, int KPW, int KBMAX = 8, class LoadF>
-__device__ __forceinline__ void mfma_sweep(f32x4 (&acc)[MT][NT], const uint4 (&wf)[KPW][NT], int fr,
-                                           int fq, int nmine, int rmax, LoadF load) {
-  constexpr int KB = KPW < KBMAX ? KPW : KBMAX;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < KPW; kb += KB) {
-    if (kb * 4 >= nmine) break;   // uniform over the wave
-    uint4 av[KB][MT];
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
-      const int gl = min((kb + kk) * 4 + fq, nmine - 1);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) av[kk][mt] = load(gl, min(mt * 16 + fr, rmax));
-    }
-    // keep the whole batch of loads in flight before the first MFMA
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < KB; ++kk)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma_chunk<BF16>(av[kk][mt], wf[kb + kk][nt], acc[mt][nt]);
-  }
-}
-
-// Copy granules [g0, g0 + n) of a ring entry to the same offsets in LDS with
-// direct global->LDS loads (lane i of an instruction moves 16 bytes to
-// M0 + 16*i); nothing passes through registers, so the whole range is in
-// flight at once.  The issuing wave waits for its own loads only.
-__device__ __forceinline__ void stage_granules(char __attribute__((address_space(3)))* lds, const char* src,
-                                               int g0, int n, int gran, int lane) {
-  const int n16 = n * (gran >> 4);
-  const int base = g0 * gran;
-  for (int c = 0; c < n16; c += 64)
-    if (c + lane < n16)
-      __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(src + base + (size_t)(c + lane) * 16),
-          (void __attribute__((address_space(3)))*)(lds + base + c * 16), 16, 0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-}
 
 // ====================================================================== fwd
 template <int MODE, bool BF16, int NT, int MT, int KPW, int NW>
@@ -810,37 +669,6 @@ struct BwdK {
   X(M, false, 1, 2, 64, 4)
 #define RNN_BWD_WIDE_true(X, M)
 
-int max_resident(const void* f, int nthr, size_t lds) {
-  int per_cu = 0;
-  if (lds > 0) {
-    // static + dynamic LDS must fit the per-workgroup limit; failed runtime
-    // calls are cleared so that no error state leaks to the caller
-    int dev = 0, lim = 0;
-    hipFuncAttributes fa{};
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&lim, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-        hipFuncGetAttributes(&fa, f) != hipSuccess) {
-      (void)hipGetLastError();
-      return 0;
-    }
-    if (fa.sharedSizeBytes + lds > (size_t)lim) return 0;
-    if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
-      (void)hipGetLastError();
-      return 0;
-    }
-  }
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, nthr, lds) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  int dev = 0, ncu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  return per_cu * ncu;
-}
 
 }  // namespace
 

@@ -51,8 +51,9 @@ struct SweepPlan {
 
 struct Plan {
   int T = 0, B = 0, training = 0;
-  int fslice = 0, bslice = 0, fgran = 0, bgran = 0;
+  int fslice = 0, bslice = 0, fgran = 0, bgran = 0, bslice2 = 0, bgran2 = 0;
   size_t fring_step = 0, fring_group = 0, bring_step = 0, bring_group = 0;
+  size_t bring_step2 = 0, bring_group2 = 0;
   bool wavefront = false;
   SweepPlan fwd, bwd;
   size_t off_err = 0, off_flags = 0, flags_bytes = 0;
@@ -94,6 +95,10 @@ struct rnn_desc {
 namespace {
 
 int in_width(const rnn_desc* h, int l) { return l == 0 ? h->I : h->D * h->H; }
+// GRU flavours whose n reads (r*h) W_hn (two exchanges per step)
+bool is_gru2(const rnn_desc* h) { return h->mode == RNN_GRU_TF || h->mode == RNN_GRU_PAPER; }
+// the cell type the kernels and the workspace layout see
+int kmode(const rnn_desc* h) { return is_gru2(h) ? RNN_GRU : h->mode; }
 
 void layout_weights(rnn_desc* h) {
   for (int grad = 0; grad < 2; ++grad) {
@@ -147,6 +152,7 @@ bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepP
     // for the fp32 DS2 forward, so the list order, fewer waves first, stands)
     for (const RecConfig& c : kFwdCfgs) {
       if (c.mt != mt) continue;
+      if (is_gru2(h) && !rnn_gru2_fwd_config_supported(h->wtype == RNN_W_BF16, c)) continue;
       if (GB * tryU > 16 * c.nt || Bc * tryU > 64 * c.nwaves) continue;
       if (ceil_div(ceil_div(ngr, c.nwaves), 4) > c.kpw) continue;
       sp->cfg = c;
@@ -167,10 +173,14 @@ bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, SweepPlan* sp) {
   for (int tryU = U; tryU >= Q; tryU -= Q) {
     const int nwg = ceil_div(h->H, tryU);
     const int ngr = h->G * nwg * (tryU / Q);   // K granules
+    // the flavours with two exchanges hold two weight sets: the n gate
+    // (nwg*U/Q granules) and r, z (twice that), each within kpw chunks
+    const int ngr2 = 2 * nwg * (tryU / Q);
     for (const RecConfig& c : kBwdCfgs) {
       if (c.mt != mt || (c.kpw > 32 && h->wtype == RNN_W_BF16)) continue;
+      if (is_gru2(h) && !rnn_gru2_bwd_config_supported(h->wtype == RNN_W_BF16, c)) continue;
       if (tryU > 16 * c.nt || Bc * tryU > 64 * c.nwaves) continue;
-      if (ceil_div(ceil_div(ngr, c.nwaves), 4) > c.kpw) continue;
+      if (ceil_div(ceil_div(is_gru2(h) ? ngr2 : ngr, c.nwaves), 4) > c.kpw) continue;
       sp->cfg = c;
       sp->U = tryU;
       sp->nwg = nwg;
@@ -220,9 +230,11 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   // GPU at once (with LDS staging if it fits, else without)
   auto fit = [&](SweepPlan& sp, bool fwd, size_t stage_bytes) {
     auto res = [&](size_t lds) {
-      return fwd ? rnn_fwd_max_resident(h->mode, bf, sp.cfg, lds)
-                 : rnn_bwd_max_resident(h->mode, bf, sp.cfg, lds);
+      if (is_gru2(h)) return fwd ? rnn_gru2_fwd_max_resident(bf, sp.cfg) : rnn_gru2_bwd_max_resident(bf, sp.cfg);
+      return fwd ? rnn_fwd_max_resident(kmode(h), bf, sp.cfg, lds)
+                 : rnn_bwd_max_resident(kmode(h), bf, sp.cfg, lds);
     };
+    if (is_gru2(h)) stage_bytes = 0;   // their backward reads fragments from the rings
     size_t lds = allow_stage ? stage_bytes : 0;
     int maxres = lds ? res(lds) : 0;
     if (lds && maxres < sp.grid) lds = 0;
@@ -235,7 +247,7 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
 
   // ---- forward sweep: batch chunks of up to 32 rows
   chunk(env_int("RNN_FWD_MAX_BC", 32), p.fwd);
-  p.wavefront = (h->D == 1 && h->L > 1 && h->L <= kMaxLayersPerLaunch &&
+  p.wavefront = (h->D == 1 && h->L > 1 && h->L <= kMaxLayersPerLaunch && !is_gru2(h) &&
                  env_int("RNN_NO_WAVEFRONT", 0) == 0);
   const int fl = p.wavefront ? h->L : 1;
   const int fmt = ceil_div(p.fwd.Bc, 16);
@@ -263,6 +275,7 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   p.fring_group = align_up(p.fring_step * (size_t)(s_total + 1));
   // the forward reads its fragments straight from the ring
   if (!fit(p.fwd, true, 0) && sched == RNN_SCHED_PERSISTENT) p.status = RNN_STATUS_NOT_CORESIDENT;
+  if (is_gru2(h) && !p.fwd.persistent) p.status = RNN_STATUS_NOT_CORESIDENT;
 
   // ---- backward sweep: batch chunks of up to 16 rows (one MFMA row tile,
   // half the exchanged bytes per workgroup) when that many workgroups fit
@@ -273,10 +286,19 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
       if (!plan_bwd(h, ceil_div(p.bwd.Bc, 16), p.bwd.Bc, h->D * p.bwd.nchunk, &p.bwd) ||
           p.bwd.nwg > kMaxWaitFlags)
         return false;
-      p.bgran = padded_rows(p.bwd.Bc, h->G * p.bwd.U / Q) * 16;
-      p.bslice = h->G * (p.bwd.U / Q) * p.bgran;
+      // the flavours with two exchanges: da_n (one gate per slice) in the
+      // first ring, [da_r, da_z] (two gates) in the second
+      const int gpr = is_gru2(h) ? 1 : h->G;
+      p.bgran = padded_rows(p.bwd.Bc, gpr * p.bwd.U / Q) * 16;
+      p.bslice = gpr * (p.bwd.U / Q) * p.bgran;
       p.bring_step = ((size_t)p.bwd.nwg * p.bslice + 1023) / 1024 * 1024;
       p.bring_group = align_up(p.bring_step * (size_t)(T + 1));
+      if (is_gru2(h)) {
+        p.bgran2 = padded_rows(p.bwd.Bc, 2 * p.bwd.U / Q) * 16;
+        p.bslice2 = 2 * (p.bwd.U / Q) * p.bgran2;
+        p.bring_step2 = ((size_t)p.bwd.nwg * p.bslice2 + 1023) / 1024 * 1024;
+        p.bring_group2 = align_up(p.bring_step2 * (size_t)(T + 1));
+      }
       return true;
     };
     const int bmax = std::max(1, std::min(32, env_int("RNN_BWD_MAX_BC", 16)));
@@ -291,6 +313,7 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
       return p;
     }
     if (!fits && sched == RNN_SCHED_PERSISTENT) p.status = RNN_STATUS_NOT_CORESIDENT;
+    if (is_gru2(h) && !p.bwd.persistent) p.status = RNN_STATUS_NOT_CORESIDENT;
   }
 
   const size_t TB = (size_t)T * B;
@@ -302,8 +325,8 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   p.flags_bytes = (size_t)std::max(p.fwd.grid, p.bwd.grid) * kFlagStride * 4;
   off = align_up(off + p.flags_bytes);
   p.off_xch = off;
-  size_t xf = (size_t)p.fwd.groups * p.fring_group;
-  size_t xb = (size_t)p.bwd.groups * p.bring_group;
+  size_t xf = (size_t)p.fwd.groups * p.fring_group * (is_gru2(h) ? 2 : 1);
+  size_t xb = (size_t)p.bwd.groups * (p.bring_group + p.bring_group2);
   p.xch_bytes = std::max(xf, training ? xb : (size_t)0);
   off = align_up(off + p.xch_bytes);
   p.off_st = off;
@@ -325,7 +348,7 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   p.tb_ld = ceil_div((int)std::max<size_t>(TB, 1), 8) * 8;
   size_t scr = bf ? align_up(TB * Ipad * 2) : 0;
   if (training) {
-    const int R = reserve_slots(h->mode);
+    const int R = reserve_slots(kmode(h));
     p.off_res = off;
     p.res_layer = align_up((size_t)h->D * TB * R * h->H * 4);
     off += p.res_layer * h->L;
@@ -343,12 +366,17 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
     // backward_data: W_ih^T [I_l][dg_ld]; backward_weights: X^T, H_prev^T, split-K partials
     scr = std::max(scr, align_up(Ipad * p.dg_ld * es));
     size_t wts = align_up(Ipad * p.tb_ld * es) + align_up((size_t)h->D * h->H * p.tb_ld * es);
+    if (is_gru2(h)) wts += align_up((size_t)h->D * h->H * p.tb_ld * es);   // (r*H_prev)^T
     size_t part = 0;
     for (int l = 0; l < h->L; ++l) {
       const int I_l = in_width(h, l);
       part = std::max(part, (size_t)gemm_split(h, (int)dgh, I_l + 1, (int)TB, 1) * dgh * (I_l + 1) * 4);
       part = std::max(part, (size_t)gemm_split(h, h->G * h->H, h->H + 1, (int)TB, h->D) * h->D *
                                 (size_t)h->G * h->H * (h->H + 1) * 4);
+      if (is_gru2(h))   // their dW_hh in two products, 2H and H rows
+        for (int m = 1; m <= 2; ++m)
+          part = std::max(part, (size_t)gemm_split(h, m * h->H, h->H + 1, (int)TB, h->D) * h->D *
+                                    (size_t)m * h->H * (h->H + 1) * 4);
     }
     scr = std::max(scr, wts + align_up(part));
   }
@@ -495,7 +523,7 @@ rnn_status_t gemm_input(rnn_desc* h, hipStream_t s, const Plan& p, int l, const 
   g.ldc = g.N;
   g.bias1 = reinterpret_cast<const float*>(layer_w(h, W, RNN_B_IH, l));
   g.bias2 = reinterpret_cast<const float*>(layer_w(h, W, RNN_B_HH, l));
-  g.bias2_skip_gate = h->mode == RNN_GRU ? 2 : -1;
+  g.bias2_skip_gate = kmode(h) == RNN_GRU ? 2 : -1;   // b_hn stays inside n
   g.gh = h->G * h->H;
   g.hh = h->H;
   g.split_k = 1;
@@ -569,6 +597,9 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   f.st_h = at<float>(ws, p.off_st);
   f.st_c = at<float>(ws, p.off_st + p.st_bytes / 2);
   f.xch = at<void>(ws, p.off_xch);
+  // the flavours with two exchanges: the r*h ring after the h rings
+  f.xch2 = is_gru2(h) ? at<void>(ws, p.off_xch + (size_t)p.fwd.groups * p.fring_group) : nullptr;
+  f.paper = h->mode == RNN_GRU_PAPER ? 1 : 0;
   f.flags = at<unsigned>(ws, p.off_flags);
   f.err = at<unsigned>(ws, p.off_err);
   f.spin_limit = spin_limit();
@@ -582,8 +613,10 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
       f.s_begin = -1;
       f.s_end = f.s_total;
       ProfScope ps(h, s, K_FWD);
+      if (is_gru2(h)) return dev(rnn_launch_gru2_fwd(f, bf, p.fwd.cfg, grid, s));
       return dev(rnn_launch_fwd(f, h->mode, bf, p.fwd.cfg, grid, p.fwd.lds, s));
     }
+    if (is_gru2(h)) return RNN_STATUS_NOT_CORESIDENT;
     for (int st = -1; st < f.s_total; ++st) {
       f.s_begin = st;
       f.s_end = st + 1;
@@ -676,7 +709,8 @@ rnn_status_t exchange_probe_impl(rnn_desc* h, void* stream, int T, int B, void* 
   const int grid = p.fwd.nwg * f.nlayers * h->D * p.fwd.nchunk;
   RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
   ProfScope ps(h, s, K_PROBE);
-  return dev(rnn_launch_fwd(f, h->mode, h->wtype == RNN_W_BF16, p.fwd.cfg, grid, p.fwd.lds, s));
+  // (the flavours with two exchanges per step probe one of them)
+  return dev(rnn_launch_fwd(f, kmode(h), h->wtype == RNN_W_BF16, p.fwd.cfg, grid, p.fwd.lds, s));
 }
 
 }  // namespace
@@ -688,7 +722,9 @@ rnn_status_t rnn_create(rnn_handle_t* out, rnn_mode_t mode, int num_layers, int 
                         int input_size, int hidden_size, rnn_wtype_t wtype) {
   if (!out) return RNN_STATUS_INVALID_ARG;
   *out = nullptr;
-  if (mode != RNN_TANH && mode != RNN_LSTM && mode != RNN_GRU) return RNN_STATUS_INVALID_ARG;
+  if (mode != RNN_TANH && mode != RNN_LSTM && mode != RNN_GRU && mode != RNN_GRU_TF &&
+      mode != RNN_GRU_PAPER)
+    return RNN_STATUS_INVALID_ARG;
   if (wtype != RNN_W_F32 && wtype != RNN_W_BF16) return RNN_STATUS_INVALID_ARG;
   if (num_layers <= 0 || input_size <= 0 || hidden_size <= 0) return RNN_STATUS_INVALID_ARG;
   if (num_dirs != 1 && num_dirs != 2) return RNN_STATUS_INVALID_ARG;
@@ -700,7 +736,7 @@ rnn_status_t rnn_create(rnn_handle_t* out, rnn_mode_t mode, int num_layers, int 
   h->I = input_size;
   h->H = hidden_size;
   h->wtype = wtype;
-  h->G = gates_of(mode);
+  h->G = gates_of(kmode(h));
   layout_weights(h);
   *out = h;
   return RNN_STATUS_SUCCESS;
@@ -819,6 +855,14 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
   b.st_dh = at<float>(ws, p.off_st);
   b.st_dc = at<float>(ws, p.off_st + p.st_bytes / 2);
   b.xch = at<void>(ws, p.off_xch);
+  if (is_gru2(h)) {   // [da_r, da_z] rings after the da_n rings
+    b.xch2 = at<void>(ws, p.off_xch + (size_t)p.bwd.groups * p.bring_group);
+    b.gran2 = p.bgran2;
+    b.slice2 = p.bslice2;
+    b.ring_step2 = (long long)p.bring_step2;
+    b.ring_group2 = (long long)p.bring_group2;
+  }
+  b.paper = h->mode == RNN_GRU_PAPER ? 1 : 0;
   b.flags = at<unsigned>(ws, p.off_flags);
   b.err = at<unsigned>(ws, p.off_err);
   b.spin_limit = spin_limit();
@@ -843,8 +887,10 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
       b.s_begin = 0;
       b.s_end = T + 1;
       ProfScope ps(h, s, K_BWD);
-      RNN_TRY(dev(rnn_launch_bwd(b, h->mode, bf, p.bwd.cfg, p.bwd.grid, p.bwd.lds, s)));
+      if (is_gru2(h)) RNN_TRY(dev(rnn_launch_gru2_bwd(b, bf, p.bwd.cfg, p.bwd.grid, s)));
+      else RNN_TRY(dev(rnn_launch_bwd(b, h->mode, bf, p.bwd.cfg, p.bwd.grid, p.bwd.lds, s)));
     } else {
+      if (is_gru2(h)) return RNN_STATUS_NOT_CORESIDENT;
       for (int st = 0; st <= T; ++st) {
         b.s_begin = st;
         b.s_end = st + 1;
@@ -921,7 +967,11 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
   char* scr = at<char>(wsm, p.off_scr);
   void* xT = scr;
   char* hT = scr + align_up(Ipad * p.tb_ld * es);
-  float* part = reinterpret_cast<float*>(hT + align_up((size_t)h->D * h->H * p.tb_ld * es));
+  const size_t hT_bytes = align_up((size_t)h->D * h->H * p.tb_ld * es);
+  // (r*H_prev)^T [D][H][T*B] for the flavours whose n reads W_hn (r*h)
+  char* rhT = is_gru2(h) ? hT + hT_bytes : nullptr;
+  float* part = reinterpret_cast<float*>(hT + hT_bytes * (is_gru2(h) ? 2 : 1));
+  const int R = reserve_slots(kmode(h));
   for (int l = 0; l < h->L; ++l) {
     const int I_l = in_width(h, l);
     const float* X = (l == 0) ? x : yl(l - 1);
@@ -956,6 +1006,16 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
           th.len_T = T;
         }
         RNN_TRY(dev(rnn_launch_transpose(th, 0, bf, s)));
+        if (rhT) {   // reserve slot 3 holds r*h_prev of every step
+          TransposeParams tr{};
+          tr.src = at<float>(wsm, p.off_res + p.res_layer * l) + (size_t)d * TB * R * h->H + 3 * (size_t)h->H;
+          tr.ld_src = (long long)R * h->H;
+          tr.out = rhT + (size_t)d * h->H * p.tb_ld * es;
+          tr.ld_out = p.tb_ld;
+          tr.R = (int)TB;
+          tr.C = h->H;
+          RNN_TRY(dev(rnn_launch_transpose(tr, 0, bf, s)));
+        }
       }
     }
     {  // dW_ih | db_ih = dG_i^T [X | 1]
@@ -978,9 +1038,14 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
       gemm_consts(h, g, ws, p.off_err);
       RNN_TRY(dev(rnn_launch_gemm(g, bf, EPI_DW, 1, s)));
     }
-    {  // dW_hh | db_hh = dG_h^T [H_prev | 1], per direction
+    // dW_hh | db_hh = dG_h^T [H_prev | 1], per direction; the flavours
+    // whose n reads W_hn (r*h) take their n rows against (r*H_prev) instead
+    const int parts = rhT ? 2 : 1;
+    for (int part_i = 0; part_i < parts; ++part_i) {
+      const int row0 = part_i == 0 ? 0 : 2 * h->H;
+      const char* Bsrc = part_i == 0 ? hT : rhT;
       GemmParams g{};
-      g.M = GH;
+      g.M = rhT ? (part_i == 0 ? 2 * h->H : h->H) : GH;
       g.N = h->H + 1;
       g.K = (int)TB;
       g.lda = p.tb_ld;
@@ -988,10 +1053,10 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
       g.n_ones = h->H;
       g.ldc = h->H;
       for (int d = 0; d < h->D; ++d) {
-        g.A[d] = dghT + (size_t)d * GH * p.tb_ld * es;
-        g.B[d] = hT + (size_t)d * h->H * p.tb_ld * es;
-        g.C[d] = reinterpret_cast<float*>(dWb + h->off[1][RNN_W_HH][l]) + (size_t)d * GH * h->H;
-        g.cbias[d] = reinterpret_cast<float*>(dWb + h->off[1][RNN_B_HH][l]) + (size_t)d * GH;
+        g.A[d] = dghT + ((size_t)d * GH + row0) * p.tb_ld * es;
+        g.B[d] = Bsrc + (size_t)d * h->H * p.tb_ld * es;
+        g.C[d] = reinterpret_cast<float*>(dWb + h->off[1][RNN_W_HH][l]) + ((size_t)d * GH + row0) * h->H;
+        g.cbias[d] = reinterpret_cast<float*>(dWb + h->off[1][RNN_B_HH][l]) + (size_t)d * GH + row0;
       }
       g.a_vec = g.b_vec = 1;
       g.split_k = gemm_split(h, g.M, g.N, g.K, h->D);

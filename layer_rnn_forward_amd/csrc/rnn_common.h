@@ -96,6 +96,8 @@ struct FwdParams {
   int persistent, training, wavefront;
   int probe;              // 1: exchange only (waits, ring stores, flags); no weights, math or outputs
   const int* lengths;     // [B] valid steps per row (clamped to [0, T]), or null: all T
+  void* xch2;             // GRU with (r*h) W_hn: rings of r*h, laid out as xch
+  int paper;              // GRU with (r*h) W_hn: 1 for h = (1-z) h_prev + z n
   int first_layer;        // index of layer 0 of this launch in the network
   const void* w_ih[kMaxLayersPerLaunch];   // layer block [D*G*H, I_l]
   const void* w_hh[kMaxLayersPerLaunch];   // layer block [D*G*H, H]
@@ -128,6 +130,12 @@ struct BwdParams {
   int s_begin, s_end;     // processing steps; s == T is the final dh0 phase
   int persistent;
   const int* lengths;     // [B] valid steps per row (clamped to [0, T]), or null: all T
+  // GRU with (r*h) W_hn: xch carries da_n (one gate per slice, gran/slice
+  // above) and xch2 carries [da_r, da_z] (two gates per slice)
+  void* xch2;
+  int gran2, slice2;
+  long long ring_step2, ring_group2;
+  int paper;
   const void* w_hh;       // layer block [D*G*H, H]
   const float* reserve;   // [D][T][B][R][H]
   const float* y;         // layer output [T, B, D*H]
@@ -178,6 +186,15 @@ hipError_t rnn_launch_fill(void* const* ptrs, const size_t* bytes, const uint32_
 hipError_t rnn_copy_state(float* dst, const float* src, size_t n, hipStream_t s);
 // Maximum co-resident workgroups of the fwd/bwd kernel for this config (0 if unsupported).
 int rnn_fwd_max_resident(int mode, int bf16, const RecConfig& c, size_t lds);
+// GRU flavours whose n reads (r*h) W_hn: two exchanges per step, persistent only.
+hipError_t rnn_launch_gru2_fwd(const rnnk::FwdParams& p, int bf16, const RecConfig& c, int grid,
+                               hipStream_t s);
+hipError_t rnn_launch_gru2_bwd(const rnnk::BwdParams& p, int bf16, const RecConfig& c, int grid,
+                               hipStream_t s);
+int rnn_gru2_fwd_max_resident(int bf16, const RecConfig& c);
+int rnn_gru2_bwd_max_resident(int bf16, const RecConfig& c);
+bool rnn_gru2_fwd_config_supported(int bf16, const RecConfig& c);
+bool rnn_gru2_bwd_config_supported(int bf16, const RecConfig& c);
 int rnn_bwd_max_resident(int mode, int bf16, const RecConfig& c, size_t lds);
 bool rnn_fwd_config_supported(int mode, int bf16, const RecConfig& c);
 bool rnn_bwd_config_supported(int mode, int bf16, const RecConfig& c);

@@ -24,7 +24,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-GATES = {"rnn_tanh": 1, "lstm": 4, "gru": 3}
+GATES = {"rnn_tanh": 1, "lstm": 4, "gru": 3, "gru_tf": 3, "gru_paper": 3}
 
 
 @dataclass(frozen=True)

@@ -77,11 +77,17 @@ def run_gpu(mode, L, D, case, wtype="f32", sched=R.SCHED_AUTO, training=True, ba
     return out
 
 
+# library modes that are oracle GRU flavours
+GRU_FLAVOURS = {"gru_tf": "tf", "gru_paper": "paper"}
+
+
 def run_oracle(mode, L, D, case, backward=True, pass_state=True, pass_grads=True, lengths=None):
+    variant = GRU_FLAVOURS.get(mode, "pytorch")
+    mode = "gru" if mode in GRU_FLAVOURS else mode
     h0 = case["h0"] if pass_state else None
     c0 = case["c0"] if (pass_state and mode == "lstm") else None
     y, hy, cy, cache = orc.forward(mode, case["x"], case["params"], h0=h0, c0=c0, num_dirs=D,
-                                   keep=backward, lengths=lengths)
+                                   gru_variant=variant, keep=backward, lengths=lengths)
     out = {"y": y, "hy": hy}
     if mode == "lstm":
         out["cy"] = cy

@@ -53,7 +53,8 @@ def test_create_rejects_bad_descriptors(R, args):
     assert e.value.status == -1
 
 
-@pytest.mark.parametrize("mode,G", [("rnn_tanh", 1), ("lstm", 4), ("gru", 3)])
+@pytest.mark.parametrize("mode,G", [("rnn_tanh", 1), ("lstm", 4), ("gru", 3), ("gru_tf", 3),
+                                    ("gru_paper", 3)])
 @pytest.mark.parametrize("wtype,es", [("f32", 4), ("bf16", 2)])
 def test_weight_layout(R, mode, G, wtype, es):
     L, D, I, H = 3, 2, 13, 7
@@ -84,7 +85,7 @@ def test_weight_layout(R, mode, G, wtype, es):
 
 
 def test_workspace_size_properties(R):
-    for mode in ("rnn_tanh", "lstm", "gru"):
+    for mode in ("rnn_tanh", "lstm", "gru", "gru_tf", "gru_paper"):
         for wtype in ("f32", "bf16"):
             h = R.rnn_create(mode, 2, 2, 800, 800, wtype)
             inf = R.rnn_workspace_size(h, 300, 20, 0)
