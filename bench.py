@@ -29,7 +29,7 @@ HBM_GBS = 8000.0
 
 
 def flops(mode, T, B, I, H, L, D):
-    G = {"rnn_tanh": 1, "lstm": 4, "gru": 3}[mode]
+    G = {"rnn_tanh": 1, "lstm": 4, "gru": 3, "gru_tf": 3, "gru_paper": 3}[mode]
     f = 0
     for l in range(L):
         I_l = I if l == 0 else D * H
@@ -102,12 +102,15 @@ def cpu_baseline(w, synth, min_seconds):
     from oracle import rnn_oracle as orc
     case = synth.make_workload(w)
     D = w.dirs
+    # the library's GRU flavour modes are oracle GRU variants
+    variant = {"gru_tf": "tf", "gru_paper": "paper"}.get(w.mode, "pytorch")
+    mode = "gru" if variant != "pytorch" else w.mode
     reps, dt = 0, 0.0
     while reps == 0 or dt < min_seconds:
         t0 = time.perf_counter()
-        _, _, _, cache = orc.forward(w.mode, case["x"], case["params"], h0=case["h0"],
-                                     c0=case["c0"], num_dirs=D, keep=True)
-        orc.backward(w.mode, case["params"], cache, case["dy"], num_dirs=D)
+        _, _, _, cache = orc.forward(mode, case["x"], case["params"], h0=case["h0"],
+                                     c0=case["c0"], num_dirs=D, gru_variant=variant, keep=True)
+        orc.backward(mode, case["params"], cache, case["dy"], num_dirs=D)
         dt += time.perf_counter() - t0
         reps += 1
     f = reps * 3 * flops(w.mode, w.T, w.B, w.input_size, w.hidden, w.layers, D)
@@ -221,7 +224,7 @@ def main():
     peak = PEAK_TFLOPS[w.wtype]
     # dominant kernel: the one with the largest total time
     dom = max(kern.items(), key=lambda kv: kv[1]["total_ms"])
-    G = {"rnn_tanh": 1, "lstm": 4, "gru": 3}[w.mode]
+    G = {"rnn_tanh": 1, "lstm": 4, "gru": 3, "gru_tf": 3, "gru_paper": 3}[w.mode]
     per_launch_flops = {
         "recurrent_fwd": 2.0 * w.T * w.B * G * w.hidden * w.hidden * w.dirs,
         "recurrent_bwd": 2.0 * w.T * w.B * G * w.hidden * w.hidden * w.dirs,

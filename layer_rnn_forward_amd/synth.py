@@ -58,6 +58,11 @@ WORKLOADS = {
     "gru_ds2_l5_bi_bf16": _w("gru_ds2_l5_bi_bf16", "gru", 5, 2, 300, 20, 800, 800, "bf16", 0.0, 5),
     "tanh_ds2_l5_bi_bf16": _w("tanh_ds2_l5_bi_bf16", "rnn_tanh", 5, 2, 300, 20, 800, 800, "bf16", 0.0, 5),
     "lstm_ds2_l5_uni_bf16": _w("lstm_ds2_l5_uni_bf16", "lstm", 5, 1, 300, 20, 800, 800, "bf16", 0.0, 6),
+    # the GRU flavours at the same shape (two exchanges per step)
+    "gru_ds2_bf16": _w("gru_ds2_bf16", "gru", 1, 1, 300, 20, 800, 800, "bf16", 0.1, 3),
+    "gru_tf_ds2_bf16": _w("gru_tf_ds2_bf16", "gru_tf", 1, 1, 300, 20, 800, 800, "bf16", 0.1, 7),
+    "gru_tf_ds2_f32": _w("gru_tf_ds2_f32", "gru_tf", 1, 1, 300, 20, 800, 800, "f32", 0.1, 7),
+    "gru_paper_ds2_bf16": _w("gru_paper_ds2_bf16", "gru_paper", 1, 1, 300, 20, 800, 800, "bf16", 0.1, 8),
 }
 
 
