@@ -57,6 +57,17 @@ In the backward pass such a step passes ``dh`` (and ``dc``) through
 unchanged, ignores ``dy`` there, and contributes nothing to ``dx``, ``dW``
 or ``db``.
 
+Inter-layer dropout (the MKL-DNN issue thread asks whether dropout will
+come as cuDNN has it; the pages fix no semantics, so the plainest reading,
+cuDNN's and PyTorch's, is taken): in training, the input of every layer ``l >= 1`` is
+``y_{l-1} * m_l`` with ``m_l = keep_l / (1 - p)`` (inverted dropout: kept
+elements are scaled so the expectation is unchanged; ``m_l = 0`` for
+``p = 1``); ``x`` itself, the recurrent state and the top layer's ``y`` are
+never dropped.  The keep mask is drawn from Philox4x32-10
+(:mod:`oracle.philox`) -- see :func:`dropout_multiplier`.  The backward pass
+multiplies the gradient reaching ``y_{l-1}`` by the same ``m_l``, and
+``dW_ih`` of layer ``l`` uses the dropped input.
+
 Backward (the pages only say forward results are reused by the backward
 pass, MXNet page "Operator Registration"; the chain rule below is derived by
 hand and pinned by central finite differences): see :func:`backward`.
@@ -64,7 +75,11 @@ hand and pinned by central finite differences): see :func:`backward`.
 
 from __future__ import annotations
 
+import math
+
 import numpy as np
+
+from oracle.philox import philox4x32_array
 
 MODES = ("rnn_tanh", "lstm", "gru")
 GATES = {"rnn_tanh": 1, "lstm": 4, "gru": 3}
@@ -150,8 +165,43 @@ def _valid_rows(lengths, t, B):
     return (t < np.asarray(lengths))[:, None]
 
 
+def dropout_threshold(p):
+    """Integer threshold of drop probability ``p``: an element is dropped
+    when its 32-bit random word is below ``floor(p * 2**32)`` (exact in
+    fp64: a power-of-two scaling), so ``p = 0`` drops nothing and ``p = 1``
+    drops everything."""
+    if not 0.0 <= p <= 1.0:
+        raise ValueError(f"dropout probability {p} outside [0, 1]")
+    return math.floor(p * 4294967296.0)
+
+
+def dropout_keep(p, seed, layer, shape):
+    """Keep mask (bool, ``shape`` = ``[T, B, C]``) of the input of layer
+    ``layer`` in a training pass with seed ``seed`` (below 2**64).
+
+    Element ``e`` (row-major flat index) takes word ``e mod 4`` of
+    Philox4x32-10 applied to the counter ``(q mod 2**32, q div 2**32, layer,
+    0)``, ``q = e div 4``, under the key ``(seed mod 2**32, seed div
+    2**32)``; it is kept when that word is at least
+    :func:`dropout_threshold`."""
+    n = int(np.prod(shape))
+    e = np.arange(n, dtype=np.uint64)
+    q = e >> np.uint64(2)
+    words = philox4x32_array(q & np.uint64(0xFFFFFFFF), q >> np.uint64(32),
+                             np.full(n, layer, dtype=np.uint64), np.zeros(n, dtype=np.uint64),
+                             seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
+    w = np.stack(words, axis=0)[(e & np.uint64(3)).astype(np.int64), np.arange(n)]
+    return (w.astype(np.int64) >= dropout_threshold(p)).reshape(shape)
+
+
+def dropout_multiplier(p, seed, layer, shape):
+    """``keep / (1 - p)`` (0 where dropped; all 0 for ``p = 1``)."""
+    k = dropout_keep(p, seed, layer, shape)
+    return np.where(k, 1.0 / (1.0 - p) if p < 1.0 else 0.0, 0.0)
+
+
 def forward(mode, x, params, h0=None, c0=None, num_dirs=1, gru_variant="pytorch",
-            keep=False, lengths=None):
+            keep=False, lengths=None, dropout=0.0, dropout_seed=0):
     """Stacked, optionally bidirectional forward pass in fp64.
 
     ``x`` ``[T, B, I]`` (TNC, the layout named in the oneDNN issue's
@@ -163,7 +213,9 @@ def forward(mode, x, params, h0=None, c0=None, num_dirs=1, gru_variant="pytorch"
     ``keep``, the per-step intermediates the backward pass reuses (the MXNet
     page's "reserved workspace"), else ``None``.  ``lengths`` (``[B]`` ints
     in ``[0, T]``, or ``None`` for all ``T``) gives each row's number of
-    valid steps (module docstring).
+    valid steps (module docstring).  ``dropout`` > 0 makes this a training
+    pass with inter-layer dropout of that probability, masks from
+    ``dropout_seed`` (module docstring).
     """
     x = np.asarray(x, dtype=np.float64)
     T, B, I = x.shape
@@ -181,11 +233,16 @@ def forward(mode, x, params, h0=None, c0=None, num_dirs=1, gru_variant="pytorch"
     if lengths is not None:
         lengths = np.asarray(lengths, dtype=np.int64)
         assert lengths.shape == (B,) and np.all((lengths >= 0) & (lengths <= T)), lengths
-    cache = ({"layer_inputs": [], "steps": {}, "gru_variant": gru_variant, "lengths": lengths}
-             if keep else None)
+    cache = ({"layer_inputs": [], "steps": {}, "gru_variant": gru_variant, "lengths": lengths,
+              "dropout": {}} if keep else None)
 
     layer_in = x
     for l in range(L):
+        if l > 0 and dropout > 0.0:
+            m = dropout_multiplier(dropout, dropout_seed, l, layer_in.shape)
+            layer_in = layer_in * m
+            if keep:
+                cache["dropout"][l] = m
         if keep:
             cache["layer_inputs"].append(layer_in)
         y_l = np.zeros((T, B, D * H))
@@ -346,7 +403,8 @@ def backward(mode, params, cache, dy, dhy=None, dcy=None, num_dirs=1):
             if mode == "lstm":
                 dc0[l * D + d] = dc
             dparams[l][d] = g
-        dY = dX
+        # the gradient of y_{l-1} passes the same dropout multiplier
+        dY = dX * cache["dropout"][l] if l in cache["dropout"] else dX
     return dY, dh0, dc0, dparams
 
 

@@ -236,10 +236,70 @@ def check_against_torch(orc, mode, L, D, T=4, B=3, I=5, H=6, seed=11, lengths=No
     return max(errs)
 
 
+def check_dropout_against_torch(orc, mode, L, D, p, seed, T=4, B=3, I=5, H=6, case_seed=23):
+    """Normwise error of the oracle's training pass with inter-layer dropout
+    against a composition of one-layer ``torch.nn`` modules (float64, CPU):
+    layer ``l``'s input is the previous module's output times
+    ``keep_l / (1 - p)``, with ``keep_l`` from ``orc.dropout_keep`` and the
+    scaling done here; torch's autograd supplies every gradient."""
+    case = rand_case(mode, L, D, T, B, I, H, case_seed)
+    params = case["params"]
+    x = torch.from_numpy(case["x"]).requires_grad_(True)
+    h0 = torch.from_numpy(case["h0"]).requires_grad_(True)
+    c0 = torch.from_numpy(case["c0"]).requires_grad_(True) if mode == "lstm" else None
+    mods, hns, cns = [], [], []
+    inp = x
+    for l in range(L):
+        I_l = I if l == 0 else D * H
+        m = _torch_module(mode, I_l, H, 1, D)
+        with torch.no_grad():
+            for d in range(D):
+                sfx = "l0" + ("_reverse" if d == 1 else "")
+                for name, tname in (("w_ih", "weight_ih_"), ("w_hh", "weight_hh_"),
+                                    ("b_ih", "bias_ih_"), ("b_hh", "bias_hh_")):
+                    getattr(m, tname + sfx).copy_(torch.from_numpy(params[l][d][name]))
+        if l > 0:
+            keep = orc.dropout_keep(p, seed, l, tuple(inp.shape))
+            scale = 1.0 / (1.0 - p) if p < 1.0 else 0.0
+            inp = inp * torch.from_numpy(np.where(keep, scale, 0.0))
+        if mode == "lstm":
+            inp, (hn, cn) = m(inp, (h0[l * D:(l + 1) * D], c0[l * D:(l + 1) * D]))
+            cns.append(cn)
+        else:
+            inp, hn = m(inp, h0[l * D:(l + 1) * D])
+        hns.append(hn)
+        mods.append(m)
+    hn = torch.cat(hns, 0)
+    loss = (inp * torch.from_numpy(case["dy"])).sum() + (hn * torch.from_numpy(case["dhy"])).sum()
+    if mode == "lstm":
+        cn = torch.cat(cns, 0)
+        loss = loss + (cn * torch.from_numpy(case["dcy"])).sum()
+    loss.backward()
+
+    y, hy, cy, cache = orc.forward(mode, case["x"], params, h0=case["h0"], c0=case["c0"],
+                                   num_dirs=D, keep=True, dropout=p, dropout_seed=seed)
+    errs = [normwise(y, inp.detach().numpy()), normwise(hy, hn.detach().numpy())]
+    if mode == "lstm":
+        errs.append(normwise(cy, cn.detach().numpy()))
+    dx, dh0, dc0, dparams = orc.backward(mode, params, cache, case["dy"], dhy=case["dhy"],
+                                         dcy=case["dcy"], num_dirs=D)
+    errs += [normwise(dx, x.grad.numpy()), normwise(dh0, h0.grad.numpy())]
+    if mode == "lstm":
+        errs.append(normwise(dc0, c0.grad.numpy()))
+    for l in range(L):
+        for d in range(D):
+            sfx = "l0" + ("_reverse" if d == 1 else "")
+            for name, tname in (("w_ih", "weight_ih_"), ("w_hh", "weight_hh_"),
+                                ("b_ih", "bias_ih_"), ("b_hh", "bias_hh_")):
+                errs.append(normwise(dparams[l][d][name], getattr(mods[l], tname + sfx).grad.numpy()))
+    return max(errs)
+
+
 # --------------------------------------------------------- finite differences
-def _loss(orc, mode, case, D, lengths=None, gru_variant="pytorch"):
+def _loss(orc, mode, case, D, lengths=None, gru_variant="pytorch", dropout=0.0, dropout_seed=0):
     y, hy, cy, _ = orc.forward(mode, case["x"], case["params"], h0=case["h0"], c0=case["c0"],
-                               num_dirs=D, lengths=lengths, gru_variant=gru_variant)
+                               num_dirs=D, lengths=lengths, gru_variant=gru_variant,
+                               dropout=dropout, dropout_seed=dropout_seed)
     v = float(np.sum(y * case["dy"]) + np.sum(hy * case["dhy"]))
     if mode == "lstm":
         v += float(np.sum(cy * case["dcy"]))
@@ -247,13 +307,14 @@ def _loss(orc, mode, case, D, lengths=None, gru_variant="pytorch"):
 
 
 def check_finite_differences(orc, mode, L, D, T=3, B=2, I=3, H=4, seed=5, eps=1e-6,
-                             lengths=None, gru_variant="pytorch"):
+                             lengths=None, gru_variant="pytorch", dropout=0.0, dropout_seed=0):
     """Worst normwise error of every analytic gradient against central
     differences of the scalar loss ``sum(y*dy) + sum(hy*dhy) + sum(cy*dcy)``
     (optionally with per-row sequence lengths, or another GRU flavour)."""
     case = rand_case(mode, L, D, T, B, I, H, seed)
     _, _, _, cache = orc.forward(mode, case["x"], case["params"], h0=case["h0"], c0=case["c0"],
-                                 num_dirs=D, keep=True, lengths=lengths, gru_variant=gru_variant)
+                                 num_dirs=D, keep=True, lengths=lengths, gru_variant=gru_variant,
+                                 dropout=dropout, dropout_seed=dropout_seed)
     dx, dh0, dc0, dparams = orc.backward(mode, case["params"], cache, case["dy"],
                                          dhy=case["dhy"], dcy=case["dcy"], num_dirs=D)
 
@@ -264,9 +325,9 @@ def check_finite_differences(orc, mode, L, D, T=3, B=2, I=3, H=4, seed=5, eps=1e
             idx = it.multi_index
             old = arr[idx]
             arr[idx] = old + eps
-            lp = _loss(orc, mode, case, D, lengths, gru_variant)
+            lp = _loss(orc, mode, case, D, lengths, gru_variant, dropout, dropout_seed)
             arr[idx] = old - eps
-            lm = _loss(orc, mode, case, D, lengths, gru_variant)
+            lm = _loss(orc, mode, case, D, lengths, gru_variant, dropout, dropout_seed)
             arr[idx] = old
             g[idx] = (lp - lm) / (2 * eps)
         return g
@@ -324,3 +385,71 @@ def check_packed_truncation(orc, mode, L, D, lengths, T=5, I=3, H=4, seed=17):
             for k in acc[l][d]:
                 errs.append(normwise(dp[l][d][k], acc[l][d][k]))
     return max(errs)
+
+
+# ---------------------------------------------------------------- dropout
+# Random123 known-answer vectors of Philox4x32-10 and Philox4x64-10:
+# (counter words, key words, output words)
+PHILOX_KAT32 = [
+    ((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+    ((0xFFFFFFFF,) * 4, (0xFFFFFFFF,) * 2, (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+]
+PHILOX_KAT64 = [((0, 0, 0, 0), (0, 0),
+                 (0x16554D9ECA36314C, 0xDB20FE9D672D0FDC, 0xD7E772CEE186176B, 0x7E68B68AEC7BA23B))]
+
+
+def philox_kat_failures(px):
+    """Known-answer vectors missed by the scalar and the array generator."""
+    bad = []
+    for ctr, key, out in PHILOX_KAT32:
+        if tuple(px.philox4(ctr, key, 32)) != out:
+            bad.append(("scalar32", ctr))
+        arr = px.philox4x32_array(*[np.array([c]) for c in ctr], *key)
+        if tuple(int(a[0]) for a in arr) != out:
+            bad.append(("array32", ctr))
+    for ctr, key, out in PHILOX_KAT64:
+        if tuple(px.philox4(ctr, key, 64)) != out:
+            bad.append(("scalar64", ctr))
+    return bad
+
+
+def dropout_mask_failures(orc, px):
+    """Properties of ``orc.dropout_keep`` that do not restate its code:
+    keep fraction within 6 sigma of 1 - p, a different mask per layer and
+    per seed (both seed words), dependence on the flat index only, nesting
+    in p, the p = 0 / p = 1 ends, and single elements against the scalar
+    generator ``px.philox4``."""
+    bad = []
+    for p in (0.1, 0.5, 0.9):
+        k = orc.dropout_keep(p, 2024, 1, (50, 20, 64))
+        if abs(k.sum() - k.size * (1 - p)) >= 6 * np.sqrt(k.size * p * (1 - p)):
+            bad.append(("fraction", p))
+    shape = (6, 5, 40)
+    a = orc.dropout_keep(0.5, 99, 1, shape)
+    if np.array_equal(a, orc.dropout_keep(0.5, 99, 2, shape)):
+        bad.append("layer")
+    if np.array_equal(a, orc.dropout_keep(0.5, 100, 1, shape)):
+        bad.append("seed")
+    if np.array_equal(a, orc.dropout_keep(0.5, 99 + (1 << 32), 1, shape)):
+        bad.append("seed-high")
+    if not np.array_equal(a.ravel(), orc.dropout_keep(0.5, 99, 1, (a.size, 1, 1)).ravel()):
+        bad.append("flat")
+    lo, hi = orc.dropout_keep(0.3, 99, 1, shape), orc.dropout_keep(0.6, 99, 1, shape)
+    if not np.all(lo[hi]):
+        bad.append("nested")
+    if not orc.dropout_keep(0.0, 99, 1, shape).all() or orc.dropout_keep(1.0, 99, 1, shape).any():
+        bad.append("ends")
+    # element e = 4q + w takes word w at counter (q mod 2^32, q div 2^32, layer, 0)
+    shape, p, layer = (7, 3, 10), 0.37, 2
+    seed = (0xA5A5A5A5 << 32) | 0x01020304
+    k = orc.dropout_keep(p, seed, layer, shape).ravel()
+    thr = orc.dropout_threshold(p)
+    for e in (0, 1, 2, 3, 4, 77, 150, k.size - 1):
+        q, w = divmod(e, 4)
+        word = px.philox4((q & 0xFFFFFFFF, q >> 32, layer, 0),
+                          (seed & 0xFFFFFFFF, seed >> 32), 32)[w]
+        if bool(k[e]) != (word >= thr):
+            bad.append(("element", e))
+    return bad

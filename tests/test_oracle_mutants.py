@@ -14,8 +14,9 @@ import pytest
 
 from tests import oracle_checks as oc
 
-SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                   "oracle", "rnn_oracle.py")
+ORACLE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+SRC = os.path.join(ORACLE_DIR, "rnn_oracle.py")
+PHILOX_SRC = os.path.join(ORACLE_DIR, "philox.py")
 
 # (id, original text, mutated text, modes whose checks must catch it)
 MUTANTS = [
@@ -66,11 +67,44 @@ MUTANTS = [
      ["gru"]),
     ("packed_bwd_no_passthrough", "direct = np.where(valid, direct, dh_carried)",
      "direct = np.where(valid, direct, 0.0)", ["rnn_tanh"]),
+    ("dropout_not_scaled", "np.where(k, 1.0 / (1.0 - p) if p < 1.0 else 0.0, 0.0)",
+     "np.where(k, 1.0, 0.0)", ["dropout"]),
+    ("dropout_bwd_unmasked", 'dY = dX * cache["dropout"][l] if l in cache["dropout"] else dX',
+     "dY = dX", ["dropout"]),
+    ("dropout_drops_x", "if l > 0 and dropout > 0.0:", "if dropout > 0.0:", ["dropout"]),
+    ("dropout_dW_ih_undropped_input",
+     "            layer_in = layer_in * m\n            if keep:\n                cache[\"dropout\"][l] = m\n"
+     "        if keep:\n            cache[\"layer_inputs\"].append(layer_in)\n",
+     "            if keep:\n                cache[\"layer_inputs\"].append(layer_in)\n"
+     "            layer_in = layer_in * m\n            if keep:\n                cache[\"dropout\"][l] = m\n"
+     "        elif keep:\n            cache[\"layer_inputs\"].append(layer_in)\n", ["dropout"]),
+    ("dropout_layer_not_in_counter", "np.full(n, layer, dtype=np.uint64)",
+     "np.zeros(n, dtype=np.uint64)", ["dropout"]),
+    ("dropout_keep_inverted", "w.astype(np.int64) >= dropout_threshold(p)",
+     "w.astype(np.int64) < dropout_threshold(p)", ["dropout"]),
+    ("dropout_word_order", "(e & np.uint64(3)).astype(np.int64)",
+     "(np.uint64(3) - (e & np.uint64(3))).astype(np.int64)", ["dropout"]),
+    ("dropout_seed_high_word_ignored", "seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)",
+     "seed & 0xFFFFFFFF, 0)", ["dropout"]),
+]
+
+# mistakes planted in the Philox generator (the known-answer vectors catch them)
+PHILOX_MUTANTS = [
+    ("philox_weyl_swapped", "k0, k1 = (k0 + w0) & mask, (k1 + w1) & mask",
+     "k0, k1 = (k0 + w1) & mask, (k1 + w0) & mask"),
+    ("philox_first_round_bumped", "        if r > 0:\n            k0, k1 = (k0 + w0) & mask",
+     "        if r >= 0:\n            k0, k1 = (k0 + w0) & mask"),
+    ("philox_words_permuted", "x = [(p1 >> bits) ^ x[1] ^ k0, p1 & mask, (p0 >> bits) ^ x[3] ^ k1, p0 & mask]",
+     "x = [(p0 >> bits) ^ x[1] ^ k0, p0 & mask, (p1 >> bits) ^ x[3] ^ k1, p1 & mask]"),
+    ("philox_array_lo_hi", "x = [(p1 >> u64(32)) ^ x[1] ^ u64(k0), p1 & lo32,",
+     "x = [(p1 & lo32) ^ x[1] ^ u64(k0), p1 >> u64(32),"),
+    ("philox_array_nine_rounds", "def philox4x32_array(c0, c1, c2, c3, k0, k1, rounds=10):",
+     "def philox4x32_array(c0, c1, c2, c3, k0, k1, rounds=9):"),
 ]
 
 
-def _load_mutant(orig, new):
-    src = open(SRC).read()
+def _load_mutant(orig, new, path=SRC):
+    src = open(path).read()
     assert src.count(orig) == 1, f"mutation anchor not unique/found: {orig!r}"
     mod = types.ModuleType("oracle_mutant")
     exec(compile(src.replace(orig, new), "oracle_mutant", "exec"), mod.__dict__)
@@ -82,6 +116,13 @@ def _pins_fail(mod, modes):
               lambda: oc.check_closed_forms(mod) > 1e-11,
               lambda: oc.check_bptt_closed_forms(mod) > 1e-12]
     for mode in modes:
+        if mode == "dropout":
+            from oracle import philox as px
+            checks.append(lambda: bool(oc.dropout_mask_failures(mod, px)))
+            for m, L, D in (("lstm", 3, 2), ("gru", 2, 1)):
+                checks.append(lambda m=m, L=L, D=D:
+                              oc.check_dropout_against_torch(mod, m, L, D, 0.3, seed=77) > 1e-11)
+            continue
         if mode.startswith("gru_"):   # another GRU flavour: finite differences only
             v = mode[4:]
             checks.append(lambda v=v: oc.check_finite_differences(mod, "gru", 1, 2, T=3, B=2, I=3, H=2,
@@ -107,6 +148,18 @@ def test_planted_mistake_is_caught(name, orig, new, modes):
     assert _pins_fail(_load_mutant(orig, new), modes), f"mutant {name} survived the pins"
 
 
+@pytest.mark.parametrize("name,orig,new", PHILOX_MUTANTS, ids=[m[0] for m in PHILOX_MUTANTS])
+def test_planted_philox_mistake_is_caught(name, orig, new):
+    mod = _load_mutant(orig, new, PHILOX_SRC)
+    try:
+        assert oc.philox_kat_failures(mod), f"mutant {name} survived the known answers"
+    except AssertionError:
+        raise
+    except Exception:
+        pass   # a crash is also a detected mistake
+
+
 def test_unmodified_copy_passes():
     mod = _load_mutant("MODES = (", "MODES = (")
-    assert not _pins_fail(mod, ["lstm", "gru", "rnn_tanh"])
+    assert not _pins_fail(mod, ["lstm", "gru", "rnn_tanh", "dropout"])
+    assert not oc.philox_kat_failures(_load_mutant("CONSTANTS = {", "CONSTANTS = {", PHILOX_SRC))
