@@ -124,6 +124,33 @@ rnn_status_t rnn_set_schedule(rnn_handle_t h, rnn_schedule_t s);
  * Errors: INVALID_ARG for a NULL handle. */
 rnn_status_t rnn_set_sequence_lengths(rnn_handle_t h, const int* lengths);
 
+/* Inter-layer dropout in training (the MKL-DNN issue thread on the "fused
+ * RNN" pages asks for it as cuDNN offers it; the pages fix no semantics, so
+ * cuDNN's and PyTorch's are taken).  In rnn_forward_training the input of
+ * every layer l >= 1 is y_{l-1} * keep / (1 - p); x, the recurrent state and
+ * the top layer's y are never dropped, and rnn_forward_inference never drops.
+ * The backward calls apply the same multiplier to the gradient of y_{l-1}
+ * and use the dropped input for dW_ih, with the p and seed of the forward
+ * they follow.  The keep mask is not stored: element e of layer l's
+ * [T][B][D*H] input is kept when word (e mod 4) of Philox4x32-10 (Salmon et
+ * al., "Parallel random numbers: as easy as 1, 2, 3", SC'11) at counter
+ * (e div 4 mod 2^32, e div 4 div 2^32, l, 0) under the key (seed mod 2^32,
+ * seed div 2^32) is at least floor(p * 2^32); p = 1 drops everything.  A
+ * different seed per training step gives fresh masks.  p > 0 enlarges the
+ * training workspace (one fp32 [T][B][D*H] slot per dropped layer), so size
+ * it after this call.  Errors: INVALID_ARG for a NULL handle or p outside
+ * [0, 1] (or NaN).  Default p = 0. */
+rnn_status_t rnn_set_dropout(rnn_handle_t h, double p, unsigned long long seed);
+
+/* The keep mask a training pass with the current dropout setting applies to
+ * layer `layer`'s input (1 <= layer < num_layers): T*B*num_dirs*hidden_size
+ * bytes at the DEVICE pointer `mask`, 1 = kept, 0 = dropped, TNC order,
+ * written on `stream`.  Errors: INVALID_ARG for a NULL handle, a layer out of
+ * range, negative sizes or a NULL mask with a non-empty shape; DEVICE for a
+ * failed launch. */
+rnn_status_t rnn_dropout_mask(rnn_handle_t h, void* stream, int T, int B, int layer,
+                              unsigned char* mask);
+
 /* Bytes of the packed weight buffer (grad = 0: matrices in the handle's
  * wtype, biases fp32) or of the packed weight-gradient buffer (grad = 1: all
  * fp32). */

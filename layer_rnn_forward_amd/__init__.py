@@ -23,6 +23,8 @@ from ._binding import (  # noqa: F401
     rnn_destroy,
     rnn_set_schedule,
     rnn_set_sequence_lengths,
+    rnn_set_dropout,
+    rnn_dropout_mask,
     rnn_weights_size,
     rnn_weight_offset,
     rnn_workspace_size,

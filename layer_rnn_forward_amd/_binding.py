@@ -46,6 +46,8 @@ def load_library():
         "rnn_destroy": [vp],
         "rnn_set_schedule": [vp, i],
         "rnn_set_sequence_lengths": [vp, vp],
+        "rnn_set_dropout": [vp, ctypes.c_double, ctypes.c_ulonglong],
+        "rnn_dropout_mask": [vp, vp, i, i, i, vp],
         "rnn_weights_size": [vp, i, psz],
         "rnn_weight_offset": [vp, i, i, i, i, psz, psz],
         "rnn_workspace_size": [vp, i, i, i, psz],
@@ -143,6 +145,20 @@ def rnn_set_sequence_lengths(h: Handle, lengths):
     _check(load_library().rnn_set_sequence_lengths(h.ptr, _ptr(lengths, "lengths", torch.int32)),
            "rnn_set_sequence_lengths")
     h.lengths = lengths
+
+
+def rnn_set_dropout(h: Handle, p: float, seed: int = 0):
+    """Inter-layer dropout probability and 64-bit seed of the training passes
+    that follow (p = 0 switches it off)."""
+    _check(load_library().rnn_set_dropout(h.ptr, float(p), int(seed) & ((1 << 64) - 1)),
+           "rnn_set_dropout")
+
+
+def rnn_dropout_mask(h: Handle, T: int, B: int, layer: int, mask):
+    """Write the keep mask (uint8 device tensor, T*B*D*H elements) a training
+    pass applies to layer ``layer``'s input."""
+    _check(load_library().rnn_dropout_mask(h.ptr, _stream(), T, B, layer,
+                                           _ptr(mask, "mask", torch.uint8)), "rnn_dropout_mask")
 
 
 def rnn_weights_size(h: Handle, grad: int = 0) -> int:

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librnn_mi355x.so")
-SOURCES = ["gemm.hip", "layout.hip", "recurrent.hip", "recurrent_gru2.hip", "rnn_api.cpp"]
+SOURCES = ["dropout.hip", "gemm.hip", "layout.hip", "recurrent.hip", "recurrent_gru2.hip", "rnn_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -67,6 +67,8 @@ struct Plan {
   size_t off_dg = 0, off_dgT = 0, off_dghT = 0, dg_layer = 0, dgT_layer = 0;
   int dg_ld = 0, tb_ld = 0;
   size_t off_dy = 0, dy_slot = 0;
+  // dropped inputs of layers 1..L-1 (training with dropout), slot l-1
+  size_t off_xd = 0, xd_slot = 0;
   size_t off_scr = 0, scr_bytes = 0;   // operand preparation for the GEMMs
   size_t total = 0;
   rnn_status_t status = RNN_STATUS_SUCCESS;
@@ -84,6 +86,12 @@ struct rnn_desc {
   int seq_stage = 0, seq_T = -1, seq_B = -1;
   const void* seq_ws = nullptr;
   const int* seq_lengths = nullptr;
+  // inter-layer dropout: current setting, and the one the pending training
+  // sequence's forward used
+  double drop_p = 0.0;
+  unsigned long long drop_seed = 0;
+  double seq_drop_p = 0.0;
+  unsigned long long seq_drop_seed = 0;
   // profiling
   int prof = 0;
   std::vector<ProfPending> pending;
@@ -203,7 +211,8 @@ int gemm_split(const rnn_desc* h, int M, int N, int K, int batches) {
   return std::max(1, s);
 }
 
-Plan make_plan(const rnn_desc* h, int T, int B, int training) {
+// `drop`: the inter-layer dropout probability of a training pass (0: none)
+Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0) {
   Plan p;
   p.T = T;
   p.B = B;
@@ -247,8 +256,9 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
 
   // ---- forward sweep: batch chunks of up to 32 rows
   chunk(env_int("RNN_FWD_MAX_BC", 32), p.fwd);
+  // (dropout between layers needs the whole layer below first)
   p.wavefront = (h->D == 1 && h->L > 1 && h->L <= kMaxLayersPerLaunch && !is_gru2(h) &&
-                 env_int("RNN_NO_WAVEFRONT", 0) == 0);
+                 !(training && drop > 0.0) && env_int("RNN_NO_WAVEFRONT", 0) == 0);
   const int fl = p.wavefront ? h->L : 1;
   const int fmt = ceil_div(p.fwd.Bc, 16);
   if (!plan_fwd(h, fmt, p.fwd.Bc, fl * h->D * p.fwd.nchunk, p.wavefront, &p.fwd)) {
@@ -340,6 +350,11 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training) {
   p.yin_slot = align_up(TB * h->D * h->H * 4);
   if (h->L > 1) p.yin_slots = (training || p.wavefront) ? h->L - 1 : std::min(2, h->L - 1);
   off += p.yin_slot * p.yin_slots;
+  p.off_xd = off;
+  if (training && drop > 0.0 && h->L > 1) {
+    p.xd_slot = p.yin_slot;
+    off += p.xd_slot * (h->L - 1);
+  }
   // operand-preparation scratch (fwd: layer input in bf16)
   int Imax = h->I;
   for (int l = 1; l < h->L; ++l) Imax = std::max(Imax, in_width(h, l));
@@ -548,7 +563,8 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   if (!W || !ws) return RNN_STATUS_INVALID_ARG;
   if (T > 0 && B > 0 && (!x || !y)) return RNN_STATUS_INVALID_ARG;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  Plan p = make_plan(h, T, B, training);
+  const double drop = training ? h->drop_p : 0.0;
+  Plan p = make_plan(h, T, B, training, drop);
   if (p.status != RNN_STATUS_SUCCESS) return p.status;
   if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
   if (h->seq_ws == ws) h->seq_stage = 0;
@@ -564,6 +580,8 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
       h->seq_B = B;
       h->seq_ws = ws;
       h->seq_lengths = h->lengths;
+      h->seq_drop_p = drop;
+      h->seq_drop_seed = h->drop_seed;
     }
     return RNN_STATUS_SUCCESS;
   }
@@ -645,6 +663,13 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
     f.wavefront = 0;
     for (int l = 0; l < h->L; ++l) {
       const float* in = (l == 0) ? x : yin(l - 1);
+      if (l > 0 && drop > 0.0) {   // layer l reads y_{l-1} * keep / (1 - p)
+        float* xd = at<float>(ws, p.off_xd + p.xd_slot * (size_t)(l - 1));
+        ProfScope ps(h, s, K_PREP);
+        RNN_TRY(dev(rnn_launch_dropout(in, xd, nullptr, (long long)T * B * h->D * h->H,
+                                       h->drop_seed, l, drop, s)));
+        in = xd;
+      }
       RNN_TRY(gemm_input(h, s, p, l, in, W, gx, ws));
       f.first_layer = l;
       f.gx = gx;
@@ -664,6 +689,8 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
     h->seq_B = B;
     h->seq_ws = ws;
     h->seq_lengths = h->lengths;
+    h->seq_drop_p = drop;
+    h->seq_drop_seed = h->drop_seed;
   }
   return RNN_STATUS_SUCCESS;
 }
@@ -756,6 +783,23 @@ rnn_status_t rnn_set_sequence_lengths(rnn_handle_t h, const int* lengths) {
   return RNN_STATUS_SUCCESS;
 }
 
+rnn_status_t rnn_set_dropout(rnn_handle_t h, double p, unsigned long long seed) {
+  if (!h || !(p >= 0.0 && p <= 1.0)) return RNN_STATUS_INVALID_ARG;
+  h->drop_p = p;
+  h->drop_seed = seed;
+  return RNN_STATUS_SUCCESS;
+}
+
+rnn_status_t rnn_dropout_mask(rnn_handle_t h, void* stream, int T, int B, int layer,
+                              unsigned char* mask) {
+  if (!h || T < 0 || B < 0 || layer < 1 || layer >= h->L) return RNN_STATUS_INVALID_ARG;
+  const long long n = (long long)T * B * h->D * h->H;
+  if (n == 0) return RNN_STATUS_SUCCESS;
+  if (!mask) return RNN_STATUS_INVALID_ARG;
+  return dev(rnn_launch_dropout(nullptr, nullptr, mask, n, h->drop_seed, layer, h->drop_p,
+                                reinterpret_cast<hipStream_t>(stream)));
+}
+
 rnn_status_t rnn_set_schedule(rnn_handle_t h, rnn_schedule_t s) {
   if (!h || (s != RNN_SCHED_AUTO && s != RNN_SCHED_PERSISTENT && s != RNN_SCHED_STEPPED))
     return RNN_STATUS_INVALID_ARG;
@@ -787,7 +831,7 @@ rnn_status_t rnn_weight_offset(rnn_handle_t h, int grad, int layer, int dir, rnn
 
 rnn_status_t rnn_workspace_size(rnn_handle_t h, int T, int B, int training, size_t* bytes) {
   if (!h || !bytes || T < 0 || B < 0) return RNN_STATUS_INVALID_ARG;
-  Plan p = make_plan(h, T, B, training ? 1 : 0);
+  Plan p = make_plan(h, T, B, training ? 1 : 0, training ? h->drop_p : 0.0);
   if (p.status == RNN_STATUS_UNSUPPORTED) return p.status;
   *bytes = p.total;
   return RNN_STATUS_SUCCESS;
@@ -817,7 +861,7 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
       h->seq_lengths != h->lengths)
     return RNN_STATUS_BAD_CALL_ORDER;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  Plan p = make_plan(h, T, B, 1);
+  Plan p = make_plan(h, T, B, 1, h->seq_drop_p);
   if (p.status != RNN_STATUS_SUCCESS) return p.status;
   if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
   RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err)));
@@ -927,9 +971,17 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
     g.a_vec = 1;
     g.b_vec = 1;
     g.split_k = 1;
-    ProfScope ps(h, s, K_GEMM_DX);
-    gemm_consts(h, g, ws, p.off_err);
-    RNN_TRY(dev(rnn_launch_gemm(g, bf, EPI_STORE, 1, s)));
+    {
+      ProfScope ps(h, s, K_GEMM_DX);
+      gemm_consts(h, g, ws, p.off_err);
+      RNN_TRY(dev(rnn_launch_gemm(g, bf, EPI_STORE, 1, s)));
+    }
+    if (l > 0 && h->seq_drop_p > 0.0) {   // d y_{l-1} = d(input of l) * keep / (1 - p)
+      float* dyl = dyslot(l - 1);
+      ProfScope ps(h, s, K_PREP);
+      RNN_TRY(dev(rnn_launch_dropout(dyl, dyl, nullptr, (long long)T * B * h->D * h->H,
+                                     h->seq_drop_seed, l, h->seq_drop_p, s)));
+    }
   }
   h->seq_stage = 2;
   return RNN_STATUS_SUCCESS;
@@ -945,7 +997,7 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
       h->seq_lengths != h->lengths)
     return RNN_STATUS_BAD_CALL_ORDER;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  Plan p = make_plan(h, T, B, 1);
+  Plan p = make_plan(h, T, B, 1, h->seq_drop_p);
   if (p.status != RNN_STATUS_SUCCESS) return p.status;
   if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
   void* wsm = const_cast<void*>(ws);
@@ -974,7 +1026,9 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
   const int R = reserve_slots(kmode(h));
   for (int l = 0; l < h->L; ++l) {
     const int I_l = in_width(h, l);
-    const float* X = (l == 0) ? x : yl(l - 1);
+    const float* X = (l == 0) ? x
+                     : (h->seq_drop_p > 0.0 ? at<float>(wsm, p.off_xd + p.xd_slot * (size_t)(l - 1))
+                                            : yl(l - 1));
     const char* dgT = at<char>(wsm, p.off_dgT + p.dgT_layer * l);
     const char* dghT = h->mode == RNN_GRU ? at<char>(wsm, p.off_dghT + p.dgT_layer * l) : dgT;
     {  // X^T [I_l][T*B] and H_prev^T [D][H][T*B] (shifted one step, h0 at the start)

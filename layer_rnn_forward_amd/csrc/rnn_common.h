@@ -184,6 +184,12 @@ hipError_t rnn_launch_bwd(const rnnk::BwdParams& p, int mode, int bf16, const Re
 hipError_t rnn_launch_fill(void* const* ptrs, const size_t* bytes, const uint32_t* values, int n,
                            hipStream_t s);
 hipError_t rnn_copy_state(float* dst, const float* src, size_t n, hipStream_t s);
+// Inter-layer dropout of n fp32 elements (dst = src * keep / (1 - prob),
+// in place allowed) and/or its keep mask (bytes, 1 = kept); either output
+// may be null.  Mask of element e: Philox4x32-10 word e mod 4 at counter
+// (e div 4, layer) under the 64-bit seed, kept when >= floor(prob * 2^32).
+hipError_t rnn_launch_dropout(const float* src, float* dst, uint8_t* mask, long long n,
+                              unsigned long long seed, int layer, double prob, hipStream_t s);
 // Maximum co-resident workgroups of the fwd/bwd kernel for this config (0 if unsupported).
 int rnn_fwd_max_resident(int mode, int bf16, const RecConfig& c, size_t lds);
 // GRU flavours whose n reads (r*h) W_hn: two exchanges per step, persistent only.

@@ -25,14 +25,17 @@ def to_dev(a, dtype=torch.float32):
 
 
 def run_gpu(mode, L, D, case, wtype="f32", sched=R.SCHED_AUTO, training=True, backward=True,
-            pass_state=True, pass_grads=True, repeat=1, lengths=None):
+            pass_state=True, pass_grads=True, repeat=1, lengths=None, dropout=None):
     """Returns a dict of numpy results from the library (fp32 -> fp64).
-    ``lengths``: per-row valid steps (list of ints) or None."""
+    ``lengths``: per-row valid steps (list of ints) or None; ``dropout``:
+    ``(p, seed)`` of inter-layer dropout or None."""
     x = case["x"]
     T, B, I = x.shape
     H = case["params"][0][0]["w_hh"].shape[1]
     h = R.rnn_create(mode, L, D, I, H, wtype)
     R.rnn_set_schedule(h, sched)
+    if dropout is not None:
+        R.rnn_set_dropout(h, *dropout)
     if lengths is not None:
         R.rnn_set_sequence_lengths(h, torch.as_tensor(lengths, dtype=torch.int32, device="cuda"))
     W = R.pack_weights(h, case["params"])
@@ -81,13 +84,16 @@ def run_gpu(mode, L, D, case, wtype="f32", sched=R.SCHED_AUTO, training=True, ba
 GRU_FLAVOURS = {"gru_tf": "tf", "gru_paper": "paper"}
 
 
-def run_oracle(mode, L, D, case, backward=True, pass_state=True, pass_grads=True, lengths=None):
+def run_oracle(mode, L, D, case, backward=True, pass_state=True, pass_grads=True, lengths=None,
+               dropout=None):
     variant = GRU_FLAVOURS.get(mode, "pytorch")
     mode = "gru" if mode in GRU_FLAVOURS else mode
     h0 = case["h0"] if pass_state else None
     c0 = case["c0"] if (pass_state and mode == "lstm") else None
     y, hy, cy, cache = orc.forward(mode, case["x"], case["params"], h0=h0, c0=c0, num_dirs=D,
-                                   gru_variant=variant, keep=backward, lengths=lengths)
+                                   gru_variant=variant, keep=backward, lengths=lengths,
+                                   dropout=dropout[0] if dropout else 0.0,
+                                   dropout_seed=dropout[1] if dropout else 0)
     out = {"y": y, "hy": hy}
     if mode == "lstm":
         out["cy"] = cy

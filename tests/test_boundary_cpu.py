@@ -102,6 +102,33 @@ def test_workspace_size_properties(R):
         R.rnn_workspace_size(h, -1, 20, 1)
 
 
+def test_dropout_setter_and_workspace(R):
+    h = R.rnn_create("lstm", 3, 2, 64, 48)
+    base_tr = R.rnn_workspace_size(h, 20, 8, 1)
+    base_inf = R.rnn_workspace_size(h, 20, 8, 0)
+    R.rnn_set_dropout(h, 0.25, (1 << 63) + 5)
+    # one fp32 [T][B][D*H] slot per dropped layer (layers 1 and 2), inference unchanged
+    assert R.rnn_workspace_size(h, 20, 8, 1) >= base_tr + 2 * 20 * 8 * 2 * 48 * 4
+    assert R.rnn_workspace_size(h, 20, 8, 0) == base_inf
+    R.rnn_set_dropout(h, 0.0, 1)
+    assert R.rnn_workspace_size(h, 20, 8, 1) == base_tr
+    R.rnn_set_dropout(h, 1.0, 1)
+    for bad in (-0.01, 1.01, float("nan")):
+        with pytest.raises(R.RNNError) as e:
+            R.rnn_set_dropout(h, bad, 1)
+        assert e.value.status == -1
+    # mask query: layer 0 and layer L have no dropout
+    for layer in (0, 3):
+        assert R.load_library().rnn_dropout_mask(h.ptr, None, 2, 2, layer, None) == -1
+    R.rnn_destroy(h)
+    # a single layer has nothing to drop
+    h1 = R.rnn_create("gru", 1, 1, 16, 16)
+    w = R.rnn_workspace_size(h1, 10, 4, 1)
+    R.rnn_set_dropout(h1, 0.5, 3)
+    assert R.rnn_workspace_size(h1, 10, 4, 1) == w
+    R.rnn_destroy(h1)
+
+
 def test_schedule_setter(R):
     h = R.rnn_create("lstm", 1, 1, 8, 8)
     for s in (0, 1, 2):
