@@ -38,13 +38,16 @@ def flops(mode, T, B, I, H, L, D):
 
 
 class Runner:
-    def __init__(self, w, torch, R, synth):
+    def __init__(self, w, torch, R, synth, dropout=0.0):
         self.torch, self.R = torch, R
         self.w = w
+        self.dropout, self.seed = dropout, 0
         case = synth.make_workload(w)
         T, B, I, H, L, D = w.T, w.B, w.input_size, w.hidden, w.layers, w.dirs
         self.T, self.B = T, B
         self.h = R.rnn_create(w.mode, L, D, I, H, w.wtype)
+        if dropout > 0.0:   # before the workspace is sized
+            R.rnn_set_dropout(self.h, dropout, 0)
         dev = "cuda"
         f32 = torch.float32
         t = lambda a: None if a is None else torch.as_tensor(a, dtype=torch.float64).to(f32).to(dev)
@@ -63,6 +66,9 @@ class Runner:
 
     def train_step(self):
         R, T, B = self.R, self.T, self.B
+        if self.dropout > 0.0:   # fresh masks every step
+            self.seed += 1
+            R.rnn_set_dropout(self.h, self.dropout, self.seed)
         R.rnn_forward_training(self.h, T, B, self.x, self.h0, self.c0, self.W, self.y, self.hy,
                                self.cy, self.ws)
         R.rnn_backward_data(self.h, T, B, self.y, self.dy, None, None, self.W, self.h0, self.c0,
@@ -166,6 +172,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fp32", action="store_true")
     ap.add_argument("--no-small-batch", action="store_true")
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="inter-layer dropout probability of the training steps")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
@@ -180,7 +188,7 @@ def main():
     from layer_rnn_forward_amd import synth
 
     w = synth.WORKLOADS[args.workload]
-    run = Runner(w, torch, R, synth)
+    run = Runner(w, torch, R, synth, dropout=args.dropout)
     F_train = 3 * flops(w.mode, w.T, w.B, w.input_size, w.hidden, w.layers, w.dirs)
     F_fwd = flops(w.mode, w.T, w.B, w.input_size, w.hidden, w.layers, w.dirs)
 
@@ -259,7 +267,7 @@ def main():
         "data": "synthetic (seeded Gaussian inputs, uniform weights; no data set)",
         "config": {"workload": w.name, "mode": w.mode, "layers": w.layers, "dirs": w.dirs,
                    "T": w.T, "B": w.B, "input": w.input_size, "hidden": w.hidden,
-                   "weights": w.wtype, "state_accum": "f32"},
+                   "weights": w.wtype, "state_accum": "f32", "dropout": args.dropout},
         "fwd_ms": round(float(np.median(fwd_ms)), 4),
         "pct_mfma_peak": round(100.0 * value / (peak * 1000.0), 4),
         "train_step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
@@ -267,7 +275,13 @@ def main():
         "roofline": roof,
         "exchange_floor": exchange,
     }
-    if not args.no_fp32 and w.wtype == "bf16":
+    if "dropout" in kern:
+        # HBM-bound pass: reads and writes one fp32 per element of a layer input
+        n_el = w.T * w.B * w.dirs * w.hidden
+        gbs = 8.0 * n_el / (kern["dropout"]["avg_us"] * 1e-6) / 1e9
+        out["dropout_pass"] = {"avg_us": kern["dropout"]["avg_us"], "bytes_per_launch": 8 * n_el,
+                               "achieved_GBs": round(gbs, 1), "frac_hbm": round(gbs / HBM_GBS, 4)}
+    if not args.no_fp32 and w.wtype == "bf16" and args.dropout == 0.0:
         w32 = synth.WORKLOADS.get(args.workload.replace("bf16", "f32"))
         if w32 is not None:
             r32 = Runner(w32, torch, R, synth)

@@ -248,7 +248,7 @@ rnn_status_t rnn_device_status(rnn_handle_t h, void* stream, const void* ws, siz
  * 0 input-projection GEMM, 1 recurrent forward sweep, 2 recurrent backward
  * sweep, 3 dX GEMM, 4 dW GEMMs, 5 workspace fill, 6 operand preparation
  * (bf16 conversion and transposes for the GEMMs), 7 exchange probe
- * (rnn_exchange_floor).  rnn_profile_read
+ * (rnn_exchange_floor), 8 inter-layer dropout passes.  rnn_profile_read
  * synchronises, accumulates the elapsed times of finished launches and
  * returns the launch count and total milliseconds for `kernel` since the last
  * reset (rnn_set_profiling(h, 1) resets). */

@@ -12,7 +12,7 @@ MODES = {"rnn_tanh": 0, "lstm": 1, "gru": 2, "gru_tf": 3, "gru_paper": 4}
 WTYPES = {"f32": 0, "bf16": 1}
 SCHED_AUTO, SCHED_PERSISTENT, SCHED_STEPPED = 0, 1, 2
 KERNEL_NAMES = ["gemm_input", "recurrent_fwd", "recurrent_bwd", "gemm_dx", "gemm_dw", "fill", "prep",
-                "exchange_probe"]
+                "exchange_probe", "dropout"]
 STATUS_DEVICE_TIMEOUT = -7
 
 _LIB = None

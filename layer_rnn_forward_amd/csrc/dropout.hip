@@ -14,35 +14,10 @@
 #include <cmath>
 #include <cstdint>
 
+#include "philox.h"
 #include "rnn_common.h"
 
 namespace {
-
-struct U4 {
-  uint32_t v[4];
-};
-
-// Philox4x32-10.  Round: words 0 and 2 are multiplied by M0 and M1; the new
-// words are (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1, lo(M0 x0));
-// the key advances by the Weyl increments (W0, W1) between rounds.
-__device__ __forceinline__ U4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
-                                            uint32_t k0, uint32_t k1) {
-  constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
-  constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    const uint32_t hi0 = __umulhi(M0, c0), lo0 = M0 * c0;
-    const uint32_t hi1 = __umulhi(M1, c2), lo1 = M1 * c2;
-    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-    c0 = n0;
-    c1 = lo1;
-    c2 = n2;
-    c3 = lo0;
-    k0 += W0;
-    k1 += W1;
-  }
-  return U4{{c0, c1, c2, c3}};
-}
 
 struct DropParams {
   const float* src;        // may equal dst
@@ -60,7 +35,7 @@ __global__ __launch_bounds__(256) void dropout_kernel(const DropParams p) {
   const long long nq = (p.n + 3) >> 2;
   const long long stride = (long long)gridDim.x * blockDim.x;
   for (long long q = (long long)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += stride) {
-    const U4 w = philox4x32_10((uint32_t)q, (uint32_t)((unsigned long long)q >> 32), p.layer, 0u,
+    const rnnk::PhiloxOut w = rnnk::philox4x32_10((uint32_t)q, (uint32_t)((unsigned long long)q >> 32), p.layer, 0u,
                                p.k0, p.k1);
     const long long e0 = q * 4;
     bool keep[4];

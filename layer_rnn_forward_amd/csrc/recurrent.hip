@@ -43,6 +43,7 @@
 #include <type_traits>
 
 #include "device_util.h"
+#include "philox.h"
 #include "recurrent_util.h"
 #include "rnn_common.h"
 
@@ -109,7 +110,12 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   const int xflag0 = (grp - DC) * p.nwg + xa0, hflag0 = grp * p.nwg + ha0;
 
   char* ring = reinterpret_cast<char*>(p.xch) + (size_t)grp * p.ring_group;
-  const char* ring_below = inproj ? reinterpret_cast<const char*>(p.xch) + (size_t)(grp - DC) * p.ring_group : ring;
+  // with dropout the layer above reads the dropped copy of this layer's h
+  const bool drop_out = p.xch_drop != nullptr && p.wavefront && li + 1 < p.nlayers;
+  char* ring_drop = drop_out ? reinterpret_cast<char*>(p.xch_drop) + (size_t)grp * p.ring_group : nullptr;
+  const char* ring_below =
+      inproj ? reinterpret_cast<const char*>(p.xch_drop ? p.xch_drop : p.xch) + (size_t)(grp - DC) * p.ring_group
+             : ring;
   const void* wih = p.w_ih[li];
   const void* whh = p.w_hh[li];
 
@@ -215,6 +221,13 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
       continue;
     }
 
+    // this step's dropout multiplier for the layer above (data independent,
+    // so computed before the wait)
+    float dmul = 0.f;
+    if (drop_out && qv && live)
+      dmul = dropout_mult(((unsigned long long)t * B + qbg) * (unsigned long long)(D * H) + (size_t)d * H + qu,
+                          (uint32_t)(layer + 1), p.drop_k0, p.drop_k1, p.drop_thr, p.drop_scale);
+
     // input part of the pre-activations (independent of other workgroups):
     // issued now, first used in the epilogue, so its latency overlaps the wait
     float gxl[4] = {0.f, 0.f, 0.f, 0.f};
@@ -314,6 +327,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     // only the exchange store precedes the flag; y and the reserve are read
     // by later kernels, so they are written after it, off the critical path
     if (qw) ring_store<BF16>(ring + (size_t)(s + 1) * p.ring_step, my_off, hnew);
+    if (qw && drop_out) ring_store<BF16>(ring_drop + (size_t)(s + 1) * p.ring_step, my_off, hnew * dmul);
     if (p.persistent) publish(p.flags, (unsigned)(s + 2));
     if (qv && live) {
       p.y[li][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = t < qlen ? hnew : 0.f;

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <new>
@@ -33,7 +34,7 @@ int env_int(const char* name, int dflt) {
 }
 
 enum KernelId { K_GEMM_IN = 0, K_FWD = 1, K_BWD = 2, K_GEMM_DX = 3, K_GEMM_DW = 4, K_FILL = 5, K_PREP = 6,
-                K_PROBE = 7, K_NKERNELS = 8 };
+                K_PROBE = 7, K_DROPOUT = 8, K_NKERNELS = 9 };
 
 struct ProfPending {
   hipEvent_t a, b;
@@ -55,6 +56,7 @@ struct Plan {
   size_t fring_step = 0, fring_group = 0, bring_step = 0, bring_group = 0;
   size_t bring_step2 = 0, bring_group2 = 0;
   bool wavefront = false;
+  bool drop_rings = false;
   SweepPlan fwd, bwd;
   size_t off_err = 0, off_flags = 0, flags_bytes = 0;
   size_t off_xch = 0, xch_bytes = 0;
@@ -256,9 +258,10 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
 
   // ---- forward sweep: batch chunks of up to 32 rows
   chunk(env_int("RNN_FWD_MAX_BC", 32), p.fwd);
-  // (dropout between layers needs the whole layer below first)
   p.wavefront = (h->D == 1 && h->L > 1 && h->L <= kMaxLayersPerLaunch && !is_gru2(h) &&
-                 !(training && drop > 0.0) && env_int("RNN_NO_WAVEFRONT", 0) == 0);
+                 env_int("RNN_NO_WAVEFRONT", 0) == 0);
+  // a wavefront with dropout also rings each layer's dropped h for the layer above
+  p.drop_rings = p.wavefront && training && drop > 0.0;
   const int fl = p.wavefront ? h->L : 1;
   const int fmt = ceil_div(p.fwd.Bc, 16);
   if (!plan_fwd(h, fmt, p.fwd.Bc, fl * h->D * p.fwd.nchunk, p.wavefront, &p.fwd)) {
@@ -335,7 +338,7 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
   p.flags_bytes = (size_t)std::max(p.fwd.grid, p.bwd.grid) * kFlagStride * 4;
   off = align_up(off + p.flags_bytes);
   p.off_xch = off;
-  size_t xf = (size_t)p.fwd.groups * p.fring_group * (is_gru2(h) ? 2 : 1);
+  size_t xf = (size_t)p.fwd.groups * p.fring_group * ((is_gru2(h) || p.drop_rings) ? 2 : 1);
   size_t xb = (size_t)p.bwd.groups * (p.bring_group + p.bring_group2);
   p.xch_bytes = std::max(xf, training ? xb : (size_t)0);
   off = align_up(off + p.xch_bytes);
@@ -647,6 +650,13 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   if (p.wavefront) {
     RNN_TRY(gemm_input(h, s, p, 0, x, W, gx, ws));
     f.wavefront = 1;
+    if (p.drop_rings) {
+      f.xch_drop = at<void>(ws, p.off_xch + (size_t)p.fwd.groups * p.fring_group);
+      f.drop_thr = (unsigned long long)std::floor(drop * 4294967296.0);
+      f.drop_scale = drop < 1.0 ? (float)(1.0 / (1.0 - drop)) : 0.f;
+      f.drop_k0 = (unsigned)(h->drop_seed & 0xFFFFFFFFull);
+      f.drop_k1 = (unsigned)(h->drop_seed >> 32);
+    }
     f.first_layer = 0;
     f.gx = gx;
     for (int l = 0; l < h->L; ++l) {
@@ -659,13 +669,19 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
       f.reserve[l] = res(l);
     }
     RNN_TRY(run_sweep(h->L));
+    // the dropped inputs of the upper layers, for their weight gradients
+    for (int l = 1; l < h->L && drop > 0.0 && training; ++l) {
+      ProfScope ps(h, s, K_DROPOUT);
+      RNN_TRY(dev(rnn_launch_dropout(yin(l - 1), at<float>(ws, p.off_xd + p.xd_slot * (size_t)(l - 1)), nullptr,
+                                     (long long)T * B * h->D * h->H, h->drop_seed, l, drop, s)));
+    }
   } else {
     f.wavefront = 0;
     for (int l = 0; l < h->L; ++l) {
       const float* in = (l == 0) ? x : yin(l - 1);
       if (l > 0 && drop > 0.0) {   // layer l reads y_{l-1} * keep / (1 - p)
         float* xd = at<float>(ws, p.off_xd + p.xd_slot * (size_t)(l - 1));
-        ProfScope ps(h, s, K_PREP);
+        ProfScope ps(h, s, K_DROPOUT);
         RNN_TRY(dev(rnn_launch_dropout(in, xd, nullptr, (long long)T * B * h->D * h->H,
                                        h->drop_seed, l, drop, s)));
         in = xd;
@@ -978,7 +994,7 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
     }
     if (l > 0 && h->seq_drop_p > 0.0) {   // d y_{l-1} = d(input of l) * keep / (1 - p)
       float* dyl = dyslot(l - 1);
-      ProfScope ps(h, s, K_PREP);
+      ProfScope ps(h, s, K_DROPOUT);
       RNN_TRY(dev(rnn_launch_dropout(dyl, dyl, nullptr, (long long)T * B * h->D * h->H,
                                      h->seq_drop_seed, l, h->seq_drop_p, s)));
     }

@@ -98,6 +98,13 @@ struct FwdParams {
   const int* lengths;     // [B] valid steps per row (clamped to [0, T]), or null: all T
   void* xch2;             // GRU with (r*h) W_hn: rings of r*h, laid out as xch
   int paper;              // GRU with (r*h) W_hn: 1 for h = (1-z) h_prev + z n
+  // wavefront training with inter-layer dropout: rings (laid out as xch) of
+  // each layer's h times its dropout multiplier, read by the layer above; or
+  // null.  Multiplier of element e of layer l's input: philox.h dropout_mult
+  void* xch_drop;
+  unsigned long long drop_thr;
+  float drop_scale;
+  unsigned drop_k0, drop_k1;
   int first_layer;        // index of layer 0 of this launch in the network
   const void* w_ih[kMaxLayersPerLaunch];   // layer block [D*G*H, I_l]
   const void* w_hh[kMaxLayersPerLaunch];   // layer block [D*G*H, H]

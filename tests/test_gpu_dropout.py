@@ -130,3 +130,21 @@ def test_backward_uses_the_forward_settings():
     e2 = np.max(np.abs(gdp[1][0]["w_ih"] - odp[1][0]["w_ih"])) / np.max(np.abs(odp[1][0]["w_ih"]))
     assert e2 < 1e-3
     R.rnn_destroy(h)
+
+
+@pytest.mark.parametrize("mode", ["lstm", "rnn_tanh", "gru"])
+def test_dropout_in_the_layer_wavefront(mode):
+    # unidirectional stacks run all layers in one launch: each layer rings a
+    # dropped copy of its h for the layer above; the stepped schedule (one
+    # launch per step) must give the same bits
+    T, B, I, H = 12, 7, 20, 64
+    drop = (0.35, 4242)
+    _announce("dropout-wavefront", mode, drop)
+    case = _case(mode, 4, 1, T, B, I, H, "f32", seed=26)
+    gp = run_gpu(mode, 4, 1, case, "f32", sched=R.SCHED_PERSISTENT, dropout=drop)
+    gs = run_gpu(mode, 4, 1, case, "f32", sched=R.SCHED_STEPPED, dropout=drop)
+    for k in gp:
+        if k != "dW":
+            assert np.array_equal(gp[k], gs[k]), k
+    o = run_oracle(mode, 4, 1, case, dropout=drop)
+    check(compare(gp, o, mode, 4, 1), *TOL["f32"])
