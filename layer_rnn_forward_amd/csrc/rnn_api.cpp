@@ -135,9 +135,12 @@ const RecConfig kFwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 1, 16, 4}, {1, 2
                               {2, 2, 8, 4},  {2, 1, 16, 4}, {2, 2, 16, 4}, {4, 1, 4, 8},  {4, 2, 4, 8},
                               {4, 1, 8, 8},  {4, 2, 8, 8},
                               {1, 2, 32, 4}, {1, 2, 16, 8}, {2, 2, 16, 8}, {4, 2, 16, 8}};
+// (measured at the DS2 shapes: eight waves of 16 K chunks beat four waves
+// of 32 by 11-13 % in the backward sweep -- half the granules per wave; 32
+// chunks on eight waves spill, so fp32 keeps four waves of 64)
 const RecConfig kBwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 1, 16, 4}, {1, 2, 16, 4},
-                              {1, 1, 32, 4}, {1, 2, 32, 4}, {1, 1, 64, 4}, {1, 2, 64, 4},
-                              {1, 1, 16, 8}, {1, 2, 16, 8}, {1, 2, 32, 8}, {1, 1, 32, 8}};
+                              {1, 1, 16, 8}, {1, 2, 16, 8}, {1, 1, 32, 4}, {1, 2, 32, 4},
+                              {1, 1, 64, 4}, {1, 2, 64, 4}, {1, 2, 32, 8}, {1, 1, 32, 8}};
 
 // Units per workgroup are a multiple of the per-lane MFMA k run (8 bf16 / 4
 // fp32 values, 16 bytes) so that every A fragment of the exchange comes from
@@ -160,7 +163,9 @@ bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepP
     const int ngr = (inproj ? 2 : 1) * nwg * (tryU / Q);   // K granules
     // (measured: four waves with two load batches beat eight waves with one
     // for the fp32 DS2 forward, so the list order, fewer waves first, stands)
+    const int force = env_int("RNN_FWD_CFG", -1);   // tuning: only this list entry
     for (const RecConfig& c : kFwdCfgs) {
+      if (force >= 0 && &c != &kFwdCfgs[force % (int)(sizeof(kFwdCfgs) / sizeof(kFwdCfgs[0]))]) continue;
       if (c.mt != mt) continue;
       if (is_gru2(h) && !rnn_gru2_fwd_config_supported(h->wtype == RNN_W_BF16, c)) continue;
       if (GB * tryU > 16 * c.nt || Bc * tryU > 64 * c.nwaves) continue;
@@ -186,7 +191,9 @@ bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, SweepPlan* sp) {
     // the flavours with two exchanges hold two weight sets: the n gate
     // (nwg*U/Q granules) and r, z (twice that), each within kpw chunks
     const int ngr2 = 2 * nwg * (tryU / Q);
+    const int force = env_int("RNN_BWD_CFG", -1);   // tuning: only this list entry
     for (const RecConfig& c : kBwdCfgs) {
+      if (force >= 0 && &c != &kBwdCfgs[force % (int)(sizeof(kBwdCfgs) / sizeof(kBwdCfgs[0]))]) continue;
       if (c.mt != mt || (c.kpw > 32 && h->wtype == RNN_W_BF16)) continue;
       if (is_gru2(h) && !rnn_gru2_bwd_config_supported(h->wtype == RNN_W_BF16, c)) continue;
       if (tryU > 16 * c.nt || Bc * tryU > 64 * c.nwaves) continue;
