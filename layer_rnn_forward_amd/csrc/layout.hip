@@ -22,44 +22,106 @@ __device__ __forceinline__ void st_elem(void* p, size_t i, float v) {
   else reinterpret_cast<float*>(p)[i] = v;
 }
 
-// 64x64 tiles through LDS; 256 threads; each thread moves 16 elements.
+// Source row of input row r (null: a row of zeros).  With lengths, row
+// r = t*len_B + b reads alt row b once t + 1 reaches the row's clamped length;
+// rows in [alt_r0, alt_r1) read alt rows from 0; every other row reads src row
+// r + shift.
+template <bool BF>
+__device__ __forceinline__ const char* src_row(const TransposeParams& p, int r) {
+  constexpr int ES = BF ? 2 : 4;
+  int lb = -1;
+  if (p.lengths) {
+    const int t = r / p.len_B, b = r - t * p.len_B;
+    if (t + 1 >= min(max(p.lengths[b], 0), p.len_T)) lb = b;
+  }
+  if (lb >= 0) return p.alt ? reinterpret_cast<const char*>(p.alt) + (size_t)lb * p.ld_alt * ES : nullptr;
+  if (r >= p.alt_r0 && r < p.alt_r1)
+    return p.alt ? reinterpret_cast<const char*>(p.alt) + (size_t)(r - p.alt_r0) * p.ld_alt * ES : nullptr;
+  return reinterpret_cast<const char*>(p.src) + (size_t)((long long)(r + p.shift) * p.ld_src) * ES;
+}
+
+// 64x64 tiles through LDS, 256 threads.  Loads: a thread reads 4 consecutive
+// columns of one row (one 16-byte fp32 or 8-byte bf16 access when p.vec_in);
+// stores: a thread writes 8 consecutive rows of one output row (one 16-byte
+// bf16 or two 16-byte fp32 accesses when p.vec_out).  Both flags are set by
+// the host only when every row start and the tile edges keep the accesses
+// aligned and inside the matrix; otherwise element accesses are used.
 template <bool IN_BF, bool OUT_BF>
 __global__ __launch_bounds__(256) void transpose_kernel(const TransposeParams p) {
   __shared__ float tile[64][65];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 64 x 4
+  const int tid = threadIdx.x;
+  const int cg = (tid & 15) * 4;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int rl = ty + 4 * i;
-    const int r = r0 + rl, c = c0 + tx;
-    float v = 0.f;
-    if (r < p.R && c < p.C) {
-      int lb = -1;   // alt row of a row whose successor is past its length
-      if (p.lengths) {
-        const int t = r / p.len_B, b = r - t * p.len_B;
-        if (t + 1 >= min(max(p.lengths[b], 0), p.len_T)) lb = b;
-      }
-      if (lb >= 0) {
-        if (p.alt) v = ld_elem<IN_BF>(p.alt, (size_t)lb * p.ld_alt + c);
-      } else if (r >= p.alt_r0 && r < p.alt_r1) {
-        if (p.alt) v = ld_elem<IN_BF>(p.alt, (size_t)(r - p.alt_r0) * p.ld_alt + c);
+  for (int i = 0; i < 4; ++i) {
+    const int rl = (tid >> 4) + 16 * i;
+    const int r = r0 + rl, c = c0 + cg;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    const char* row = r < p.R ? src_row<IN_BF>(p, r) : nullptr;
+    if (row) {
+      if (p.vec_in && c + 3 < p.C) {
+        if constexpr (IN_BF) {
+          const uint2 u = *reinterpret_cast<const uint2*>(row + (size_t)c * 2);
+          v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+          v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+          const float4 f = *reinterpret_cast<const float4*>(row + (size_t)c * 4);
+          v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        }
       } else {
-        v = ld_elem<IN_BF>(p.src, (size_t)((long long)(r + p.shift) * p.ld_src) + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < p.C) v[e] = ld_elem<IN_BF>(row, (size_t)(c + e));
       }
     }
-    tile[rl][tx] = v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[rl][cg + e] = v[e];
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int cl = ty + 4 * i;
-    const int c = c0 + cl, r = r0 + tx;
-    if (c < p.C && r < p.R) st_elem<OUT_BF>(p.out, (size_t)c * p.ld_out + r, tile[tx][cl]);
+  for (int j = 0; j < 2; ++j) {
+    const int item = tid + 256 * j;
+    const int cl = item >> 3, rg = (item & 7) * 8;
+    const int c = c0 + cl, r = r0 + rg;
+    if (c >= p.C) continue;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[rg + e][cl];
+    if (p.vec_out && r + 7 < p.R) {
+      if constexpr (OUT_BF) {
+        const uint4 u = make_uint4(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]), pack2bf(v[4], v[5]),
+                                   pack2bf(v[6], v[7]));
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.out) + (size_t)c * p.ld_out + r) = u;
+      } else {
+        float4* o = reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + (size_t)c * p.ld_out + r);
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (r + e < p.R) st_elem<OUT_BF>(p.out, (size_t)c * p.ld_out + r + e, v[e]);
+    }
   }
 }
 
+// fp32 -> bf16 (round to nearest even).  Vector path (cols % 8 == 0 and every
+// row start 16-byte aligned on both sides): a thread converts 8 consecutive
+// elements with two 16-byte loads and one 16-byte store.
 __global__ void convert_kernel(const float* src, long long ld_src, uint16_t* dst, long long ld_dst,
-                               int rows, int cols) {
+                               int rows, int cols, int vec) {
+  if (vec) {
+    const int cv = cols >> 3;
+    const size_t n = (size_t)rows * cv;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+      const int r = (int)(i / (unsigned)cv), c = (int)(i - (size_t)r * cv) * 8;
+      const float4* s4 = reinterpret_cast<const float4*>(src + (size_t)r * ld_src + c);
+      const float4 a = s4[0], b = s4[1];
+      *reinterpret_cast<uint4*>(dst + (size_t)r * ld_dst + c) =
+          make_uint4(pack2bf(a.x, a.y), pack2bf(a.z, a.w), pack2bf(b.x, b.y), pack2bf(b.z, b.w));
+    }
+    return;
+  }
   const size_t n = (size_t)rows * cols;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
     const size_t r = i / cols, c = i % cols;
@@ -72,19 +134,28 @@ __global__ void convert_kernel(const float* src, long long ld_src, uint16_t* dst
 hipError_t rnn_launch_transpose(const TransposeParams& p, int in_bf16, int out_bf16, hipStream_t s) {
   if (p.R <= 0 || p.C <= 0) return hipSuccess;
   dim3 grid((p.C + 63) / 64, (p.R + 63) / 64);
-  if (in_bf16 && out_bf16) hipLaunchKernelGGL((transpose_kernel<true, true>), grid, dim3(256), 0, s, p);
-  else if (in_bf16 && !out_bf16) hipLaunchKernelGGL((transpose_kernel<true, false>), grid, dim3(256), 0, s, p);
-  else if (!in_bf16 && out_bf16) hipLaunchKernelGGL((transpose_kernel<false, true>), grid, dim3(256), 0, s, p);
-  else hipLaunchKernelGGL((transpose_kernel<false, false>), grid, dim3(256), 0, s, p);
+  // vector accesses only where every row start they can touch is aligned
+  TransposeParams q = p;
+  const uintptr_t ia = in_bf16 ? 8 : 16, es_in = in_bf16 ? 2 : 4, es_out = out_bf16 ? 2 : 4;
+  auto al = [](const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; };
+  q.vec_in = al(p.src, ia) && (p.ld_src * es_in) % ia == 0 &&
+             (!p.alt || (al(p.alt, ia) && (p.ld_alt * es_in) % ia == 0));
+  q.vec_out = al(p.out, 16) && (p.ld_out * es_out) % 16 == 0;
+  if (in_bf16 && out_bf16) hipLaunchKernelGGL((transpose_kernel<true, true>), grid, dim3(256), 0, s, q);
+  else if (in_bf16 && !out_bf16) hipLaunchKernelGGL((transpose_kernel<true, false>), grid, dim3(256), 0, s, q);
+  else if (!in_bf16 && out_bf16) hipLaunchKernelGGL((transpose_kernel<false, true>), grid, dim3(256), 0, s, q);
+  else hipLaunchKernelGGL((transpose_kernel<false, false>), grid, dim3(256), 0, s, q);
   return hipGetLastError();
 }
 
 hipError_t rnn_launch_convert(const float* src, long long ld_src, void* dst, long long ld_dst, int rows,
                               int cols, hipStream_t s) {
   if (rows <= 0 || cols <= 0) return hipSuccess;
-  size_t n = (size_t)rows * cols;
+  const int vec = cols % 8 == 0 && (uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0 && ld_src % 4 == 0 &&
+                  ld_dst % 8 == 0;
+  size_t n = (size_t)rows * cols / (vec ? 8 : 1);
   unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 8192);
   hipLaunchKernelGGL(convert_kernel, dim3(blocks), dim3(256), 0, s, src, ld_src,
-                     reinterpret_cast<uint16_t*>(dst), ld_dst, rows, cols);
+                     reinterpret_cast<uint16_t*>(dst), ld_dst, rows, cols, vec);
   return hipGetLastError();
 }

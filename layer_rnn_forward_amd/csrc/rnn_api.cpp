@@ -209,15 +209,33 @@ bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, SweepPlan* sp) {
   return false;
 }
 
-// Split-K factor of a weight-gradient product: enough workgroups for the
-// 256 CUs, at least 256 k per split.
+// Split-K factor of a weight-gradient product, from a two-term time model
+// fitted to the DS2 LSTM weight gradient (M = 3200, N = 801, K = 6000; split
+// 1/2/3/4: 89/67/82/79 us):
+//  * the K loop: tiles*split workgroups of K/split each, dealt in rounds of
+//    512 (two per CU, 9.3 ns per k each); a last round of at most 256 runs
+//    one per CU, 1.59x faster per workgroup than two sharing a CU;
+//  * summing the partials: 2.15 ps per element of the result per split.
+// At least 256 k per split, at most 8 splits.
 int gemm_split(const rnn_desc* h, int M, int N, int K, int batches) {
   (void)h;
   const int tiles = ceil_div(M, 128) * ceil_div(N, 128) * std::max(1, batches);
-  int s = ceil_div(512, std::max(1, tiles));
-  s = std::min(s, 8);
-  s = std::min(s, std::max(1, K / 256));
-  return std::max(1, s);
+  const int smax = std::min(8, std::max(1, K / 256));
+  const int force = env_int("RNN_DW_SPLIT", 0);   // tuning: this split factor
+  if (force > 0) return std::min(force, smax);
+  const double elems = (double)M * N * std::max(1, batches);
+  int best = 1;
+  double best_us = 1e30;
+  for (int s = 1; s <= smax; ++s) {
+    const int n = tiles * s, rem = n % 512;
+    const double rounds = 2.0 * (n / 512) + (rem == 0 ? 0.0 : rem <= 256 ? 1.59 : 2.0);
+    const double us = rounds * ceil_div(K, s) * 0.00933 + (s > 1 ? 2.15e-6 * s * elems : 0.0);
+    if (us < best_us - 1e-9) {
+      best_us = us;
+      best = s;
+    }
+  }
+  return best;
 }
 
 // `drop`: the inter-layer dropout probability of a training pass (0: none)
@@ -301,8 +319,15 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
     return true;
   };
   {
+    // training sweeps of the bf16 LSTM and GRU start at 4-row chunks (16
+    // units and eight waves per workgroup: measured 6-11 % faster at the DS2
+    // shapes, the two-exchange GRU flavours 11 %); inference and fp32 start
+    // at 16 rows (4-row chunks measured 3 % slower for LSTM inference and up
+    // to 60 % slower with fp32 weights, whose 4-unit granules make the
+    // 4-row grids wide)
+    const int fwd_pref = (training && bf && h->G >= 3) ? 4 : 16;
     bool ok = false, fits = false;
-    for (int mb : ladder(env_int("RNN_FWD_MAX_BC", 16), {16, 32})) {
+    for (int mb : ladder(env_int("RNN_FWD_MAX_BC", fwd_pref), {16, 32})) {
       if (ok && Bq <= p.fwd.Bc) break;   // a larger cap changes nothing
       ok = plan_f(mb);
       // the forward reads its fragments straight from the ring
@@ -506,13 +531,15 @@ rnn_status_t fill(rnn_desc* h, hipStream_t s, std::initializer_list<std::pair<vo
 // 16-byte constant vectors for the GEMMs after it: bf16 ones at 128, fp32
 // ones at 192.
 constexpr size_t kZero16 = 64, kOnesBf16 = 128, kOnesF32 = 192;
-rnn_status_t fill_head(rnn_desc* h, hipStream_t s, void* head) {
+// `flags` (optional): the sweep flags, cleared in the same launch.
+rnn_status_t fill_head(rnn_desc* h, hipStream_t s, void* head, void* flags = nullptr,
+                       size_t flag_bytes = 0) {
   char* c = reinterpret_cast<char*>(head);
-  void* ptrs[3] = {c, c + kOnesBf16, c + kOnesF32};
-  size_t bytes[3] = {kOnesBf16, 64, 64};
-  uint32_t vals[3] = {0u, 0x3f803f80u, 0x3f800000u};
+  void* ptrs[4] = {c, c + kOnesBf16, c + kOnesF32, flags};
+  size_t bytes[4] = {kOnesBf16, 64, 64, flag_bytes};
+  uint32_t vals[4] = {0u, 0x3f803f80u, 0x3f800000u, 0u};
   ProfScope ps_(h, s, K_FILL);
-  return dev(rnn_launch_fill(ptrs, bytes, vals, 3, s));
+  return dev(rnn_launch_fill(ptrs, bytes, vals, flags && flag_bytes ? 4 : 3, s));
 }
 
 // Constant vectors and the kernel choice of a GEMM on this workspace.
@@ -599,7 +626,10 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
   if (h->seq_ws == ws) h->seq_stage = 0;
 
-  RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err)));
+  // the first persistent sweep's flags are cleared with the head
+  bool flags_clear = p.fwd.persistent && T > 0 && B > 0;
+  RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err), flags_clear ? at<void>(ws, p.off_flags) : nullptr,
+                    p.flags_bytes));
   const size_t nstate = (size_t)h->L * h->D * B * h->H;
   if (T == 0 || B == 0) {
     if (hy) RNN_TRY(dev(rnn_copy_state(hy, h0, nstate, s)));
@@ -656,7 +686,8 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
     f.nlayers = nlayers;
     f.s_total = T + nlayers - 1;
     const int grid = p.fwd.nwg * nlayers * h->D * p.fwd.nchunk;
-    if (f.persistent) RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
+    if (f.persistent && !flags_clear) RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
+    flags_clear = false;
     if (f.persistent) {
       f.s_begin = -1;
       f.s_end = f.s_total;
@@ -907,7 +938,9 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
   Plan p = make_plan(h, T, B, 1, h->seq_drop_p);
   if (p.status != RNN_STATUS_SUCCESS) return p.status;
   if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
-  RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err)));
+  bool flags_clear = p.bwd.persistent && T > 0 && B > 0;
+  RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err), flags_clear ? at<void>(ws, p.off_flags) : nullptr,
+                    p.flags_bytes));
   const size_t nstate = (size_t)h->L * h->D * B * h->H;
   if (T == 0 || B == 0) {
     if (dh0) RNN_TRY(dev(rnn_copy_state(dh0, dhy, nstate, s)));
@@ -969,7 +1002,8 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
     b.tb_ld = p.tb_ld;
     b.dh0 = dh0 ? dh0 + l * lstride : nullptr;
     b.dc0 = dc0 ? dc0 + l * lstride : nullptr;
-    if (b.persistent) RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
+    if (b.persistent && !flags_clear) RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
+    flags_clear = false;
     if (b.persistent) {
       b.s_begin = 0;
       b.s_end = T + 1;

@@ -74,6 +74,9 @@ struct TransposeParams {
   // step whose successor is past the row's end starts from h0)
   const int* lengths;
   int len_B, len_T;
+  // set by the launcher: 16-byte (fp32) / 8-byte (bf16) row loads and
+  // 16-byte stores of 8 output elements are aligned
+  int vec_in, vec_out;
 };
 
 // ------------------------------------------------------------- recurrence
