@@ -2,6 +2,7 @@
 // conversion and row-gather transposes, so that every product reads both
 // operands K-contiguous in the compute type (the "Matrix pre-transposition"
 // row of the cuDNN-5 optimisation table in Keras issue #3692).
+#include <algorithm>
 #include <type_traits>
 
 #include "device_util.h"
@@ -46,10 +47,17 @@ __device__ __forceinline__ const char* src_row(const TransposeParams& p, int r) 
 // bf16 or two 16-byte fp32 accesses when p.vec_out).  Both flags are set by
 // the host only when every row start and the tile edges keep the accesses
 // aligned and inside the matrix; otherwise element accesses are used.
+// Up to four independent transposes in one launch (blockIdx.z selects one).
+struct TransposeBatch {
+  TransposeParams p[4];
+};
+
 template <bool IN_BF, bool OUT_BF>
-__global__ __launch_bounds__(256) void transpose_kernel(const TransposeParams p) {
+__global__ __launch_bounds__(256) void transpose_kernel(const TransposeBatch batch) {
   __shared__ float tile[64][65];
+  const TransposeParams& p = batch.p[blockIdx.z];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (r0 >= p.R || c0 >= p.C) return;   // the grid covers the largest job
   const int tid = threadIdx.x;
   const int cg = (tid & 15) * 4;
 #pragma unroll
@@ -131,21 +139,36 @@ __global__ void convert_kernel(const float* src, long long ld_src, uint16_t* dst
 
 }  // namespace
 
-hipError_t rnn_launch_transpose(const TransposeParams& p, int in_bf16, int out_bf16, hipStream_t s) {
-  if (p.R <= 0 || p.C <= 0) return hipSuccess;
-  dim3 grid((p.C + 63) / 64, (p.R + 63) / 64);
-  // vector accesses only where every row start they can touch is aligned
-  TransposeParams q = p;
+hipError_t rnn_launch_transpose_batch(const TransposeParams* ps, int n, int in_bf16, int out_bf16, hipStream_t s) {
+  if (n < 1 || n > 4) return hipErrorInvalidValue;
+  TransposeBatch b{};
+  int gx = 0, gy = 0;
   const uintptr_t ia = in_bf16 ? 8 : 16, es_in = in_bf16 ? 2 : 4, es_out = out_bf16 ? 2 : 4;
   auto al = [](const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; };
-  q.vec_in = al(p.src, ia) && (p.ld_src * es_in) % ia == 0 &&
-             (!p.alt || (al(p.alt, ia) && (p.ld_alt * es_in) % ia == 0));
-  q.vec_out = al(p.out, 16) && (p.ld_out * es_out) % 16 == 0;
-  if (in_bf16 && out_bf16) hipLaunchKernelGGL((transpose_kernel<true, true>), grid, dim3(256), 0, s, q);
-  else if (in_bf16 && !out_bf16) hipLaunchKernelGGL((transpose_kernel<true, false>), grid, dim3(256), 0, s, q);
-  else if (!in_bf16 && out_bf16) hipLaunchKernelGGL((transpose_kernel<false, true>), grid, dim3(256), 0, s, q);
-  else hipLaunchKernelGGL((transpose_kernel<false, false>), grid, dim3(256), 0, s, q);
+  for (int i = 0; i < 4; ++i) {
+    // slots past n stay empty (the grid's z extent is n)
+    TransposeParams q = i < n ? ps[i] : TransposeParams{};
+    // vector accesses only where every row start they can touch is aligned
+    q.vec_in = al(q.src, ia) && (q.ld_src * es_in) % ia == 0 &&
+               (!q.alt || (al(q.alt, ia) && (q.ld_alt * es_in) % ia == 0));
+    q.vec_out = al(q.out, 16) && (q.ld_out * es_out) % 16 == 0;
+    b.p[i] = q;
+    if (i < n && q.R > 0 && q.C > 0) {
+      gx = std::max(gx, (q.C + 63) / 64);
+      gy = std::max(gy, (q.R + 63) / 64);
+    }
+  }
+  if (gx == 0 || gy == 0) return hipSuccess;
+  dim3 grid(gx, gy, n);
+  if (in_bf16 && out_bf16) hipLaunchKernelGGL((transpose_kernel<true, true>), grid, dim3(256), 0, s, b);
+  else if (in_bf16 && !out_bf16) hipLaunchKernelGGL((transpose_kernel<true, false>), grid, dim3(256), 0, s, b);
+  else if (!in_bf16 && out_bf16) hipLaunchKernelGGL((transpose_kernel<false, true>), grid, dim3(256), 0, s, b);
+  else hipLaunchKernelGGL((transpose_kernel<false, false>), grid, dim3(256), 0, s, b);
   return hipGetLastError();
+}
+
+hipError_t rnn_launch_transpose(const TransposeParams& p, int in_bf16, int out_bf16, hipStream_t s) {
+  return rnn_launch_transpose_batch(&p, 1, in_bf16, out_bf16, s);
 }
 
 hipError_t rnn_launch_convert(const float* src, long long ld_src, void* dst, long long ld_dst, int rows,

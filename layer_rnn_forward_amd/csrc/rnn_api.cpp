@@ -238,6 +238,13 @@ int gemm_split(const rnn_desc* h, int M, int N, int K, int batches) {
   return best;
 }
 
+// The weight gradients of layer l run as one launch of two products when
+// dW_ih and dW_hh have the same shape: one direction, input width = hidden
+// width, one product per matrix (not the two-exchange GRU flavours).
+bool dw_fused(const rnn_desc* h, int l) {
+  return h->D == 1 && in_width(h, l) == h->H && !is_gru2(h) && env_int("RNN_NO_DW_FUSE", 0) == 0;
+}
+
 // `drop`: the inter-layer dropout probability of a training pass (0: none)
 Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0) {
   Plan p;
@@ -440,6 +447,9 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
     size_t part = 0;
     for (int l = 0; l < h->L; ++l) {
       const int I_l = in_width(h, l);
+      if (dw_fused(h, l))
+        part = std::max(part, (size_t)gemm_split(h, h->G * h->H, h->H + 1, (int)TB, 2) * 2 *
+                                  (size_t)h->G * h->H * (h->H + 1) * 4);
       part = std::max(part, (size_t)gemm_split(h, (int)dgh, I_l + 1, (int)TB, 1) * dgh * (I_l + 1) * 4);
       part = std::max(part, (size_t)gemm_split(h, h->G * h->H, h->H + 1, (int)TB, h->D) * h->D *
                                 (size_t)h->G * h->H * (h->H + 1) * 4);
@@ -1108,8 +1118,10 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
                                             : yl(l - 1));
     const char* dgT = at<char>(wsm, p.off_dgT + p.dgT_layer * l);
     const char* dghT = h->mode == RNN_GRU ? at<char>(wsm, p.off_dghT + p.dgT_layer * l) : dgT;
-    {  // X^T [I_l][T*B] and H_prev^T [D][H][T*B] (shifted one step, h0 at the start)
+    {  // X^T [I_l][T*B] and H_prev^T [D][H][T*B] (shifted one step, h0 at the start),
+       // in as few launches as the batched transpose allows
       ProfScope ps(h, s, K_PREP);
+      std::vector<TransposeParams> jobs;
       TransposeParams tp{};
       tp.src = X;
       tp.ld_src = I_l;
@@ -1117,7 +1129,7 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
       tp.ld_out = p.tb_ld;
       tp.R = (int)TB;
       tp.C = I_l;
-      RNN_TRY(dev(rnn_launch_transpose(tp, 0, bf, s)));
+      jobs.push_back(tp);
       for (int d = 0; d < h->D; ++d) {
         TransposeParams th{};
         th.src = yl(l) + (size_t)d * h->H;
@@ -1136,7 +1148,7 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
           th.len_B = B;
           th.len_T = T;
         }
-        RNN_TRY(dev(rnn_launch_transpose(th, 0, bf, s)));
+        jobs.push_back(th);
         if (rhT) {   // reserve slot 3 holds r*h_prev of every step
           TransposeParams tr{};
           tr.src = at<float>(wsm, p.off_res + p.res_layer * l) + (size_t)d * TB * R * h->H + 3 * (size_t)h->H;
@@ -1145,9 +1157,36 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
           tr.ld_out = p.tb_ld;
           tr.R = (int)TB;
           tr.C = h->H;
-          RNN_TRY(dev(rnn_launch_transpose(tr, 0, bf, s)));
+          jobs.push_back(tr);
         }
       }
+      for (size_t j = 0; j < jobs.size(); j += 4)
+        RNN_TRY(dev(rnn_launch_transpose_batch(jobs.data() + j, (int)std::min<size_t>(4, jobs.size() - j), 0, bf, s)));
+    }
+    if (dw_fused(h, l)) {   // dW_ih | db_ih and dW_hh | db_hh: one launch of two same-shape products
+      GemmParams g{};
+      g.M = GH;
+      g.N = h->H + 1;
+      g.K = (int)TB;
+      g.A[0] = dgT;
+      g.A[1] = dghT;
+      g.B[0] = xT;
+      g.B[1] = hT;
+      g.lda = p.tb_ld;
+      g.ldb = p.tb_ld;
+      g.n_ones = h->H;
+      g.C[0] = reinterpret_cast<float*>(dWb + h->off[1][RNN_W_IH][l]);
+      g.C[1] = reinterpret_cast<float*>(dWb + h->off[1][RNN_W_HH][l]);
+      g.ldc = h->H;
+      g.cbias[0] = reinterpret_cast<float*>(dWb + h->off[1][RNN_B_IH][l]);
+      g.cbias[1] = reinterpret_cast<float*>(dWb + h->off[1][RNN_B_HH][l]);
+      g.a_vec = g.b_vec = 1;
+      g.split_k = gemm_split(h, g.M, g.N, g.K, 2);
+      g.partial = part;
+      ProfScope ps(h, s, K_GEMM_DW);
+      gemm_consts(h, g, ws, p.off_err);
+      RNN_TRY(dev(rnn_launch_gemm(g, bf, EPI_DW, 2, s)));
+      continue;
     }
     {  // dW_ih | db_ih = dG_i^T [X | 1]
       GemmParams g{};

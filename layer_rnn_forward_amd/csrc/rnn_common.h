@@ -183,6 +183,9 @@ struct RecConfig {
 hipError_t rnn_launch_gemm(const rnnk::GemmParams& p, int bf16, int epi, int batches, hipStream_t s);
 // in_bf16 / out_bf16: element types of src (and alt) / out.
 hipError_t rnn_launch_transpose(const rnnk::TransposeParams& p, int in_bf16, int out_bf16, hipStream_t s);
+// One launch for 1..4 transposes of the same element types.
+hipError_t rnn_launch_transpose_batch(const rnnk::TransposeParams* ps, int n, int in_bf16, int out_bf16,
+                                      hipStream_t s);
 hipError_t rnn_launch_convert(const float* src, long long ld_src, void* dst, long long ld_dst, int rows,
                               int cols, hipStream_t s);   // fp32 -> bf16 (round to nearest even)
 // lds: dynamic LDS bytes (the ring-entry staging buffer, 0 when not staging)
