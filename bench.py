@@ -161,6 +161,34 @@ def copy_calibration(torch, mib=1024, reps=3):
     print(json.dumps({"copy_calibration_bytes": n * 4, "reps": reps}))
 
 
+def blas_reference(torch, w, reps=50):
+    """Context for the GEMM rows: the vendor BLAS (hipBLASLt through torch.mm,
+    bf16 operands, bf16 output, operands in the same K-contiguous layout as
+    this library's) on the three time-parallel products of the workload.
+    Not part of the operator; reported only with --blas-reference."""
+    G = {"rnn_tanh": 1, "lstm": 4, "gru": 3, "gru_tf": 3, "gru_paper": 3}[w.mode]
+    TB, N, I = w.T * w.B, w.dirs * G * w.hidden, w.input_size
+    shapes = {"gemm_input": (TB, N, I), "gemm_dx": (TB, I, N), "gemm_dw (one of dW_ih, dW_hh)": (N, I, TB)}
+    out = {}
+    for name, (M, Nn, K) in shapes.items():
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(Nn, K, device="cuda", dtype=torch.bfloat16)
+        for _ in range(5):
+            torch.mm(a, b.t())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            torch.mm(a, b.t())
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * e0.elapsed_time(e1) / reps
+        tf = 2.0 * M * Nn * K / (us * 1e-6) / 1e12
+        out[name] = {"M": M, "N": Nn, "K": K, "avg_us": round(us, 2), "TFLOPs": round(tf, 1),
+                     "frac_bf16_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +200,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fp32", action="store_true")
     ap.add_argument("--no-small-batch", action="store_true")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="also time the vendor BLAS on the same GEMM shapes (context only)")
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="inter-layer dropout probability of the training steps")
     args = ap.parse_args()
@@ -208,16 +238,16 @@ def main():
     R.rnn_set_profiling(run.h, False)
     assert R.rnn_device_status(run.h, run.ws) == 0
 
-    # latency floor of the recurrence: the forward sweep's launch with only
-    # its exchange (flag waits, ring stores, flags), no arithmetic
+    # latency floor of the recurrence: the training forward sweep's launch
+    # with only its exchange (flag waits, ring stores, flags), no arithmetic
     exchange = None
     try:
         R.rnn_set_profiling(run.h, True)
         for _ in range(max(3, args.steps // 4)):
-            R.rnn_exchange_floor(run.h, w.T, w.B, run.ws_inf)
+            R.rnn_exchange_floor(run.h, w.T, w.B, run.ws, training=True)
         n_p, ms_p = R.rnn_profile_read(run.h, R.KERNEL_NAMES.index("exchange_probe"))
         R.rnn_set_profiling(run.h, False)
-        assert R.rnn_device_status(run.h, run.ws_inf) == 0
+        assert R.rnn_device_status(run.h, run.ws) == 0
         steps_per_sweep = w.T + (w.layers - 1 if w.dirs == 1 and w.layers > 1 else 0)
         floor = 1000.0 * ms_p / n_p / steps_per_sweep
         fwd_step = kern["recurrent_fwd"]["avg_us"] / steps_per_sweep
@@ -302,6 +332,8 @@ def main():
             med = float(np.median(f_ms))
             sb[str(Bs)] = {"fwd_ms": round(med, 4), "us_per_step": round(1000.0 * med / w.T, 3)}
         out["small_batch_fwd"] = sb
+    if args.blas_reference and w.wtype == "bf16":
+        out["vendor_gemm_reference"] = blas_reference(torch, w)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, synth, args.cpu_seconds)
     print(json.dumps(out))

@@ -225,17 +225,20 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
                                   size_t ws_bytes, float* dW);
 
 /* Diagnostic: the latency floor of the persistent forward sweep.  Runs the
- * launch rnn_forward_inference would use for its first recurrent sweep (same
- * grid, same per-step waits on the producers' flags, same exchange-ring
- * stores and flag publication: the step-wise grid synchronisation of the
- * persistent-RNN design discussed in the TVM thread "Persist RNN
- * Implementation") with no weights, arithmetic or outputs, so that its time
- * divided by the steps is the cost of the exchange alone.  Writes only the
- * workspace (at least rnn_workspace_size(h, T, B, 0) bytes); invalidates a
- * pending training sequence on it.  Timed like the other launches by
+ * launch that rnn_forward_inference (training = 0) or rnn_forward_training
+ * (training = 1) would use for its first recurrent sweep -- the two passes
+ * may plan different batch chunks -- with the same grid, the same per-step
+ * waits on the producers' flags and the same exchange-ring stores and flag
+ * publication (the step-wise grid synchronisation of the persistent-RNN
+ * design discussed in the TVM thread "Persist RNN Implementation"), but no
+ * weights, arithmetic or outputs, so that its time divided by the steps is
+ * the cost of the exchange alone.  Writes only the workspace (at least
+ * rnn_workspace_size(h, T, B, training) bytes); invalidates a pending
+ * training sequence on it.  Timed like the other launches by
  * rnn_set_profiling (kernel id 7).  Errors: as rnn_forward_inference, and
  * NOT_CORESIDENT when the sweep could not run persistently. */
-rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, void* ws, size_t ws_bytes);
+rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, int training, void* ws,
+                                size_t ws_bytes);
 
 /* Synchronise `stream` and report whether a kernel that used `ws` hit an
  * expired bounded wait since the workspace was last handed to a compute

@@ -56,7 +56,7 @@ def load_library():
         "rnn_backward_data": [vp, vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz],
         "rnn_backward_weights": [vp, vp, i, i, vp, vp, vp, vp, sz, vp],
         "rnn_device_status": [vp, vp, vp, sz],
-        "rnn_exchange_floor": [vp, vp, i, i, vp, sz],
+        "rnn_exchange_floor": [vp, vp, i, i, i, vp, sz],
         "rnn_set_profiling": [vp, i],
         "rnn_profile_read": [vp, i, ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_double)],
     }
@@ -218,9 +218,11 @@ def rnn_device_status(h, ws) -> int:
     return s
 
 
-def rnn_exchange_floor(h, T, B, ws):
-    """Run the forward sweep's exchange alone (same launch, no arithmetic)."""
-    _check(load_library().rnn_exchange_floor(h.ptr, _stream(), T, B, _ptr(ws, "ws", None), _nbytes(ws)),
+def rnn_exchange_floor(h, T, B, ws, training=False):
+    """Run the forward sweep's exchange alone (same launch, no arithmetic),
+    with the plan of the training (True) or inference (False) pass."""
+    _check(load_library().rnn_exchange_floor(h.ptr, _stream(), T, B, 1 if training else 0,
+                                             _ptr(ws, "ws", None), _nbytes(ws)),
            "rnn_exchange_floor")
 
 

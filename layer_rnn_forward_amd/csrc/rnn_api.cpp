@@ -781,11 +781,12 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
 
 // The forward sweep's launch with only its exchange: the same grid, waits,
 // ring stores and flags, no weights, arithmetic or outputs.
-rnn_status_t exchange_probe_impl(rnn_desc* h, void* stream, int T, int B, void* ws, size_t ws_bytes) {
+rnn_status_t exchange_probe_impl(rnn_desc* h, void* stream, int T, int B, int training, void* ws,
+                                 size_t ws_bytes) {
   RNN_TRY(check_common(h, T, B, ws, ws_bytes));
   if (!ws) return RNN_STATUS_INVALID_ARG;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  Plan p = make_plan(h, T, B, 0);
+  Plan p = make_plan(h, T, B, training ? 1 : 0);
   if (p.status != RNN_STATUS_SUCCESS) return p.status;
   if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
   if (!p.fwd.persistent) return RNN_STATUS_NOT_CORESIDENT;
@@ -1239,8 +1240,9 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
   return RNN_STATUS_SUCCESS;
 }
 
-rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, void* ws, size_t ws_bytes) {
-  return exchange_probe_impl(h, stream, T, B, ws, ws_bytes);
+rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, int training, void* ws,
+                                size_t ws_bytes) {
+  return exchange_probe_impl(h, stream, T, B, training, ws, ws_bytes);
 }
 
 rnn_status_t rnn_device_status(rnn_handle_t h, void* stream, const void* ws, size_t ws_bytes) {

@@ -245,6 +245,10 @@ def test_exchange_floor_probe(mode, L, D, wtype):
     with pytest.raises(R.RNNError) as e:
         R.rnn_exchange_floor(h, T, B, small)
     assert e.value.status == -3
+    # the training pass's plan, on a training workspace
+    wst = torch.empty(R.rnn_workspace_size(h, T, B, 1), dtype=torch.uint8, device="cuda")
+    R.rnn_exchange_floor(h, T, B, wst, training=True)
+    assert R.rnn_device_status(h, wst) == 0
     R.rnn_destroy(h)
 
 
