@@ -79,6 +79,33 @@ class Runner:
         self.R.rnn_forward_inference(self.h, self.T, self.B, self.x, self.h0, self.c0, self.W,
                                      self.y, self.hy, self.cy, self.ws_inf)
 
+    def graph_timed(self, steps, warmup):
+        """The same training step captured once into a HIP graph on this
+        stream and replayed: what a caller that captures its step sees (the
+        library allocates, memsets and synchronises nothing inside its calls).
+        Mean ms per replay over `steps` replays."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.train_step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.train_step()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
     def timed(self, fn, steps, warmup):
         torch = self.torch
         for _ in range(warmup):
@@ -305,6 +332,12 @@ def main():
         "roofline": roof,
         "exchange_floor": exchange,
     }
+    if args.dropout == 0.0:   # (a captured step would replay one dropout seed)
+        g_ms = run.graph_timed(args.steps, args.warmup)
+        assert R.rnn_device_status(run.h, run.ws) == 0
+        out["graph_replay"] = {"ms_per_step": round(g_ms, 4),
+                               "value": round(F_train / (g_ms * 1e-3) / 1e9, 3), "unit": "GFLOP/s",
+                               "note": "the same training step captured once into a HIP graph and replayed"}
     if "dropout" in kern:
         # HBM-bound pass: reads and writes one fp32 per element of a layer input
         n_el = w.T * w.B * w.dirs * w.hidden
