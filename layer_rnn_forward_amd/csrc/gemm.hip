@@ -409,7 +409,9 @@ hipError_t launch_one(const GemmParams& p, int batches, hipStream_t s) {
 
 hipError_t rnn_launch_gemm(const GemmParams& p, int bf16, int epi, int batches, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0 || batches <= 0) return hipSuccess;
-  if (batches > 2 || p.split_k < 1 || (p.split_k > 1 && (epi != EPI_DW || !p.partial)))
+  // split-K: the weight gradients and the plain store (the partials' sum is
+  // written by splitk_reduce_kernel); never with the bias epilogue
+  if (batches > 2 || p.split_k < 1 || (p.split_k > 1 && (epi == EPI_BIAS || !p.partial)))
     return hipErrorInvalidValue;
   if (bf16) {
     if (epi == EPI_BIAS) return launch_one<true, EPI_BIAS>(p, batches, s);

@@ -209,33 +209,38 @@ bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, SweepPlan* sp) {
   return false;
 }
 
-// Split-K factor of a weight-gradient product, from a two-term time model
-// fitted to the DS2 LSTM weight gradient (M = 3200, N = 801, K = 6000; split
-// 1/2/3/4: 89/67/82/79 us):
+// Split-K factor of a time-parallel product (weight gradients, and the data
+// gradient), from a two-term time model fitted at the DS2 shapes:
 //  * the K loop: tiles*split workgroups of K/split each, dealt in rounds of
-//    512 (two per CU, 9.3 ns per k each); a last round of at most 256 runs
-//    one per CU, 1.59x faster per workgroup than two sharing a CU;
+//    512 (two per CU, 9.3 ns per k each with bf16 operands -- the DS2 LSTM
+//    weight gradient, M = 3200, N = 801, K = 6000, split 1/2/3/4: 89/67/82/79
+//    us -- and 66 ns with fp32 operands -- the fp32 input projection, data
+//    gradient and weight gradients unsplit: 295, 420 and 790 us); a last
+//    round of at most 256 runs one per CU, 1.59x faster per workgroup than
+//    two sharing a CU;
 //  * summing the partials: 2.15 ps per element of the result per split.
 // At least 256 k per split, at most 8 splits.
 int gemm_split(const rnn_desc* h, int M, int N, int K, int batches) {
-  (void)h;
+  const double us_per_k = h->wtype == RNN_W_BF16 ? 0.00933 : 0.0658;
   const int tiles = ceil_div(M, 128) * ceil_div(N, 128) * std::max(1, batches);
   const int smax = std::min(8, std::max(1, K / 256));
   const int force = env_int("RNN_DW_SPLIT", 0);   // tuning: this split factor
   if (force > 0) return std::min(force, smax);
   const double elems = (double)M * N * std::max(1, batches);
   int best = 1;
-  double best_us = 1e30;
+  double best_us = 1e30, unsplit_us = 0.0;
   for (int s = 1; s <= smax; ++s) {
     const int n = tiles * s, rem = n % 512;
     const double rounds = 2.0 * (n / 512) + (rem == 0 ? 0.0 : rem <= 256 ? 1.59 : 2.0);
-    const double us = rounds * ceil_div(K, s) * 0.00933 + (s > 1 ? 2.15e-6 * s * elems : 0.0);
+    const double us = rounds * ceil_div(K, s) * us_per_k + (s > 1 ? 2.15e-6 * s * elems : 0.0);
+    if (s == 1) unsplit_us = us;
     if (us < best_us - 1e-9) {
       best_us = us;
       best = s;
     }
   }
-  return best;
+  // split only for a predicted gain of at least 10 % (the model's error)
+  return best_us < 0.9 * unsplit_us ? best : 1;
 }
 
 // The weight gradients of layer l run as one launch of two products when
@@ -440,8 +445,15 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
     p.off_dy = off;
     p.dy_slot = align_up(TB * h->D * h->H * 4);
     if (h->L > 1) off += 2 * p.dy_slot;
-    // backward_data: W_ih^T [I_l][dg_ld]; backward_weights: X^T, H_prev^T, split-K partials
-    scr = std::max(scr, align_up(Ipad * p.dg_ld * es));
+    // backward_data: W_ih^T [I_l][dg_ld] and the dX split-K partials;
+    // backward_weights: X^T, H_prev^T, split-K partials
+    size_t part_dx = 0;
+    for (int l = 0; l < h->L; ++l) {
+      const int I_l = in_width(h, l);
+      const int sdx = gemm_split(h, (int)TB, I_l, (int)dgh, 1);
+      if (sdx > 1) part_dx = std::max(part_dx, (size_t)sdx * TB * I_l * 4);
+    }
+    scr = std::max(scr, align_up(Ipad * p.dg_ld * es) + align_up(part_dx));
     size_t wts = align_up(Ipad * p.tb_ld * es) + align_up((size_t)h->D * h->H * p.tb_ld * es);
     if (is_gru2(h)) wts += align_up((size_t)h->D * h->H * p.tb_ld * es);   // (r*H_prev)^T
     size_t part = 0;
@@ -1058,7 +1070,13 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
     g.ldc = I_l;
     g.a_vec = 1;
     g.b_vec = 1;
-    g.split_k = 1;
+    g.split_k = gemm_split(h, g.M, g.N, g.K, 1);
+    if (g.split_k > 1) {   // partials after W_ih^T in the scratch
+      int Imax = h->I;
+      for (int ll = 1; ll < h->L; ++ll) Imax = std::max(Imax, in_width(h, ll));
+      const size_t Ipad = (size_t)ceil_div(Imax, 8) * 8;
+      g.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(wT) + align_up(Ipad * p.dg_ld * (bf ? 2 : 4)));
+    }
     {
       ProfScope ps(h, s, K_GEMM_DX);
       gemm_consts(h, g, ws, p.off_err);
