@@ -262,3 +262,20 @@ def test_serving_batches(mode, B):
     g = run_gpu(mode, 1, 2, case, "bf16")
     o = run_oracle(mode, 1, 2, case)
     check(compare(g, o, mode, 1, 2), *TOL["bf16"])
+
+
+@pytest.mark.parametrize("mode,L,D,wtype,split", [("lstm", 1, 1, "f32", 3), ("gru", 1, 2, "bf16", 3),
+                                                  ("lstm", 2, 1, "bf16", 2), ("rnn_tanh", 1, 2, "f32", 8)])
+def test_forced_split_k(monkeypatch, mode, L, D, wtype, split):
+    """Split-K of the data- and weight-gradient products (fp32 partials
+    summed in split order by a second kernel), forced at a ragged shape:
+    T*B = 820 gives three K splits whose last is short, D*G*H = 544..1632
+    gives two or three for the data gradient, and no dimension is a whole
+    number of 128-wide tiles.  The factor is clamped to 256 k per split."""
+    monkeypatch.setenv("RNN_DW_SPLIT", str(split))
+    T, B, I, H = 41, 20, 72, 136
+    _announce("forced_split_k", mode, L, D, wtype, split)
+    case = _case(mode, L, D, T, B, I, H, wtype, seed=43)
+    g = run_gpu(mode, L, D, case, wtype)
+    o = run_oracle(mode, L, D, case)
+    check(compare(g, o, mode, L, D), *TOL[wtype])
