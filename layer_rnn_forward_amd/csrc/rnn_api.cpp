@@ -243,6 +243,14 @@ int gemm_split(const rnn_desc* h, int M, int N, int K, int batches) {
   return best_us < 0.9 * unsplit_us ? best : 1;
 }
 
+// Widest layer input, rounded up to whole 16-byte bf16 vectors: the row
+// count of the transposed-operand scratch (W_ih^T, X^T).
+size_t input_pad(const rnn_desc* h) {
+  int Imax = h->I;
+  for (int l = 1; l < h->L; ++l) Imax = std::max(Imax, in_width(h, l));
+  return (size_t)ceil_div(Imax, 8) * 8;
+}
+
 // The weight gradients of layer l run as one launch of two products when
 // dW_ih and dW_hh have the same shape: one direction, input width = hidden
 // width, one product per matrix (not the two-exchange GRU flavours).
@@ -423,9 +431,7 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
     off += p.xd_slot * (h->L - 1);
   }
   // operand-preparation scratch (fwd: layer input in bf16)
-  int Imax = h->I;
-  for (int l = 1; l < h->L; ++l) Imax = std::max(Imax, in_width(h, l));
-  const size_t Ipad = (size_t)ceil_div(Imax, 8) * 8;
+  const size_t Ipad = input_pad(h);
   p.dg_ld = ceil_div((int)dgh, 8) * 8;
   p.tb_ld = ceil_div((int)std::max<size_t>(TB, 1), 8) * 8;
   size_t scr = bf ? align_up(TB * Ipad * 2) : 0;
@@ -1071,12 +1077,8 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
     g.a_vec = 1;
     g.b_vec = 1;
     g.split_k = gemm_split(h, g.M, g.N, g.K, 1);
-    if (g.split_k > 1) {   // partials after W_ih^T in the scratch
-      int Imax = h->I;
-      for (int ll = 1; ll < h->L; ++ll) Imax = std::max(Imax, in_width(h, ll));
-      const size_t Ipad = (size_t)ceil_div(Imax, 8) * 8;
-      g.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(wT) + align_up(Ipad * p.dg_ld * (bf ? 2 : 4)));
-    }
+    if (g.split_k > 1)   // partials after W_ih^T in the scratch
+      g.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(wT) + align_up(input_pad(h) * p.dg_ld * (bf ? 2 : 4)));
     {
       ProfScope ps(h, s, K_GEMM_DX);
       gemm_consts(h, g, ws, p.off_err);
@@ -1119,9 +1121,7 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
   char* dWb = reinterpret_cast<char*>(dW);
   const size_t TB = (size_t)T * B;
   const size_t es = bf ? 2 : 4;
-  int Imax = h->I;
-  for (int l = 1; l < h->L; ++l) Imax = std::max(Imax, in_width(h, l));
-  const size_t Ipad = (size_t)ceil_div(Imax, 8) * 8;
+  const size_t Ipad = input_pad(h);
   char* scr = at<char>(wsm, p.off_scr);
   void* xT = scr;
   char* hT = scr + align_up(Ipad * p.tb_ld * es);
