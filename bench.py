@@ -188,6 +188,27 @@ def copy_calibration(torch, mib=1024, reps=3):
     print(json.dumps({"copy_calibration_bytes": n * 4, "reps": reps}))
 
 
+def mfma_peak(torch, R, kind, reps=3):
+    """Measured dense MFMA throughput (TFLOP/s) of this device for one MFMA
+    instruction: the library's throughput probe on two workgroups per CU,
+    timed with events."""
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    flop1, A, K, iters = {"f32_16x16x4": (8192, 32, 16, 2000), "bf16_16x16x32": (16384, 32, 32, 10000),
+                          "bf16_32x32x16": (32768, 128, 16, 5000)}[kind]
+    out = torch.empty(blocks * 256, device="cuda")
+    R.rnn_mfma_peak_probe(kind, blocks, iters // 10, out)   # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        R.rnn_mfma_peak_probe(kind, blocks, iters, out)
+    e1.record()
+    torch.cuda.synchronize()
+    assert float(out[0]) == A * iters * K / 512.0, "MFMA probe result"
+    flop = reps * blocks * 4 * iters * 8 * flop1
+    return flop / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def blas_reference(torch, w, reps=50):
     """Context for the GEMM rows: the vendor BLAS (hipBLASLt through torch.mm,
     bf16 operands, bf16 output, operands in the same K-contiguous layout as
@@ -332,6 +353,13 @@ def main():
         "roofline": roof,
         "exchange_floor": exchange,
     }
+    # measured denominators next to the published peaks
+    probes = {k: mfma_peak(torch, R, k) for k in R.MFMA_PROBES}
+    meas = {"bf16": max(probes["bf16_16x16x32"], probes["bf16_32x32x16"]), "f32": probes["f32_16x16x4"]}
+    out["mfma_peak_measured"] = {**{f"{k}_TFLOPs": round(v, 1) for k, v in probes.items()},
+                                 "published_bf16_TFLOPs": PEAK_TFLOPS["bf16"],
+                                 "published_f32_TFLOPs": PEAK_TFLOPS["f32"]}
+    out["pct_measured_mfma_peak"] = round(100.0 * value / (meas[w.wtype] * 1000.0), 4)
     if args.dropout == 0.0:   # (a captured step would replay one dropout seed)
         try:
             g_ms = run.graph_timed(args.steps, args.warmup)
@@ -358,7 +386,8 @@ def main():
             out["fp32_weights"] = {"value": round(v32, 3), "unit": "GFLOP/s",
                                    "ms_per_step": round(float(np.mean(s_ms)), 4),
                                    "fwd_ms": round(float(np.median(f_ms)), 4),
-                                   "pct_mfma_peak": round(100.0 * v32 / (PEAK_TFLOPS["f32"] * 1000), 4)}
+                                   "pct_mfma_peak": round(100.0 * v32 / (PEAK_TFLOPS["f32"] * 1000), 4),
+                                   "pct_measured_mfma_peak": round(100.0 * v32 / (meas["f32"] * 1000), 4)}
     if not args.no_small_batch and w.layers == 1:
         # serving-size batches: forward-inference latency of the same layer
         import dataclasses

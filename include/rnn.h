@@ -240,6 +240,23 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
 rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, int training, void* ws,
                                 size_t ws_bytes);
 
+/* Diagnostic: the device's achievable dense MFMA throughput, the measured
+ * denominator next to the published peak when the time-parallel products
+ * are rated against the matrix roofline.  Enqueues on `stream` one launch of
+ * `blocks` workgroups of 256 threads (four waves); every wave runs `iters`
+ * rounds of eight independent MFMA accumulations on register operands:
+ *   kind 0: four v_mfma_f32_16x16x4_f32 per round and chain (8192 flop),
+ *   kind 1: v_mfma_f32_16x16x32_bf16 (16384 flop),
+ *   kind 2: v_mfma_f32_32x32x16_bf16 (32768 flop),
+ * so the launch performs blocks * 4 * iters * 8 * (that many) flop; time it
+ * with events on `stream`.  Writes one float per thread to `out` (device
+ * memory of the caller, at least blocks * 256 floats), exactly
+ * A * iters * K / 512 with (A, K) = (32, 16), (32, 32), (128, 16) for kinds
+ * 0, 1, 2 -- a check that no work was skipped.  Touches nothing else; needs
+ * no handle.  Errors: INVALID_ARG for an unknown kind, blocks <= 0,
+ * iters <= 0 or a null `out`; DEVICE for a launch error. */
+rnn_status_t rnn_mfma_peak_probe(void* stream, int kind, int blocks, int iters, float* out);
+
 /* Synchronise `stream` and report whether a kernel that used `ws` hit an
  * expired bounded wait since the workspace was last handed to a compute
  * call: RNN_STATUS_SUCCESS or RNN_STATUS_DEVICE_TIMEOUT (or DEVICE if the

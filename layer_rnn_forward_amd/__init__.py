@@ -32,6 +32,8 @@ from ._binding import (  # noqa: F401
     rnn_forward_training,
     rnn_backward_data,
     rnn_exchange_floor,
+    rnn_mfma_peak_probe,
+    MFMA_PROBES,
     rnn_backward_weights,
     rnn_device_status,
     rnn_set_profiling,

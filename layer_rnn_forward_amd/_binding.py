@@ -57,6 +57,7 @@ def load_library():
         "rnn_backward_weights": [vp, vp, i, i, vp, vp, vp, vp, sz, vp],
         "rnn_device_status": [vp, vp, vp, sz],
         "rnn_exchange_floor": [vp, vp, i, i, i, vp, sz],
+        "rnn_mfma_peak_probe": [vp, i, i, i, vp],
         "rnn_set_profiling": [vp, i],
         "rnn_profile_read": [vp, i, ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_double)],
     }
@@ -224,6 +225,19 @@ def rnn_exchange_floor(h, T, B, ws, training=False):
     _check(load_library().rnn_exchange_floor(h.ptr, _stream(), T, B, 1 if training else 0,
                                              _ptr(ws, "ws", None), _nbytes(ws)),
            "rnn_exchange_floor")
+
+
+MFMA_PROBES = {"f32_16x16x4": 0, "bf16_16x16x32": 1, "bf16_32x32x16": 2}
+
+
+def rnn_mfma_peak_probe(kind: str, blocks: int, iters: int, out):
+    """Enqueue the dense MFMA throughput probe (`kind` a key of MFMA_PROBES)
+    on the current stream; `out` is a float32 device tensor of at least
+    blocks*256 elements."""
+    if out.numel() < blocks * 256:
+        raise ValueError("out holds fewer than blocks*256 floats")
+    _check(load_library().rnn_mfma_peak_probe(_stream(), MFMA_PROBES[kind], blocks, iters,
+                                              _ptr(out, "out")), "rnn_mfma_peak_probe")
 
 
 def rnn_set_profiling(h, enable: bool):

@@ -137,7 +137,71 @@ __global__ void convert_kernel(const float* src, long long ld_src, uint16_t* dst
   }
 }
 
+// Achievable dense MFMA throughput: every wave runs `iters` rounds of eight
+// independent accumulations (v_mfma_f32_16x16x32_bf16, or four
+// v_mfma_f32_16x16x4_f32 per round and chain for fp32) on constant operands,
+// so the matrix pipes never wait for data or for one another.  Operands are
+// powers of two (a = 2^-4, b = 2^-5 in every element) so that each thread's
+// output, the sum of its 32 accumulator values, is exact:
+// 32 * iters * K * 2^-9 with K = 32 (bf16) or 16 (fp32) per round.
+template <bool BF16>
+__global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float* out) {
+  uint4 a, b;
+  if constexpr (BF16) {
+    a = make_uint4(0x3D803D80u, 0x3D803D80u, 0x3D803D80u, 0x3D803D80u);   // bf16 2^-4
+    b = make_uint4(0x3D003D00u, 0x3D003D00u, 0x3D003D00u, 0x3D003D00u);   // bf16 2^-5
+  } else {
+    a = make_uint4(0x3D800000u, 0x3D800000u, 0x3D800000u, 0x3D800000u);   // fp32 2^-4
+    b = make_uint4(0x3D000000u, 0x3D000000u, 0x3D000000u, 0x3D000000u);   // fp32 2^-5
+  }
+  f32x4 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = mfma_chunk<BF16>(a, b, acc[c]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s += acc[c][r];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// The same with v_mfma_f32_32x32x16_bf16 (32768 flop each; a lane holds 8
+// consecutive k of one row and 16 accumulators): each thread's sum of its
+// 128 accumulator values is 128 * iters * 16 * 2^-9.
+__global__ __launch_bounds__(256) void mfma_peak_32_kernel(int iters, float* out) {
+  const uint4 a = make_uint4(0x3D803D80u, 0x3D803D80u, 0x3D803D80u, 0x3D803D80u);
+  const uint4 b = make_uint4(0x3D003D00u, 0x3D003D00u, 0x3D003D00u, 0x3D003D00u);
+  const bf16x8 av = __builtin_bit_cast(bf16x8, a), bv = __builtin_bit_cast(bf16x8, b);
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  f32x16 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
+
+hipError_t rnn_launch_mfma_peak(int kind, int blocks, int iters, float* out, hipStream_t s) {
+  if (kind == 2) hipLaunchKernelGGL(mfma_peak_32_kernel, dim3(blocks), dim3(256), 0, s, iters, out);
+  else if (kind == 1) hipLaunchKernelGGL(mfma_peak_kernel<true>, dim3(blocks), dim3(256), 0, s, iters, out);
+  else hipLaunchKernelGGL(mfma_peak_kernel<false>, dim3(blocks), dim3(256), 0, s, iters, out);
+  return hipGetLastError();
+}
 
 hipError_t rnn_launch_transpose_batch(const TransposeParams* ps, int n, int in_bf16, int out_bf16, hipStream_t s) {
   if (n < 1 || n > 4) return hipErrorInvalidValue;

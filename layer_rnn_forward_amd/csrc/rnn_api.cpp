@@ -1263,6 +1263,11 @@ rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, int 
   return exchange_probe_impl(h, stream, T, B, training, ws, ws_bytes);
 }
 
+rnn_status_t rnn_mfma_peak_probe(void* stream, int kind, int blocks, int iters, float* out) {
+  if (kind < 0 || kind > 2 || blocks <= 0 || iters <= 0 || !out) return RNN_STATUS_INVALID_ARG;
+  return dev(rnn_launch_mfma_peak(kind, blocks, iters, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
 rnn_status_t rnn_device_status(rnn_handle_t h, void* stream, const void* ws, size_t ws_bytes) {
   if (!h || !ws || ws_bytes < 256) return RNN_STATUS_INVALID_ARG;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -279,3 +279,19 @@ def test_forced_split_k(monkeypatch, mode, L, D, wtype, split):
     g = run_gpu(mode, L, D, case, wtype)
     o = run_oracle(mode, L, D, case)
     check(compare(g, o, mode, L, D), *TOL[wtype])
+
+
+@pytest.mark.parametrize("kind,A,K", [("bf16_16x16x32", 32, 32), ("f32_16x16x4", 32, 16),
+                                      ("bf16_32x32x16", 128, 16)])
+def test_mfma_peak_probe_is_exact(kind, A, K):
+    """The throughput probe behind the measured MFMA peak does all its work:
+    every thread's sum of its A accumulators is exactly A * iters * K / 512
+    (power-of-two operands, K products per round and chain)."""
+    _announce("mfma_peak_probe", kind)
+    blocks, iters = 64, 1000
+    out = torch.full((blocks * 256,), float("nan"), device="cuda")
+    R.rnn_mfma_peak_probe(kind, blocks, iters, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == A * iters * K / 512.0)
+    with pytest.raises(R.RNNError):
+        R.rnn_mfma_peak_probe(kind, 0, iters, out)
