@@ -61,7 +61,19 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   constexpr int NROW = MT * 16;
   constexpr int ES = BF16 ? 2 : 4;
 
-  __shared__ float red[NW][NROW][NCOL + 1];
+  // per-wave partial tiles; with four 16-column tiles and one row tile the
+  // 16-column group of (row, col) is XORed with (row ^ row / 4) % 4 and rows
+  // are not padded: the four row groups one write instruction covers (rows
+  // 4*fq + r) and the four batch rows one epilogue read covers then fall in
+  // distinct banks (measured 49 % -> 2 % conflict cycles; the two-row-tile
+  // kernels, which spill, keep the padded layout: slower with the swizzle)
+  constexpr bool RSWZ = NT == 4 && MT == 1;
+  constexpr int RSTR = RSWZ ? NCOL : NCOL + 1;
+  __shared__ float red[NW][NROW][RSTR];
+  auto rcol = [](int row, int col) {
+    if constexpr (RSWZ) return col ^ ((((row ^ (row >> 2)) & 3)) << 4);
+    else return col;
+  };
   __shared__ float sh_h[NROW * NCOL];
   __shared__ float sh_c[NROW * NCOL];
   __shared__ int s_fail;
@@ -277,7 +289,10 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][mt * 16 + fq * 4 + r][nt * 16 + fr] = acc[mt][nt][r];
+        for (int r = 0; r < 4; ++r) {
+          const int row = mt * 16 + fq * 4 + r;
+          red[wave][row][rcol(row, nt * 16 + fr)] = acc[mt][nt][r];
+        }
     lds_barrier();
     if (s_fail) return;   // every wave leaves after the same barrier
 
@@ -293,7 +308,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         float v = 0.f;
         if (gb < GB) {
 #pragma unroll
-          for (int w = 0; w < NW; ++w) v += red[w][qb][gb * U + qj];
+          for (int w = 0; w < NW; ++w) v += red[w][qb][rcol(qb, gb * U + qj)];
         }
         pre[gb] = v;
       }
