@@ -61,14 +61,16 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   constexpr int NROW = MT * 16;
   constexpr int ES = BF16 ? 2 : 4;
 
-  // per-wave partial tiles; with four 16-column tiles and one row tile the
-  // 16-column group of (row, col) is XORed with (row ^ row / 4) % 4 and rows
-  // are not padded: the four row groups one write instruction covers (rows
-  // 4*fq + r) and the four batch rows one epilogue read covers then fall in
-  // distinct banks (measured 49 % -> 2 % conflict cycles; the two-row-tile
-  // kernels, which spill, keep the padded layout: slower with the swizzle)
+  // per-wave partial tiles, laid out so that the four row groups one write
+  // instruction covers (rows 4*fq + r) fall in distinct 16-bank groups: with
+  // four 16-column tiles and one row tile the 16-column group of (row, col)
+  // is XORed with (row ^ row / 4) % 4 in unpadded rows (the epilogue's four
+  // batch rows then fall apart too; measured 49 % -> 2 % conflict cycles);
+  // with one or two column tiles and one row tile rows are padded by 4
+  // floats (4 * stride = 16 banks mod 64); the two-row-tile kernels, which
+  // spill, keep a padding of 1 (slower with the others)
   constexpr bool RSWZ = NT == 4 && MT == 1;
-  constexpr int RSTR = RSWZ ? NCOL : NCOL + 1;
+  constexpr int RSTR = RSWZ ? NCOL : (MT == 1 ? NCOL + 4 : NCOL + 1);
   __shared__ float red[NW][NROW][RSTR];
   auto rcol = [](int row, int col) {
     if constexpr (RSWZ) return col ^ ((((row ^ (row >> 2)) & 3)) << 4);
@@ -376,7 +378,9 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   constexpr int NROW = MT * 16;
   constexpr int ES = BF16 ? 2 : 4;
 
-  __shared__ float red[NW][NROW][NCOL + 1];
+  // rows padded by 4 floats with one row tile: the four row groups of one
+  // write instruction fall in distinct 16-bank groups
+  __shared__ float red[NW][NROW][MT == 1 ? NCOL + 4 : NCOL + 1];
   __shared__ float sh_dh[NROW * NCOL];
   __shared__ float sh_dc[NROW * NCOL];
   __shared__ int s_fail;
