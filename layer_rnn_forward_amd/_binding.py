@@ -37,7 +37,7 @@ def load_library():
     if not os.path.exists(path):
         raise RuntimeError(
             f"{path} is missing: build the HIP extension first "
-            "(python -m layer_rnn_forward_amd.build or __graft_entry__.build())")
+            "(python -m layer_rnn_forward_amd.build)")
     lib = ctypes.CDLL(path)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     psz = ctypes.POINTER(ctypes.c_size_t)
