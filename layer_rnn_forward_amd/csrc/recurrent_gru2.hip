@@ -31,7 +31,17 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
   constexpr int NROW = MT * 16;
   constexpr int ES = BF16 ? 2 : 4;
 
-  __shared__ float red[NW][NROW][NCOL + 1];
+  // per-wave partial tiles, laid out so that the four row groups of one
+  // write instruction fall in distinct 16-bank groups: four 16-column tiles
+  // and one row tile -- unpadded rows, the 16-column group XORed with
+  // (row ^ row / 4) % 4; one or two column tiles and one row tile -- rows
+  // padded by 4 floats; otherwise a padding of 1
+  constexpr bool RSWZ = NT == 4 && MT == 1;
+  __shared__ float red[NW][NROW][RSWZ ? NCOL : (MT == 1 ? NCOL + 4 : NCOL + 1)];
+  auto rcol = [](int row, int col) {
+    if constexpr (RSWZ) return col ^ ((((row ^ (row >> 2)) & 3)) << 4);
+    else return col;
+  };
   __shared__ float sh_h[NROW * NCOL];
   __shared__ int s_fail;
 
@@ -135,14 +145,17 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][mt * 16 + fq * 4 + r][nt * 16 + fr] = acc[mt][nt][r];
+        for (int r = 0; r < 4; ++r) {
+          const int row = mt * 16 + fq * 4 + r;
+          red[wave][row][rcol(row, nt * 16 + fr)] = acc[mt][nt][r];
+        }
     lds_barrier();
     return s_fail == 0;
   };
   auto reduce = [&](int gb) {
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += red[w][qb][gb * U + qj];
+    for (int w = 0; w < NW; ++w) v += red[w][qb][rcol(qb, gb * U + qj)];
     return v;
   };
 
@@ -203,7 +216,9 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
   constexpr int NROW = MT * 16;
   constexpr int ES = BF16 ? 2 : 4;
 
-  __shared__ float red[NW][NROW][NCOL + 1];
+  // rows padded by 4 floats with one row tile: the four row groups of one
+  // write instruction fall in distinct 16-bank groups
+  __shared__ float red[NW][NROW][MT == 1 ? NCOL + 4 : NCOL + 1];
   __shared__ float sh_dh[NROW * NCOL];
   __shared__ int s_fail;
 
