@@ -339,13 +339,15 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
     return true;
   };
   {
-    // training sweeps of the bf16 LSTM and GRU start at 4-row chunks (16
-    // units and eight waves per workgroup: measured 6-11 % faster at the DS2
-    // shapes, the two-exchange GRU flavours 11 %); inference and fp32 start
-    // at 16 rows (4-row chunks measured 3 % slower for LSTM inference and up
-    // to 60 % slower with fp32 weights, whose 4-unit granules make the
-    // 4-row grids wide)
-    const int fwd_pref = (training && bf && h->G >= 3) ? 4 : 16;
+    // bf16 sweeps of the LSTM (training) and of every GRU flavour (training
+    // and inference) start at 4-row chunks (16 units and eight waves per
+    // workgroup: measured 6-11 % faster training sweeps at the DS2 shapes,
+    // the two-exchange GRU flavours 11 %, GRU inference 2 %); LSTM inference
+    // and fp32 start at 16 rows (4-row chunks measured 1.5 % slower for LSTM
+    // inference and up to 60 % slower with fp32 weights, whose 4-unit
+    // granules make the 4-row grids wide)
+    const bool gru = h->mode == RNN_GRU || is_gru2(h);
+    const int fwd_pref = (bf && h->G >= 3 && (training || gru)) ? 4 : 16;
     bool ok = false, fits = false;
     for (int mb : ladder(env_int("RNN_FWD_MAX_BC", fwd_pref), {16, 32})) {
       if (ok && Bq <= p.fwd.Bc) break;   // a larger cap changes nothing
