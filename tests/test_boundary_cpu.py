@@ -148,3 +148,22 @@ def test_product_path_has_no_oracle_dependency():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not pat.search(text), f
                 assert "rnn_oracle" not in text, f
+
+
+def test_workspace_covers_split_k_partials(R, monkeypatch):
+    """The workspace holds the fp32 partials of split-K products: forcing
+    eight splits (clamped to K/256 per product) must make room for eight
+    partial copies of the fused weight gradients (dW_ih and dW_hh, 3200 x 801
+    each at this shape) and for the data gradient's (6000 x 800)."""
+    h = R.rnn_create("lstm", 1, 1, 800, 800, "f32")
+    T, B = 300, 20
+    monkeypatch.setenv("RNN_DW_SPLIT", "1")
+    w1 = R.rnn_workspace_size(h, T, B, 1)
+    monkeypatch.setenv("RNN_DW_SPLIT", "8")
+    w8 = R.rnn_workspace_size(h, T, B, 1)
+    assert w8 > w1
+    assert w8 >= 8 * 2 * 3200 * 801 * 4          # weight-gradient partials (K = 6000)
+    assert w8 >= 8 * T * B * 800 * 4              # data-gradient partials (K = 3200)
+    monkeypatch.delenv("RNN_DW_SPLIT")
+    assert R.rnn_workspace_size(h, T, B, 1) <= w8
+    R.rnn_destroy(h)
