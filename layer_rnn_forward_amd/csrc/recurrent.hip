@@ -76,8 +76,10 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     if constexpr (RSWZ) return col ^ ((((row ^ (row >> 2)) & 3)) << 4);
     else return col;
   };
-  __shared__ float sh_h[NROW * NCOL];
-  __shared__ float sh_c[NROW * NCOL];
+  // per-(row, unit) state of the epilogue threads, unit-major with a padded
+  // row count: the rows and units one wave covers fall in distinct banks
+  __shared__ float sh_h[NCOL * (NROW + 1)];
+  __shared__ float sh_c[NCOL * (NROW + 1)];
   __shared__ int s_fail;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -177,6 +179,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   const bool qw = q < Bact * U;             // writes the ring (zeros for padded units)
   const int qb = qw ? q / U : 0, qj = qw ? q - (q / U) * U : 0;
   const bool qv = qw && qj < Uact;          // a real (row, unit)
+  const int shix = qj * (NROW + 1) + qb;    // its slot in sh_h / sh_c
   const int qu = u0 + qj, qbg = b0 + qb;
   const size_t st_idx = (((size_t)li * D + d) * B + qbg) * H + qu;
   const size_t hx_idx = (((size_t)layer * D + d) * B + qbg) * H + qu;
@@ -190,15 +193,15 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     if (qv && live) {
       hv = p.h0 ? p.h0[hx_idx] : 0.f;
       cv = (MODE == MODE_LSTM && p.c0) ? p.c0[hx_idx] : 0.f;
-      sh_h[qb * NCOL + qj] = hv;
-      sh_c[qb * NCOL + qj] = cv;
+      sh_h[shix] = hv;
+      sh_c[shix] = cv;
     }
     const int first = p.wavefront ? li : 0;
     if (qw) ring_store<BF16>(ring + (size_t)first * p.ring_step, my_off, hv);
     if (p.persistent) publish(p.flags, 1u);
   } else if (qv && live) {
-    sh_h[qb * NCOL + qj] = p.st_h[st_idx];
-    if (MODE == MODE_LSTM) sh_c[qb * NCOL + qj] = p.st_c[st_idx];
+    sh_h[shix] = p.st_h[st_idx];
+    if (MODE == MODE_LSTM) sh_c[shix] = p.st_c[st_idx];
   }
   __syncthreads();
 
@@ -314,17 +317,17 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         }
         pre[gb] = v;
       }
-      const float hprev = sh_h[qb * NCOL + qj];
+      const float hprev = sh_h[shix];
       const bool tv = t < qlen;
       if (MODE == MODE_LSTM) {
         const float ig = sigmoidf_(pre[0] + gxv[0]);
         const float fg = sigmoidf_(pre[1] + gxv[1]);
         const float gg = tanhf_(pre[2] + gxv[2]);
         const float og = sigmoidf_(pre[3] + gxv[3]);
-        const float cprev = sh_c[qb * NCOL + qj];
+        const float cprev = sh_c[shix];
         const float cn = tv ? fg * cprev + ig * gg : cprev;
         hnew = og * tanhf_(cn);
-        sh_c[qb * NCOL + qj] = cn;
+        sh_c[shix] = cn;
         rv[0] = ig; rv[1] = fg; rv[2] = gg; rv[3] = og; rv[4] = cn;
       } else if (MODE == MODE_GRU) {
         const float rg = sigmoidf_(pre[0] + gxv[0]);
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         hnew = tanhf_(pre[0] + gxv[0]);
       }
       if (!tv) hnew = hprev;
-      sh_h[qb * NCOL + qj] = hnew;
+      sh_h[shix] = hnew;
     }
     // only the exchange store precedes the flag; y and the reserve are read
     // by later kernels, so they are written after it, off the critical path
@@ -359,11 +362,11 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
 
   if (qv && live) {
     if (p.s_end >= p.s_total) {
-      if (p.hy) p.hy[hx_idx] = sh_h[qb * NCOL + qj];
-      if (MODE == MODE_LSTM && p.cy) p.cy[hx_idx] = sh_c[qb * NCOL + qj];
+      if (p.hy) p.hy[hx_idx] = sh_h[shix];
+      if (MODE == MODE_LSTM && p.cy) p.cy[hx_idx] = sh_c[shix];
     } else {
-      p.st_h[st_idx] = sh_h[qb * NCOL + qj];
-      if (MODE == MODE_LSTM) p.st_c[st_idx] = sh_c[qb * NCOL + qj];
+      p.st_h[st_idx] = sh_h[shix];
+      if (MODE == MODE_LSTM) p.st_c[st_idx] = sh_c[shix];
     }
   }
 }
@@ -381,6 +384,8 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   // rows padded by 4 floats with one row tile: the four row groups of one
   // write instruction fall in distinct 16-bank groups
   __shared__ float red[NW][NROW][MT == 1 ? NCOL + 4 : NCOL + 1];
+  // per-(row, unit) state of the epilogue threads, row-major (with one
+  // 16-column tile the rows and units of a wave already fall in distinct banks)
   __shared__ float sh_dh[NROW * NCOL];
   __shared__ float sh_dc[NROW * NCOL];
   __shared__ int s_fail;
@@ -444,6 +449,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   const bool qw = q < Bact * U;
   const int qb = qw ? q / U : 0, qj = qw ? q - (q / U) * U : 0;
   const bool qv = qw && qj < Uact;
+  const int shix = qb * NCOL + qj;   // its slot in sh_dh / sh_dc
   const int qu = u0 + qj, qbg = b0 + qb;
   const size_t sidx = ((size_t)d * B + qbg) * H + qu;   // [D][B][H] state index
   // valid steps of this row (t < qlen); every step without lengths
@@ -453,11 +459,11 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   if (tid == 0) s_fail = 0;
   if (qv) {
     if (p.s_begin == 0) {
-      sh_dh[qb * NCOL + qj] = p.dhy ? p.dhy[sidx] : 0.f;
-      sh_dc[qb * NCOL + qj] = (MODE == MODE_LSTM && p.dcy) ? p.dcy[sidx] : 0.f;
+      sh_dh[shix] = p.dhy ? p.dhy[sidx] : 0.f;
+      sh_dc[shix] = (MODE == MODE_LSTM && p.dcy) ? p.dcy[sidx] : 0.f;
     } else {
-      sh_dh[qb * NCOL + qj] = p.st_dh[sidx];
-      if (MODE == MODE_LSTM) sh_dc[qb * NCOL + qj] = p.st_dc[sidx];
+      sh_dh[shix] = p.st_dh[sidx];
+      if (MODE == MODE_LSTM) sh_dc[shix] = p.st_dc[sidx];
     }
   }
   __syncthreads();
@@ -540,15 +546,15 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
     float dgi[4] = {0.f, 0.f, 0.f, 0.f}, dgh[4] = {0.f, 0.f, 0.f, 0.f};
     if (final_phase) {
       if (qv) {
-        if (p.dh0) p.dh0[sidx] = dhrec + sh_dh[qb * NCOL + qj];
-        if (MODE == MODE_LSTM && p.dc0) p.dc0[sidx] = sh_dc[qb * NCOL + qj];
+        if (p.dh0) p.dh0[sidx] = dhrec + sh_dh[shix];
+        if (MODE == MODE_LSTM && p.dc0) p.dc0[sidx] = sh_dc[shix];
       }
     } else {
       if (qv) {
         // a step past the row's length passes dh (and dc) through and
         // ignores dy; its gate gradients stay zero
         const bool tv = t < qlen;
-        const float dh = dhrec + (tv ? dyv : 0.f) + sh_dh[qb * NCOL + qj];
+        const float dh = dhrec + (tv ? dyv : 0.f) + sh_dh[shix];
         float ncarry = dh;
         if (!tv) {
         } else if (MODE == MODE_LSTM) {
@@ -556,14 +562,14 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
           const float ig = rv[0], fg = rv[1], gg = rv[2], og = rv[3], cc = rv[4];
           const float tau = tanhf_(cc);
           const float d_o = dh * tau;
-          const float dc = sh_dc[qb * NCOL + qj] + dh * og * (1.f - tau * tau);
+          const float dc = sh_dc[shix] + dh * og * (1.f - tau * tau);
           dgi[0] = dc * gg * ig * (1.f - ig);
           dgi[1] = dc * prevv * fg * (1.f - fg);
           dgi[2] = dc * ig * (1.f - gg * gg);
           dgi[3] = d_o * og * (1.f - og);
 #pragma unroll
           for (int g = 0; g < 4; ++g) dgh[g] = dgi[g];
-          sh_dc[qb * NCOL + qj] = dc * fg;
+          sh_dc[shix] = dc * fg;
         } else if (MODE == MODE_GRU) {
           const float rg = rv[0], zg = rv[1], ng = rv[2], ghn = rv[3];
           const float dn = dh * (1.f - zg);
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
           dgi[0] = dh * (1.f - hcur * hcur);
           dgh[0] = dgi[0];
         }
-        sh_dh[qb * NCOL + qj] = ncarry;
+        sh_dh[shix] = ncarry;
       }
       // only the exchange stores precede the flag
       if (qw) {
@@ -609,8 +615,8 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
     lds_barrier();   // red and sh_* are reused by the next step
   }
   if (qv && p.s_end <= T) {
-    p.st_dh[sidx] = sh_dh[qb * NCOL + qj];
-    if (MODE == MODE_LSTM) p.st_dc[sidx] = sh_dc[qb * NCOL + qj];
+    p.st_dh[sidx] = sh_dh[shix];
+    if (MODE == MODE_LSTM) p.st_dc[sidx] = sh_dc[shix];
   }
 }
 
