@@ -116,12 +116,23 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TransposeBatch bat
 // fp32 -> bf16 (round to nearest even).  Vector path (cols % 8 == 0 and every
 // row start 16-byte aligned on both sides): a thread converts 8 consecutive
 // elements with two 16-byte loads and one 16-byte store.
+// The first `fill_blocks` blocks of the launch set the fill ranges instead.
 __global__ void convert_kernel(const float* src, long long ld_src, uint16_t* dst, long long ld_dst,
-                               int rows, int cols, int vec) {
+                               int rows, int cols, int vec, const FillJob fill, int fill_blocks) {
+  if ((int)blockIdx.x < fill_blocks) {
+    const size_t t0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x, stride = (size_t)fill_blocks * blockDim.x;
+    for (int j = 0; j < fill.count; ++j) {
+      uint32_t* q = reinterpret_cast<uint32_t*>(fill.p[j]);
+      const size_t nw = fill.bytes[j] / 4;
+      for (size_t i = t0; i < nw; i += stride) q[i] = fill.v[j];
+    }
+    return;
+  }
+  const size_t bid = blockIdx.x - fill_blocks, nblk = gridDim.x - fill_blocks;
   if (vec) {
     const int cv = cols >> 3;
     const size_t n = (size_t)rows * cv;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    for (size_t i = bid * blockDim.x + threadIdx.x; i < n; i += nblk * blockDim.x) {
       const int r = (int)(i / (unsigned)cv), c = (int)(i - (size_t)r * cv) * 8;
       const float4* s4 = reinterpret_cast<const float4*>(src + (size_t)r * ld_src + c);
       const float4 a = s4[0], b = s4[1];
@@ -131,7 +142,7 @@ __global__ void convert_kernel(const float* src, long long ld_src, uint16_t* dst
     return;
   }
   const size_t n = (size_t)rows * cols;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+  for (size_t i = bid * blockDim.x + threadIdx.x; i < n; i += nblk * blockDim.x) {
     const size_t r = i / cols, c = i % cols;
     dst[r * ld_dst + c] = f2bf(src[r * ld_src + c]);
   }
@@ -236,13 +247,22 @@ hipError_t rnn_launch_transpose(const TransposeParams& p, int in_bf16, int out_b
 }
 
 hipError_t rnn_launch_convert(const float* src, long long ld_src, void* dst, long long ld_dst, int rows,
-                              int cols, hipStream_t s) {
-  if (rows <= 0 || cols <= 0) return hipSuccess;
+                              int cols, hipStream_t s, const FillJob* fill) {
+  FillJob f{};
+  size_t fill_bytes = 0;
+  if (fill) {
+    if (fill->count < 0 || fill->count > 4) return hipErrorInvalidValue;
+    f = *fill;
+    for (int j = 0; j < f.count; ++j) fill_bytes += f.bytes[j];
+  }
+  // enough fill blocks for the ranges (each thread sets a few words)
+  const int fill_blocks = fill_bytes ? (int)std::min<size_t>((fill_bytes / 4 + 1023) / 1024, 256) : 0;
+  if ((rows <= 0 || cols <= 0) && fill_blocks == 0) return hipSuccess;
   const int vec = cols % 8 == 0 && (uintptr_t)src % 16 == 0 && (uintptr_t)dst % 16 == 0 && ld_src % 4 == 0 &&
                   ld_dst % 8 == 0;
-  size_t n = (size_t)rows * cols / (vec ? 8 : 1);
-  unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 8192);
-  hipLaunchKernelGGL(convert_kernel, dim3(blocks), dim3(256), 0, s, src, ld_src,
-                     reinterpret_cast<uint16_t*>(dst), ld_dst, rows, cols, vec);
+  const size_t n = (rows > 0 && cols > 0) ? (size_t)rows * cols / (vec ? 8 : 1) : 0;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(convert_kernel, dim3(blocks + fill_blocks), dim3(256), 0, s, src, ld_src,
+                     reinterpret_cast<uint16_t*>(dst), ld_dst, rows, cols, vec, f, fill_blocks);
   return hipGetLastError();
 }

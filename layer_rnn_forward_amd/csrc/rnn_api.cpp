@@ -572,6 +572,24 @@ rnn_status_t fill_head(rnn_desc* h, hipStream_t s, void* head, void* flags = nul
   return dev(rnn_launch_fill(ptrs, bytes, vals, flags && flag_bytes ? 4 : 3, s));
 }
 
+// The same ranges as fill_head, for a launch that sets them alongside its
+// own job.
+FillJob head_fill_job(void* head, void* extra = nullptr, size_t extra_bytes = 0) {
+  char* c = reinterpret_cast<char*>(head);
+  FillJob f{};
+  void* ptrs[4] = {c, c + kOnesBf16, c + kOnesF32, extra};
+  size_t bytes[4] = {kOnesBf16, 64, 64, extra_bytes};
+  uint32_t vals[4] = {0u, 0x3f803f80u, 0x3f800000u, 0u};
+  for (int i = 0; i < 4; ++i)
+    if (ptrs[i] && bytes[i]) {
+      f.p[f.count] = ptrs[i];
+      f.bytes[f.count] = bytes[i];
+      f.v[f.count] = vals[i];
+      ++f.count;
+    }
+  return f;
+}
+
 // Constant vectors and the kernel choice of a GEMM on this workspace.
 void gemm_consts(const rnn_desc* h, GemmParams& g, const void* ws, size_t off_head) {
   const char* c = reinterpret_cast<const char*>(ws) + off_head;
@@ -593,8 +611,9 @@ const void* layer_w(const rnn_desc* h, const void* W, int which, int l) {
 // Hoisted input projection of layer l: GX[T*B, D*G*H] = in W_ih^T + b_ih + b_hh
 // (b_hh not folded into GRU's n gate, which needs it inside r*(.)).  The bf16
 // path first rounds the layer input to bf16 (the MFMA operand precision).
+// `pre` (bf16 only, optional): ranges the bf16 rounding launch also sets.
 rnn_status_t gemm_input(rnn_desc* h, hipStream_t s, const Plan& p, int l, const float* in,
-                        const void* W, float* gx, void* ws) {
+                        const void* W, float* gx, void* ws, const FillJob* pre = nullptr) {
   GemmParams g{};
   const int I_l = in_width(h, l);
   const bool bf = h->wtype == RNN_W_BF16;
@@ -607,7 +626,7 @@ rnn_status_t gemm_input(rnn_desc* h, hipStream_t s, const Plan& p, int l, const 
     void* xb = at<void>(ws, p.off_scr);
     {
       ProfScope ps(h, s, K_PREP);
-      RNN_TRY(dev(rnn_launch_convert(in, I_l, xb, ldx, g.M, I_l, s)));
+      RNN_TRY(dev(rnn_launch_convert(in, I_l, xb, ldx, g.M, I_l, s, pre)));
     }
     g.A[0] = xb;
     g.lda = ldx;
@@ -656,10 +675,17 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
   if (h->seq_ws == ws) h->seq_stage = 0;
 
-  // the first persistent sweep's flags are cleared with the head
+  // the first persistent sweep's flags are cleared with the head; with bf16
+  // operands both are set by the launch that rounds layer 0's input (one
+  // launch fewer per call)
   bool flags_clear = p.fwd.persistent && T > 0 && B > 0;
-  RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err), flags_clear ? at<void>(ws, p.off_flags) : nullptr,
-                    p.flags_bytes));
+  const bool head_in_convert = h->wtype == RNN_W_BF16 && T > 0 && B > 0;
+  const FillJob head_job = head_fill_job(at<void>(ws, p.off_err), flags_clear ? at<void>(ws, p.off_flags) : nullptr,
+                                         p.flags_bytes);
+  if (!head_in_convert)
+    RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err), flags_clear ? at<void>(ws, p.off_flags) : nullptr,
+                      p.flags_bytes));
+  const FillJob* pre = head_in_convert ? &head_job : nullptr;
   const size_t nstate = (size_t)h->L * h->D * B * h->H;
   if (T == 0 || B == 0) {
     if (hy) RNN_TRY(dev(rnn_copy_state(hy, h0, nstate, s)));
@@ -736,7 +762,7 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   };
 
   if (p.wavefront) {
-    RNN_TRY(gemm_input(h, s, p, 0, x, W, gx, ws));
+    RNN_TRY(gemm_input(h, s, p, 0, x, W, gx, ws, pre));
     f.wavefront = 1;
     if (p.drop_rings) {
       f.xch_drop = at<void>(ws, p.off_xch + (size_t)p.fwd.groups * p.fring_group);
@@ -774,7 +800,7 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
                                        h->drop_seed, l, drop, s)));
         in = xd;
       }
-      RNN_TRY(gemm_input(h, s, p, l, in, W, gx, ws));
+      RNN_TRY(gemm_input(h, s, p, l, in, W, gx, ws, l == 0 ? pre : nullptr));
       f.first_layer = l;
       f.gx = gx;
       f.w_ih[0] = layer_w(h, W, RNN_W_IH, l);

@@ -190,8 +190,18 @@ hipError_t rnn_launch_mfma_peak(int kind, int blocks, int iters, float* out, hip
 // One launch for 1..4 transposes of the same element types.
 hipError_t rnn_launch_transpose_batch(const rnnk::TransposeParams* ps, int n, int in_bf16, int out_bf16,
                                       hipStream_t s);
+// Up to four ranges to fill with 32-bit patterns in the same launch as
+// another job (bytes: multiples of 4; count 0: none).
+struct FillJob {
+  void* p[4];
+  unsigned long long bytes[4];
+  uint32_t v[4];
+  int count;
+};
+// fp32 -> bf16 (round to nearest even); `fill` (optional): ranges set by
+// the same launch (its first blocks), complete when the launch is
 hipError_t rnn_launch_convert(const float* src, long long ld_src, void* dst, long long ld_dst, int rows,
-                              int cols, hipStream_t s);   // fp32 -> bf16 (round to nearest even)
+                              int cols, hipStream_t s, const FillJob* fill = nullptr);
 // lds: dynamic LDS bytes (the ring-entry staging buffer, 0 when not staging)
 hipError_t rnn_launch_fwd(const rnnk::FwdParams& p, int mode, int bf16, const RecConfig& c,
                           int grid, size_t lds, hipStream_t s);
