@@ -47,14 +47,27 @@ __device__ __forceinline__ const char* src_row(const TransposeParams& p, int r) 
 // bf16 or two 16-byte fp32 accesses when p.vec_out).  Both flags are set by
 // the host only when every row start and the tile edges keep the accesses
 // aligned and inside the matrix; otherwise element accesses are used.
-// Up to four independent transposes in one launch (blockIdx.z selects one).
+// Up to four independent transposes in one launch (blockIdx.z selects one);
+// a z slice past them, if present, sets the fill ranges instead.
 struct TransposeBatch {
   TransposeParams p[4];
+  int n;          // transposes
+  FillJob fill;   // fill.count > 0: one more z slice
 };
 
 template <bool IN_BF, bool OUT_BF>
 __global__ __launch_bounds__(256) void transpose_kernel(const TransposeBatch batch) {
   __shared__ float tile[64][65];
+  if ((int)blockIdx.z >= batch.n) {
+    const size_t nb = (size_t)gridDim.x * gridDim.y;
+    const size_t t0 = ((size_t)blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    for (int j = 0; j < batch.fill.count; ++j) {
+      uint32_t* q = reinterpret_cast<uint32_t*>(batch.fill.p[j]);
+      const size_t nw = batch.fill.bytes[j] / 4;
+      for (size_t i = t0; i < nw; i += nb * blockDim.x) q[i] = batch.fill.v[j];
+    }
+    return;
+  }
   const TransposeParams& p = batch.p[blockIdx.z];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   if (r0 >= p.R || c0 >= p.C) return;   // the grid covers the largest job
@@ -214,9 +227,13 @@ hipError_t rnn_launch_mfma_peak(int kind, int blocks, int iters, float* out, hip
   return hipGetLastError();
 }
 
-hipError_t rnn_launch_transpose_batch(const TransposeParams* ps, int n, int in_bf16, int out_bf16, hipStream_t s) {
+hipError_t rnn_launch_transpose_batch(const TransposeParams* ps, int n, int in_bf16, int out_bf16, hipStream_t s,
+                                      const FillJob* fill) {
   if (n < 1 || n > 4) return hipErrorInvalidValue;
+  if (fill && (fill->count < 0 || fill->count > 4)) return hipErrorInvalidValue;
   TransposeBatch b{};
+  b.n = n;
+  if (fill) b.fill = *fill;
   int gx = 0, gy = 0;
   const uintptr_t ia = in_bf16 ? 8 : 16, es_in = in_bf16 ? 2 : 4, es_out = out_bf16 ? 2 : 4;
   auto al = [](const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; };
@@ -233,8 +250,13 @@ hipError_t rnn_launch_transpose_batch(const TransposeParams* ps, int n, int in_b
       gy = std::max(gy, (q.R + 63) / 64);
     }
   }
+  const int nz = n + (b.fill.count > 0 ? 1 : 0);
+  if (b.fill.count > 0) {   // the fill slice needs a grid of at least one block
+    gx = std::max(gx, 1);
+    gy = std::max(gy, 1);
+  }
   if (gx == 0 || gy == 0) return hipSuccess;
-  dim3 grid(gx, gy, n);
+  dim3 grid(gx, gy, nz);
   if (in_bf16 && out_bf16) hipLaunchKernelGGL((transpose_kernel<true, true>), grid, dim3(256), 0, s, b);
   else if (in_bf16 && !out_bf16) hipLaunchKernelGGL((transpose_kernel<true, false>), grid, dim3(256), 0, s, b);
   else if (!in_bf16 && out_bf16) hipLaunchKernelGGL((transpose_kernel<false, true>), grid, dim3(256), 0, s, b);
@@ -242,8 +264,9 @@ hipError_t rnn_launch_transpose_batch(const TransposeParams* ps, int n, int in_b
   return hipGetLastError();
 }
 
-hipError_t rnn_launch_transpose(const TransposeParams& p, int in_bf16, int out_bf16, hipStream_t s) {
-  return rnn_launch_transpose_batch(&p, 1, in_bf16, out_bf16, s);
+hipError_t rnn_launch_transpose(const TransposeParams& p, int in_bf16, int out_bf16, hipStream_t s,
+                                const FillJob* fill) {
+  return rnn_launch_transpose_batch(&p, 1, in_bf16, out_bf16, s, fill);
 }
 
 hipError_t rnn_launch_convert(const float* src, long long ld_src, void* dst, long long ld_dst, int rows,

@@ -995,9 +995,16 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
   Plan p = make_plan(h, T, B, 1, h->seq_drop_p);
   if (p.status != RNN_STATUS_SUCCESS) return p.status;
   if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
+  // the head and the first sweep's flags are set by the launch that
+  // transposes the top layer's W_ih (it depends on nothing the sweep makes,
+  // so it runs before the sweep): one launch fewer per call
   bool flags_clear = p.bwd.persistent && T > 0 && B > 0;
-  RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err), flags_clear ? at<void>(ws, p.off_flags) : nullptr,
-                    p.flags_bytes));
+  const bool head_in_transpose = T > 0 && B > 0;
+  const FillJob head_job = head_fill_job(at<void>(ws, p.off_err), flags_clear ? at<void>(ws, p.off_flags) : nullptr,
+                                         p.flags_bytes);
+  if (!head_in_transpose)
+    RNN_TRY(fill_head(h, s, at<void>(ws, p.off_err), flags_clear ? at<void>(ws, p.off_flags) : nullptr,
+                      p.flags_bytes));
   const size_t nstate = (size_t)h->L * h->D * B * h->H;
   if (T == 0 || B == 0) {
     if (dh0) RNN_TRY(dev(rnn_copy_state(dh0, dhy, nstate, s)));
@@ -1043,6 +1050,21 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
   b.flags = at<unsigned>(ws, p.off_flags);
   b.err = at<unsigned>(ws, p.off_err);
   b.spin_limit = spin_limit();
+  // W_ih^T [I_l][dg_ld] in the scratch, the B operand of layer l's dX product
+  void* wT = at<void>(ws, p.off_scr);
+  auto transpose_w = [&](int l, const FillJob* fill) -> rnn_status_t {
+    TransposeParams tp{};
+    tp.src = layer_w(h, W, RNN_W_IH, l);
+    tp.ld_src = in_width(h, l);
+    tp.alt_r0 = tp.alt_r1 = 0;
+    tp.out = wT;
+    tp.ld_out = p.dg_ld;
+    tp.R = (int)dgh;
+    tp.C = in_width(h, l);
+    ProfScope ps(h, s, K_PREP);
+    return dev(rnn_launch_transpose(tp, bf, bf, s, fill));
+  };
+  if (head_in_transpose) RNN_TRY(transpose_w(h->L - 1, &head_job));
   for (int l = h->L - 1; l >= 0; --l) {
     b.w_hh = layer_w(h, W, RNN_W_HH, l);
     b.reserve = at<float>(ws, p.off_res + p.res_layer * l);
@@ -1077,20 +1099,9 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
       }
     }
     // dX_l = dG_i W_ih  (both directions in one product, K = D*G*H); B = W_ih^T
+    // (the top layer's was transposed before its sweep)
     const int I_l = in_width(h, l);
-    void* wT = at<void>(ws, p.off_scr);
-    {
-      TransposeParams tp{};
-      tp.src = layer_w(h, W, RNN_W_IH, l);
-      tp.ld_src = I_l;
-      tp.alt_r0 = tp.alt_r1 = 0;
-      tp.out = wT;
-      tp.ld_out = p.dg_ld;
-      tp.R = (int)dgh;
-      tp.C = I_l;
-      ProfScope ps(h, s, K_PREP);
-      RNN_TRY(dev(rnn_launch_transpose(tp, bf, bf, s)));
-    }
+    if (!(head_in_transpose && l == h->L - 1)) RNN_TRY(transpose_w(l, nullptr));
     GemmParams g{};
     g.M = T * B;
     g.N = I_l;

@@ -181,15 +181,10 @@ struct RecConfig {
 
 // Launchers (defined in the .hip files).  Return hipSuccess or the launch error.
 hipError_t rnn_launch_gemm(const rnnk::GemmParams& p, int bf16, int epi, int batches, hipStream_t s);
-// in_bf16 / out_bf16: element types of src (and alt) / out.
-hipError_t rnn_launch_transpose(const rnnk::TransposeParams& p, int in_bf16, int out_bf16, hipStream_t s);
 // Dense MFMA throughput probe: `blocks` workgroups of 256 threads, `iters`
 // rounds of eight independent MFMA chains per wave; one float per thread.
 // kind 0: fp32 16x16x4, 1: bf16 16x16x32, 2: bf16 32x32x16.
 hipError_t rnn_launch_mfma_peak(int kind, int blocks, int iters, float* out, hipStream_t s);
-// One launch for 1..4 transposes of the same element types.
-hipError_t rnn_launch_transpose_batch(const rnnk::TransposeParams* ps, int n, int in_bf16, int out_bf16,
-                                      hipStream_t s);
 // Up to four ranges to fill with 32-bit patterns in the same launch as
 // another job (bytes: multiples of 4; count 0: none).
 struct FillJob {
@@ -198,6 +193,14 @@ struct FillJob {
   uint32_t v[4];
   int count;
 };
+// Transposes; in_bf16 / out_bf16: element types of src (and alt) / out;
+// `fill` (optional): ranges set by one more z slice of the same launch,
+// complete when the launch is.
+hipError_t rnn_launch_transpose(const rnnk::TransposeParams& p, int in_bf16, int out_bf16, hipStream_t s,
+                                const FillJob* fill = nullptr);
+// One launch for 1..4 transposes of the same element types.
+hipError_t rnn_launch_transpose_batch(const rnnk::TransposeParams* ps, int n, int in_bf16, int out_bf16,
+                                      hipStream_t s, const FillJob* fill = nullptr);
 // fp32 -> bf16 (round to nearest even); `fill` (optional): ranges set by
 // the same launch (its first blocks), complete when the launch is
 hipError_t rnn_launch_convert(const float* src, long long ld_src, void* dst, long long ld_dst, int rows,
