@@ -450,6 +450,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   const int qb = qw ? q / U : 0, qj = qw ? q - (q / U) * U : 0;
   const bool qv = qw && qj < Uact;
   const int shix = qb * NCOL + qj;   // its slot in sh_dh / sh_dc
+  const bool w0 = Bact * U <= 64;     // every ring store is made by wave 0
   const int qu = u0 + qj, qbg = b0 + qb;
   const size_t sidx = ((size_t)d * B + qbg) * H + qu;   // [D][B][H] state index
   // valid steps of this row (t < qlen); every step without lengths
@@ -596,7 +597,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
         for (int g = 0; g < G; ++g) ring_store<BF16>(en, my_off + (size_t)g * UJ * gran, dgh[g]);
       }
     }
-    if (p.persistent && !final_phase) publish(p.flags, (unsigned)(s + 1));
+    if (p.persistent && !final_phase) publish(p.flags, (unsigned)(s + 1), w0);
     if (!final_phase && qv) {
       // gate gradients for the dX product ([T*B, D*G*H]) and, transposed
       // ([D*G*H, T*B]), for the weight-gradient products (later kernels)

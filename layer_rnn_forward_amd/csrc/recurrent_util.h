@@ -93,8 +93,18 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Every wave waits for completion of its stores (the ring stores are agent
-// scope), then one thread publishes the flag.
-__device__ __forceinline__ void publish(unsigned* flags, unsigned v) {
+// scope), then one thread publishes the flag.  `wave0_only`: every ring store
+// of the step was made by wave 0, so wave 0 alone waits for them and
+// publishes, with no workgroup barrier before the flag (the other waves meet
+// wave 0 again at the step's closing LDS barrier).
+__device__ __forceinline__ void publish(unsigned* flags, unsigned v, bool wave0_only = false) {
+  if (wave0_only) {
+    if (threadIdx.x < 64) {
+      __builtin_amdgcn_s_waitcnt(0);
+      if (threadIdx.x == 0) flag_store(flags + (size_t)blockIdx.x * kFlagStride, v);
+    }
+    return;
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) flag_store(flags + (size_t)blockIdx.x * kFlagStride, v);
