@@ -180,6 +180,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   const int qb = qw ? q / U : 0, qj = qw ? q - (q / U) * U : 0;
   const bool qv = qw && qj < Uact;          // a real (row, unit)
   const int shix = qj * (NROW + 1) + qb;    // its slot in sh_h / sh_c
+  const bool w0 = Bact * U <= 64;           // every ring store is made by wave 0
   const int qu = u0 + qj, qbg = b0 + qb;
   const size_t st_idx = (((size_t)li * D + d) * B + qbg) * H + qu;
   const size_t hx_idx = (((size_t)layer * D + d) * B + qbg) * H + qu;
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     // by later kernels, so they are written after it, off the critical path
     if (qw) ring_store<BF16>(ring + (size_t)(s + 1) * p.ring_step, my_off, hnew);
     if (qw && drop_out) ring_store<BF16>(ring_drop + (size_t)(s + 1) * p.ring_step, my_off, hnew * dmul);
-    if (p.persistent) publish(p.flags, (unsigned)(s + 2));
+    if (p.persistent) publish(p.flags, (unsigned)(s + 2), w0);
     if (qv && live) {
       p.y[li][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = t < qlen ? hnew : 0.f;
       if (p.training && R > 0) {
