@@ -67,19 +67,27 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   // is XORed with (row ^ row / 4) % 4 in unpadded rows (the epilogue's four
   // batch rows then fall apart too; measured 49 % -> 2 % conflict cycles);
   // with one or two column tiles and one row tile rows are padded by 4
-  // floats (4 * stride = 16 banks mod 64); the two-row-tile kernels, which
-  // spill, keep a padding of 1 (slower with the others)
+  // floats (4 * stride = 16 banks mod 64); with two column tiles the
+  // 8-column block of (row, col) in unpadded rows is XORed with
+  // (bit 1 of row) | (bit 0 ^ bit 2 of row) << 1, which keeps the two rows
+  // of each half-wave write and the four rows of 8 units each half-wave of
+  // the epilogue reads per gate in distinct banks (counters: 27 % -> 0 %
+  // conflict cycles); the two-row-tile kernels, which spill, keep a padding
+  // of 1 (slower with the others)
   constexpr bool RSWZ = NT == 4 && MT == 1;
-  constexpr int RSTR = RSWZ ? NCOL : (MT == 1 ? NCOL + 4 : NCOL + 1);
+  constexpr bool RSWZ2 = NT == 2 && MT == 1;
+  constexpr int RSTR = (RSWZ || RSWZ2) ? NCOL : (MT == 1 ? NCOL + 4 : NCOL + 1);
   __shared__ float red[NW][NROW][RSTR];
   auto rcol = [](int row, int col) {
     if constexpr (RSWZ) return col ^ ((((row ^ (row >> 2)) & 3)) << 4);
+    else if constexpr (RSWZ2) return col ^ ((((row >> 1) & 1) | (((row ^ (row >> 2)) & 1) << 1)) << 3);
     else return col;
   };
-  // per-(row, unit) state of the epilogue threads, unit-major with a padded
-  // row count: the rows and units one wave covers fall in distinct banks
-  __shared__ float sh_h[NCOL * (NROW + 1)];
-  __shared__ float sh_c[NCOL * (NROW + 1)];
+  // per-(row, unit) state of the epilogue threads, indexed by the thread
+  // (row-major with the workgroup's unit count as stride): one wave's
+  // accesses are consecutive words
+  __shared__ float sh_h[NCOL * NROW];
+  __shared__ float sh_c[NCOL * NROW];
   __shared__ int s_fail;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   const bool qw = q < Bact * U;             // writes the ring (zeros for padded units)
   const int qb = qw ? q / U : 0, qj = qw ? q - (q / U) * U : 0;
   const bool qv = qw && qj < Uact;          // a real (row, unit)
-  const int shix = qj * (NROW + 1) + qb;    // its slot in sh_h / sh_c
+  const int shix = qw ? q : 0;              // its slot in sh_h / sh_c (qb * U + qj)
   const bool w0 = Bact * U <= 64;           // every ring store is made by wave 0
   const int qu = u0 + qj, qbg = b0 + qb;
   const size_t st_idx = (((size_t)li * D + d) * B + qbg) * H + qu;
