@@ -67,15 +67,16 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   // is XORed with (row ^ row / 4) % 4 in unpadded rows (the epilogue's four
   // batch rows then fall apart too; measured 49 % -> 2 % conflict cycles);
   // with one or two column tiles and one row tile rows are padded by 4
-  // floats (4 * stride = 16 banks mod 64); with two column tiles the
-  // 8-column block of (row, col) in unpadded rows is XORed with
+  // floats (4 * stride = 16 banks mod 64); with two column tiles and bf16
+  // weights the 8-column block of (row, col) in unpadded rows is XORed with
   // (bit 1 of row) | (bit 0 ^ bit 2 of row) << 1, which keeps the two rows
   // of each half-wave write and the four rows of 8 units each half-wave of
   // the epilogue reads per gate in distinct banks (counters: 27 % -> 0 %
-  // conflict cycles); the two-row-tile kernels, which spill, keep a padding
-  // of 1 (slower with the others)
+  // conflict cycles; the fp32-weight kernel, at the register limit, measured
+  // 4 % slower with it and keeps the padding); the two-row-tile kernels,
+  // which spill, keep a padding of 1 (slower with the others)
   constexpr bool RSWZ = NT == 4 && MT == 1;
-  constexpr bool RSWZ2 = NT == 2 && MT == 1;
+  constexpr bool RSWZ2 = BF16 && NT == 2 && MT == 1;
   constexpr int RSTR = (RSWZ || RSWZ2) ? NCOL : (MT == 1 ? NCOL + 4 : NCOL + 1);
   __shared__ float red[NW][NROW][RSTR];
   auto rcol = [](int row, int col) {
