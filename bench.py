@@ -154,20 +154,43 @@ def cpu_baseline(w, synth, min_seconds):
     except Exception:
         pass
     return {"value": round(f / dt / 1e9, 3), "unit": "GFLOP/s", "cores": cores or os.cpu_count(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"{w.name}: {reps} full training step(s) (T={w.T}) in fp64 on the host, "
                       f"forward + backward through time + weight gradients, {dt:.1f} s"}
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when the kernel sources changed since it was taken."""
-    import glob
+def source_hash():
+    """sha256[:16] over every native source of the library (kernels, their
+    headers and the host planner, which decides grids and layouts) and the
+    public header: a counter figure taken under another hash is stale."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(root, "layer_rnn_forward_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in ("recurrent.hip", "gemm.hip"))
-    h = hashlib.sha256(src).hexdigest()[:16]
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".cpp")))
+    files.append(os.path.join(root, "include", "rnn.h"))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the library sources changed since it was taken."""
+    import glob
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = source_hash()
     for path in glob.glob(os.path.join(root, "profiles", "traffic_*.txt")):
         for line in open(path):
             parts = line.split()
@@ -237,6 +260,131 @@ def blas_reference(torch, w, reps=50):
     return out
 
 
+GATES = {"rnn_tanh": 1, "lstm": 4, "gru": 3, "gru_tf": 3, "gru_paper": 3}
+
+# stacked and GRU workloads reported next to the headline (one GPU, same step)
+SECONDARY = ("gru_ds2_f32", "lstm_ds2_l5_bi_bf16", "gru_ds2_l5_bi_bf16", "tanh_ds2_l5_bi_bf16",
+             "lstm_ds2_l5_uni_bf16")
+
+
+def kernel_flops(w):
+    """Algorithmic GEMM flops per training step of each kernel kind (2*M*N*K
+    summed over layers; the bias-gradient ones column is not counted)."""
+    G, T, B, H, D = GATES[w.mode], w.T, w.B, w.hidden, w.dirs
+    f = {"gemm_input": 0.0, "gemm_dx": 0.0, "gemm_dw": 0.0, "recurrent_fwd": 0.0, "recurrent_bwd": 0.0}
+    for l in range(w.layers):
+        I_l = w.input_size if l == 0 else D * H
+        f["gemm_input"] += 2.0 * T * B * D * G * H * I_l
+        f["gemm_dx"] += 2.0 * T * B * D * G * H * I_l
+        f["gemm_dw"] += 2.0 * T * B * D * G * H * (I_l + H)
+        f["recurrent_fwd"] += 2.0 * T * B * D * G * H * H
+        f["recurrent_bwd"] += 2.0 * T * B * D * G * H * H
+    return f
+
+
+def timed_region(torch, fn, steps, warmup):
+    """W untimed steps, then exactly K steps bracketed by synchronisations:
+    (ms per step from events around the K steps, wall seconds)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps, time.perf_counter() - t0
+
+
+def kernel_breakdown(run, torch, R, steps):
+    """Per-kernel launch times from the HIP events the library records on the
+    caller's stream around each launch (a separate pass: the events are off
+    while the headline is timed)."""
+    R.rnn_set_profiling(run.h, True)
+    for _ in range(steps):
+        run.train_step()
+    torch.cuda.synchronize()
+    kern = {}
+    for k, name in enumerate(R.KERNEL_NAMES):
+        n, ms = R.rnn_profile_read(run.h, k)
+        if n:
+            kern[name] = {"launches": n, "avg_us": round(1000 * ms / n, 3), "total_ms": round(ms, 3)}
+    R.rnn_set_profiling(run.h, False)
+    assert R.rnn_device_status(run.h, run.ws) == 0
+    return kern
+
+
+def exchange_floor(run, w, R, reps):
+    """The training forward sweep's launch with only its exchange (flag
+    waits, ring stores, flags), per step: the recurrence's latency floor."""
+    try:
+        R.rnn_set_profiling(run.h, True)
+        for _ in range(reps):
+            R.rnn_exchange_floor(run.h, w.T, w.B, run.ws, training=True)
+        n_p, ms_p = R.rnn_profile_read(run.h, R.KERNEL_NAMES.index("exchange_probe"))
+        R.rnn_set_profiling(run.h, False)
+        assert R.rnn_device_status(run.h, run.ws) == 0
+        steps_per_sweep = w.T + (w.layers - 1 if w.dirs == 1 and w.layers > 1 else 0)
+        return 1000.0 * ms_p / n_p / steps_per_sweep
+    except R.RNNError:   # the sweep could not run persistently
+        R.rnn_set_profiling(run.h, False)
+        return None
+
+
+def kernel_rooflines(w, kern, steps, floor_us):
+    """One entry per kernel kind: the time-parallel products against the
+    dense MFMA peak of their operand type; the recurrent sweeps, bound by
+    their per-step latency, against the measured exchange floor (their
+    fraction of the MFMA peak is given too)."""
+    peak = PEAK_TFLOPS[w.wtype]
+    fl = kernel_flops(w)
+    sweeps_per_step = {"recurrent_fwd": 1 if (w.dirs == 1 and w.layers > 1) else w.layers,
+                       "recurrent_bwd": w.layers}
+    out = {}
+    for name, f in fl.items():
+        k = kern.get(name)
+        if not k:
+            continue
+        t_step = k["total_ms"] / steps * 1e-3    # seconds of this kernel kind per training step
+        achieved = f / t_step / 1e12
+        e = {"achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+             "frac_mfma_peak": round(achieved / peak, 5), "avg_launch_us": k["avg_us"],
+             "launches_per_step": round(k["launches"] / steps, 2), "flops_per_step": f}
+        if name.startswith("recurrent"):
+            steps_per_sweep = w.T + (w.layers - 1 if name == "recurrent_fwd" and w.dirs == 1 and w.layers > 1 else 0)
+            us_step = k["total_ms"] / steps * 1000.0 / sweeps_per_step[name] / steps_per_sweep
+            e.update(bound="latency", us_per_recurrent_step=round(us_step, 3))
+            if floor_us:
+                e.update(exchange_floor_us_per_step=round(floor_us, 3),
+                         frac_of_latency_floor=round(floor_us / us_step, 4))
+        else:
+            e["bound"] = "mfma"
+        out[name] = e
+    return out
+
+
+def measure(w, torch, R, synth, steps, warmup, dropout=0.0, detail=True):
+    run = Runner(w, torch, R, synth, dropout=dropout)
+    F_train = 3 * flops(w.mode, w.T, w.B, w.input_size, w.hidden, w.layers, w.dirs)
+    fwd_ms, _ = run.timed(run.fwd, max(5, steps // 2), warmup)
+    T_ms, wall = timed_region(torch, run.train_step, steps, warmup)
+    assert R.rnn_device_status(run.h, run.ws) == 0
+    value = F_train / (T_ms * 1e-3) / 1e9
+    r = {"value": round(value, 3), "ms_per_step": round(T_ms, 4), "wall_s": round(wall, 4),
+         "fwd_ms": round(float(np.median(fwd_ms)), 4),
+         "pct_mfma_peak": round(100.0 * value / (PEAK_TFLOPS[w.wtype] * 1000.0), 4)}
+    if not detail:
+        return run, r
+    step_ms, _ = run.timed(run.train_step, steps, 0)   # per-step spread (events per step)
+    r["train_step_ms_p10_p50_p90"] = [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)]
+    r["kernels"] = kernel_breakdown(run, torch, R, steps)
+    r["plan"] = R.rnn_plan_info(run.h, w.T, w.B, True)
+    return run, r
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -248,6 +396,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-fp32", action="store_true")
     ap.add_argument("--no-small-batch", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the stacked / GRU workloads reported next to the headline")
     ap.add_argument("--blas-reference", action="store_true",
                     help="also time the vendor BLAS on the same GEMM shapes (context only)")
     ap.add_argument("--dropout", type=float, default=0.0,
@@ -266,78 +416,41 @@ def main():
     from layer_rnn_forward_amd import synth
 
     w = synth.WORKLOADS[args.workload]
-    run = Runner(w, torch, R, synth, dropout=args.dropout)
-    F_train = 3 * flops(w.mode, w.T, w.B, w.input_size, w.hidden, w.layers, w.dirs)
-    F_fwd = flops(w.mode, w.T, w.B, w.input_size, w.hidden, w.layers, w.dirs)
-
-    # forward-inference latency
-    fwd_ms, _ = run.timed(run.fwd, max(5, args.steps // 2), args.warmup)
-    # training steps, per-kernel HIP events recorded by the library on this stream
-    for _ in range(args.warmup):
-        run.train_step()
-    torch.cuda.synchronize()
-    R.rnn_set_profiling(run.h, True)
-    step_ms, wall = run.timed(run.train_step, args.steps, 0)
-    kern = {}
-    for k, name in enumerate(R.KERNEL_NAMES):
-        n, ms = R.rnn_profile_read(run.h, k)
-        if n:
-            kern[name] = {"launches": n, "avg_us": round(1000 * ms / n, 3), "total_ms": round(ms, 3)}
-    R.rnn_set_profiling(run.h, False)
-    assert R.rnn_device_status(run.h, run.ws) == 0
-
-    # latency floor of the recurrence: the training forward sweep's launch
-    # with only its exchange (flag waits, ring stores, flags), no arithmetic
-    exchange = None
-    try:
-        R.rnn_set_profiling(run.h, True)
-        for _ in range(max(3, args.steps // 4)):
-            R.rnn_exchange_floor(run.h, w.T, w.B, run.ws, training=True)
-        n_p, ms_p = R.rnn_profile_read(run.h, R.KERNEL_NAMES.index("exchange_probe"))
-        R.rnn_set_profiling(run.h, False)
-        assert R.rnn_device_status(run.h, run.ws) == 0
-        steps_per_sweep = w.T + (w.layers - 1 if w.dirs == 1 and w.layers > 1 else 0)
-        floor = 1000.0 * ms_p / n_p / steps_per_sweep
-        fwd_step = kern["recurrent_fwd"]["avg_us"] / steps_per_sweep
-        exchange = {"floor_us_per_step": round(floor, 3), "recurrent_fwd_us_per_step": round(fwd_step, 3),
-                    "floor_fraction_of_step": round(floor / fwd_step, 4)}
-    except R.RNNError as e:   # the sweep could not run persistently
-        R.rnn_set_profiling(run.h, False)
-        exchange = {"error": str(e)}
-
-    T_ms = float(np.mean(step_ms))
-    value = F_train / (T_ms * 1e-3) / 1e9
+    run, m = measure(w, torch, R, synth, args.steps, args.warmup, dropout=args.dropout)
+    kern = m["kernels"]
+    floor = exchange_floor(run, w, R, max(3, args.steps // 4))
     peak = PEAK_TFLOPS[w.wtype]
-    # dominant kernel: the one with the largest total time
-    dom = max(kern.items(), key=lambda kv: kv[1]["total_ms"])
-    G = {"rnn_tanh": 1, "lstm": 4, "gru": 3, "gru_tf": 3, "gru_paper": 3}[w.mode]
-    per_launch_flops = {
-        "recurrent_fwd": 2.0 * w.T * w.B * G * w.hidden * w.hidden * w.dirs,
-        "recurrent_bwd": 2.0 * w.T * w.B * G * w.hidden * w.hidden * w.dirs,
-        "gemm_input": 2.0 * w.T * w.B * G * w.hidden * w.input_size * w.dirs,
-        "gemm_dx": 2.0 * w.T * w.B * G * w.hidden * w.input_size * w.dirs,
-    }
-    dname, dk = dom
-    launches_per_step = dk["launches"] / args.steps
-    if dname in per_launch_flops and w.layers == 1:
-        achieved = per_launch_flops[dname] / (dk["avg_us"] * 1e-6) / 1e12
+    roofs = kernel_rooflines(w, kern, args.steps, floor)
+
+    # the dominant kernel: the kind with the largest total time
+    dname, dk = max(kern.items(), key=lambda kv: kv[1]["total_ms"])
+    fl = kernel_flops(w)
+    if dname in fl:
+        per_launch = fl[dname] * args.steps / dk["launches"]
+        achieved = per_launch / (dk["avg_us"] * 1e-6) / 1e12
         roof = {"kernel": dname, "bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 5),
                 "traffic": measured_traffic(dname) if w.name == "lstm_ds2_bf16" else None,
-                "avg_launch_us": dk["avg_us"],
-                "algorithmic_flops_per_launch": per_launch_flops[dname]}
+                "avg_launch_us": dk["avg_us"], "algorithmic_flops_per_launch": per_launch}
+        if dname.startswith("recurrent"):
+            # a step-serial recurrence: its time is set by the per-step latency
+            # (exchange round trip, fragment loads, cell math), not by MFMA or
+            # HBM throughput; the MFMA fraction above is the contract's figure
+            roof["limiter"] = "per-step latency of the recurrence (exchange-bound)"
+            roof["us_per_recurrent_step"] = roofs[dname]["us_per_recurrent_step"]
+            roof["exchange_floor_us_per_step"] = round(floor, 3) if floor else None
     else:
-        roof = {"kernel": dname, "bound": "mfma", "achieved": None, "peak": peak,
-                "unit": "TFLOP/s", "frac": None, "traffic": None, "avg_launch_us": dk["avg_us"]}
+        roof = {"kernel": dname, "bound": "mfma", "achieved": None, "peak": peak, "unit": "TFLOP/s",
+                "frac": None, "traffic": None, "avg_launch_us": dk["avg_us"]}
 
     out = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": m["value"],
         "unit": "GFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(T_ms, 4),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -346,24 +459,32 @@ def main():
         "config": {"workload": w.name, "mode": w.mode, "layers": w.layers, "dirs": w.dirs,
                    "T": w.T, "B": w.B, "input": w.input_size, "hidden": w.hidden,
                    "weights": w.wtype, "state_accum": "f32", "dropout": args.dropout},
-        "fwd_ms": round(float(np.median(fwd_ms)), 4),
-        "pct_mfma_peak": round(100.0 * value / (peak * 1000.0), 4),
-        "train_step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)],
+        "fwd_ms": m["fwd_ms"],
+        "pct_mfma_peak": m["pct_mfma_peak"],
+        "timed_wall_s": m["wall_s"],
+        "train_step_ms_p10_p50_p90": m["train_step_ms_p10_p50_p90"],
         "kernels": kern,
         "roofline": roof,
-        "exchange_floor": exchange,
+        "kernel_rooflines": roofs,
+        "plan": m["plan"],
+        "source_sha16": source_hash(),
     }
+    if floor:
+        fwd_step = roofs["recurrent_fwd"]["us_per_recurrent_step"]
+        out["exchange_floor"] = {"floor_us_per_step": round(floor, 3), "recurrent_fwd_us_per_step": fwd_step,
+                                 "floor_fraction_of_step": round(floor / fwd_step, 4)}
     # measured denominators next to the published peaks
     probes = {k: mfma_peak(torch, R, k) for k in R.MFMA_PROBES}
     meas = {"bf16": max(probes["bf16_16x16x32"], probes["bf16_32x32x16"]), "f32": probes["f32_16x16x4"]}
     out["mfma_peak_measured"] = {**{f"{k}_TFLOPs": round(v, 1) for k, v in probes.items()},
                                  "published_bf16_TFLOPs": PEAK_TFLOPS["bf16"],
                                  "published_f32_TFLOPs": PEAK_TFLOPS["f32"]}
-    out["pct_measured_mfma_peak"] = round(100.0 * value / (meas[w.wtype] * 1000.0), 4)
+    out["pct_measured_mfma_peak"] = round(100.0 * m["value"] / (meas[w.wtype] * 1000.0), 4)
     if args.dropout == 0.0:   # (a captured step would replay one dropout seed)
         try:
             g_ms = run.graph_timed(args.steps, args.warmup)
             assert R.rnn_device_status(run.h, run.ws) == 0
+            F_train = 3 * flops(w.mode, w.T, w.B, w.input_size, w.hidden, w.layers, w.dirs)
             out["graph_replay"] = {"ms_per_step": round(g_ms, 4),
                                    "value": round(F_train / (g_ms * 1e-3) / 1e9, 3), "unit": "GFLOP/s",
                                    "note": "the same training step captured once into a HIP graph and replayed"}
@@ -376,18 +497,30 @@ def main():
         gbs = 8.0 * n_el / (kern["dropout"]["avg_us"] * 1e-6) / 1e9
         out["dropout_pass"] = {"avg_us": kern["dropout"]["avg_us"], "bytes_per_launch": 8 * n_el,
                                "achieved_GBs": round(gbs, 1), "frac_hbm": round(gbs / HBM_GBS, 4)}
+    del run
     if not args.no_fp32 and w.wtype == "bf16" and args.dropout == 0.0:
         w32 = synth.WORKLOADS.get(args.workload.replace("bf16", "f32"))
         if w32 is not None:
-            r32 = Runner(w32, torch, R, synth)
-            f_ms, _ = r32.timed(r32.fwd, max(5, args.steps // 2), args.warmup)
-            s_ms, _ = r32.timed(r32.train_step, args.steps, args.warmup)
-            v32 = F_train / (float(np.mean(s_ms)) * 1e-3) / 1e9
-            out["fp32_weights"] = {"value": round(v32, 3), "unit": "GFLOP/s",
-                                   "ms_per_step": round(float(np.mean(s_ms)), 4),
-                                   "fwd_ms": round(float(np.median(f_ms)), 4),
-                                   "pct_mfma_peak": round(100.0 * v32 / (PEAK_TFLOPS["f32"] * 1000), 4),
-                                   "pct_measured_mfma_peak": round(100.0 * v32 / (meas["f32"] * 1000), 4)}
+            r32, m32 = measure(w32, torch, R, synth, args.steps, args.warmup, detail=False)
+            del r32
+            out["fp32_weights"] = {"value": m32["value"], "unit": "GFLOP/s", "ms_per_step": m32["ms_per_step"],
+                                   "fwd_ms": m32["fwd_ms"], "pct_mfma_peak": m32["pct_mfma_peak"],
+                                   "pct_measured_mfma_peak": round(100.0 * m32["value"] / (meas["f32"] * 1000), 4)}
+    if not args.no_secondary and args.workload == "lstm_ds2_bf16" and args.dropout == 0.0:
+        # the other workloads: GRU, 5-layer bidirectional stacks, the
+        # unidirectional 5-layer stack (layer wavefront); same step and timing
+        sec = {}
+        for name in SECONDARY:
+            ws_ = synth.WORKLOADS[name]
+            r2, m2 = measure(ws_, torch, R, synth, max(5, args.steps // 2), args.warmup, detail=False)
+            k2 = kernel_breakdown(r2, torch, R, 3)
+            del r2
+            sec[name] = {"mode": ws_.mode, "layers": ws_.layers, "dirs": ws_.dirs, "weights": ws_.wtype,
+                         "value": m2["value"], "unit": "GFLOP/s", "ms_per_step": m2["ms_per_step"],
+                         "fwd_ms": m2["fwd_ms"], "pct_mfma_peak": m2["pct_mfma_peak"],
+                         "pct_measured_mfma_peak": round(100.0 * m2["value"] / (meas[ws_.wtype] * 1000.0), 4),
+                         "kernel_ms_per_step": {k: round(v["total_ms"] / 3, 4) for k, v in k2.items()}}
+        out["workloads"] = sec
     if not args.no_small_batch and w.layers == 1:
         # serving-size batches: forward-inference latency of the same layer
         import dataclasses
@@ -396,7 +529,9 @@ def main():
             rs = Runner(dataclasses.replace(w, B=Bs), torch, R, synth)
             f_ms, _ = rs.timed(rs.fwd, max(5, args.steps // 2), args.warmup)
             med = float(np.median(f_ms))
-            sb[str(Bs)] = {"fwd_ms": round(med, 4), "us_per_step": round(1000.0 * med / w.T, 3)}
+            sb[str(Bs)] = {"fwd_ms": round(med, 4), "us_per_step": round(1000.0 * med / w.T, 3),
+                           "plan": R.rnn_plan_info(rs.h, w.T, Bs, False)["fwd"]}
+            del rs
         out["small_batch_fwd"] = sb
     if args.blas_reference and w.wtype == "bf16":
         out["vendor_gemm_reference"] = blas_reference(torch, w)

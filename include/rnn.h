@@ -219,10 +219,13 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
  * same T, B and workspace (else BAD_CALL_ORDER).  x, h0 and y are the
  * forward's.  dW (rnn_weights_size(h, 1, .) bytes, layout of
  * rnn_weight_offset with grad = 1) is OVERWRITTEN with dLoss/dW, dLoss/db.
- * May be called again without repeating backward_data. */
+ * The gate gradients backward_data left in the workspace are only read; its
+ * operand scratch (transposed inputs and states, split-K partials) is
+ * overwritten, so the workspace is an in/out argument.  May be called again
+ * without repeating backward_data. */
 rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, const float* x,
-                                  const float* h0, const float* y, const void* ws,
-                                  size_t ws_bytes, float* dW);
+                                  const float* h0, const float* y, void* ws, size_t ws_bytes,
+                                  float* dW);
 
 /* Diagnostic: the latency floor of the persistent forward sweep.  Runs the
  * launch that rnn_forward_inference (training = 0) or rnn_forward_training
@@ -256,6 +259,17 @@ rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, int 
  * no handle.  Errors: INVALID_ARG for an unknown kind, blocks <= 0,
  * iters <= 0 or a null `out`; DEVICE for a launch error. */
 rnn_status_t rnn_mfma_peak_probe(void* stream, int kind, int blocks, int iters, float* out);
+
+/* Diagnostic: the launch plan of the recurrent sweeps for (T, B, training)
+ * as the compute calls would make it now (environment and device included).
+ * Writes 16 ints to `out` (host memory): out[0..7] the forward sweep and
+ * out[8..15] the backward sweep (zeros when training = 0), each as: batch
+ * chunks, rows per chunk, hidden units per workgroup, workgroups per group,
+ * groups, grid (workgroups launched), placement (0: linear, 1: XCD-local
+ * recurrence groups), persistent (1) or stepped (0).  Host only; touches no
+ * device memory.  Errors: INVALID_ARG for a NULL handle or out, T < 0 or
+ * B < 0; UNSUPPORTED when no kernel configuration fits. */
+rnn_status_t rnn_plan_info(rnn_handle_t h, int T, int B, int training, int* out);
 
 /* Synchronise `stream` and report whether a kernel that used `ws` hit an
  * expired bounded wait since the workspace was last handed to a compute

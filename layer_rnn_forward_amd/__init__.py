@@ -34,6 +34,8 @@ from ._binding import (  # noqa: F401
     rnn_exchange_floor,
     rnn_mfma_peak_probe,
     MFMA_PROBES,
+    rnn_plan_info,
+    PLAN_FIELDS,
     rnn_backward_weights,
     rnn_device_status,
     rnn_set_profiling,

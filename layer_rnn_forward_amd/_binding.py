@@ -58,6 +58,7 @@ def load_library():
         "rnn_device_status": [vp, vp, vp, sz],
         "rnn_exchange_floor": [vp, vp, i, i, i, vp, sz],
         "rnn_mfma_peak_probe": [vp, i, i, i, vp],
+        "rnn_plan_info": [vp, i, i, i, ctypes.POINTER(ctypes.c_int)],
         "rnn_set_profiling": [vp, i],
         "rnn_profile_read": [vp, i, ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_double)],
     }
@@ -225,6 +226,20 @@ def rnn_exchange_floor(h, T, B, ws, training=False):
     _check(load_library().rnn_exchange_floor(h.ptr, _stream(), T, B, 1 if training else 0,
                                              _ptr(ws, "ws", None), _nbytes(ws)),
            "rnn_exchange_floor")
+
+
+PLAN_FIELDS = ("nchunk", "rows", "units", "nwg", "groups", "grid", "place", "persistent")
+
+
+def rnn_plan_info(h, T: int, B: int, training: bool):
+    """The recurrent sweeps' launch plan: ``{"fwd": {...}, "bwd": {...}}``
+    with the fields of PLAN_FIELDS (``bwd`` only for training)."""
+    out = (ctypes.c_int * 16)()
+    _check(load_library().rnn_plan_info(h.ptr, T, B, 1 if training else 0, out), "rnn_plan_info")
+    r = {"fwd": dict(zip(PLAN_FIELDS, out[0:8]))}
+    if training:
+        r["bwd"] = dict(zip(PLAN_FIELDS, out[8:16]))
+    return r
 
 
 MFMA_PROBES = {"f32_16x16x4": 0, "bf16_16x16x32": 1, "bf16_32x32x16": 2}

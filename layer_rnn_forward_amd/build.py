@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librnn_mi355x.so")
-SOURCES = ["dropout.hip", "gemm.hip", "layout.hip", "recurrent.hip", "recurrent_gru2.hip", "rnn_api.cpp"]
+SOURCES = ["dropout.hip", "gemm.hip", "layout.hip", "recurrent.hip", "recurrent_gru2.hip", "rnn_api.cpp",
+           *[f"recurrent_{m}_{k}.hip" for m in ("tanh", "lstm", "gru") for k in ("fwd", "bwd")]]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -29,6 +30,13 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
     "-I", CSRC,
 ]
+
+
+# per-source extra flags: the MFMA throughput probes in layout.hip keep their
+# accumulators in VGPRs (with AGPR accumulators the compiler rotated some of
+# the independent chains through accumulator moves, which halved the
+# 16x16x32 bf16 probe's rate)
+EXTRA = {"layout.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd):
@@ -48,7 +56,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
         objs.append(obj)
         extra = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmds.append([HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         outs = list(ex.map(_run, cmds))
     if verbose:

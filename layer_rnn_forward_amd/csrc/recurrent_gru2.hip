@@ -47,7 +47,8 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
-  const int wg = blockIdx.x;
+  const int wg = logical_wg(p.place, p.nwg, p.ngroups);
+  if (wg < 0) return;   // an idle slot of the XCD-local placement
   const int slice = wg % p.nwg;
   const int grp = wg / p.nwg;
   const int c = grp % p.nchunk;
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
       sh_h[qb * NCOL + qj] = hv;
     }
     if (qw) ring_store<BF16>(ring, my_off, hv);
-    publish(p.flags, 1u);
+    publish(p.flags, wg, 1u);
   }
   __syncthreads();
 
@@ -130,8 +131,11 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
     f32x4 acc[MT][NT];
     const bool ok = wave_wait(p.flags, p.err, p.spin_limit, hflag0, hn, 0, 0, target);
     if (ok) {
+      // the read offset passes through an asm statement after the wait
+      int g0s = g0;
+      asm volatile("" : "+v"(g0s));
       mfma_sweep<BF16, NT, MT, KPW, (NW >= 8 ? 4 : 8)>(acc, wf, fr, fq, nmine, rmax, [&](int gl, int row) -> uint4 {
-        return *reinterpret_cast<const uint4*>(e + (size_t)(g0 + gl) * gran + row * 16);
+        return *reinterpret_cast<const uint4*>(e + (size_t)(g0s + gl) * gran + row * 16);
       });
     } else {
 #pragma unroll
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
       rh = rg * hprev;
     }
     if (qw) ring_store<BF16>(ring2 + (size_t)s * p.ring_step, my_off, rh);
-    publish(p.flags, (unsigned)(2 * s + 2));
+    publish(p.flags, wg, (unsigned)(2 * s + 2));
     // (2) r*h -> n, h
     if (!exchange(ring2 + (size_t)s * p.ring_step, (unsigned)(2 * s + 2))) return;
     float hnew = 0.f, ng = 0.f;
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
       sh_h[qb * NCOL + qj] = hnew;
     }
     if (qw) ring_store<BF16>(ring + (size_t)(s + 1) * p.ring_step, my_off, hnew);
-    publish(p.flags, (unsigned)(2 * s + 3));
+    publish(p.flags, wg, (unsigned)(2 * s + 3));
     if (qv) {
       p.y[0][(size_t)t * ystride_t + (size_t)qbg * D * H + (size_t)d * H + qu] = tv ? hnew : 0.f;
       if (p.training) {
@@ -224,7 +228,8 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
-  const int wg = blockIdx.x;
+  const int wg = logical_wg(p.place, p.nwg, p.ngroups);
+  if (wg < 0) return;   // an idle slot of the XCD-local placement
   const int slice = wg % p.nwg;
   const int grp = wg / p.nwg;
   const int c = grp % p.nchunk;
@@ -302,8 +307,11 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
     f32x4 acc[MT][NT];
     const bool ok = wave_wait(p.flags, p.err, p.spin_limit, grp * p.nwg + fa0, fn, 0, 0, target);
     if (ok) {
+      // the read offset passes through an asm statement after the wait
+      int gb = gbase;
+      asm volatile("" : "+v"(gb));
       mfma_sweep<BF16, NT, MT, KW, (NW >= 8 ? 4 : 8)>(acc, wf, fr, fq, nmine, rmax, [&](int gl, int row) -> uint4 {
-        return *reinterpret_cast<const uint4*>(e + (size_t)(gbase + gl) * gran + row * 16);
+        return *reinterpret_cast<const uint4*>(e + (size_t)(gb + gl) * gran + row * 16);
       });
     } else {
 #pragma unroll
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
     else { dn = dh * (1.f - zg); dz = dh * (hp - ng); direct = dh * zg; }
     float dan = tv ? dn * (1.f - ng * ng) : 0.f;
     if (qw) ring_store<BF16>(ringA + (size_t)s * p.ring_step, offA, qv ? dan : 0.f);
-    publish(p.flags, (unsigned)(2 * s + 1));
+    publish(p.flags, wg, (unsigned)(2 * s + 1));
     // (A) d(r*h) = da_n W_hn for the own units
     const float drh = exchange(wfA, ringA + (size_t)s * p.ring_step, gA0, nA, granA, rmaxA, pA0, pnA,
                                (unsigned)(2 * s + 1));
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
       ring_store<BF16>(en, offB, qv ? dar : 0.f);
       ring_store<BF16>(en, offB + (size_t)UJ * granB, qv ? daz : 0.f);
     }
-    publish(p.flags, (unsigned)(2 * s + 2));
+    publish(p.flags, wg, (unsigned)(2 * s + 2));
     if (qv) {
       // gate gradients (dG_i = dG_h) for the dX and weight-gradient products
       using X = typename std::conditional<BF16, uint16_t, float>::type;

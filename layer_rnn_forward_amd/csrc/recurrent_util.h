@@ -49,12 +49,27 @@ __device__ __forceinline__ void ring_store(char* base, size_t off, float v) {
     __hip_atomic_store(reinterpret_cast<float*>(base + off), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Compiler-only ordering point: no memory operation is moved across it at
+// the IR level (the s_waitcnt builtin does not order memory operations
+// there); it emits no instruction.  The hardware order of the exchange is
+// given by the waits around it.
+__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
 // Bounded wait of one wave for the flags of two ranges of producers,
 // [a0, a0 + na) and [b0, b0 + nb) (flag indices), to reach `target`.
 // Returns false (uniformly over the wave) if the wait expired -- the error
-// word is then set -- or another workgroup reported an error.
+// word is then set -- or another workgroup reported an error.  A spin limit
+// of 0 expires every wait at once (a host-forced timeout for tests).  The
+// callers order their reads of the producers' ring lines after a successful
+// wait by computing the read addresses through an empty asm statement that
+// follows it (a register dependency the compiler cannot hoist above the
+// loop); a compiler fence at this exit measured 0.06 us per step slower.
 __device__ bool wave_wait(const unsigned* flags, unsigned* err, unsigned spin_limit, int a0, int na,
                           int b0, int nb, unsigned target) {
+  if (spin_limit == 0) {
+    flag_store(err, 1u);
+    return false;
+  }
   const int lane = threadIdx.x & 63;
   const int total = na + nb;
   const int nper = (total + 63) / 64;   // flags per lane, uniform
@@ -84,6 +99,22 @@ __device__ bool wave_wait(const unsigned* flags, unsigned* err, unsigned spin_li
   }
 }
 
+// Logical index (group * nwg + slice) of this workgroup in a sweep's grid,
+// or -1 for a workgroup with no work.  place 0: blockIdx.x.  place 1
+// (XCD-local groups): the dispatcher deals workgroups to the XCDs round-robin
+// (blockIdx.x % kXcds); group g gets slots (g / kXcds) * nwg .. + nwg - 1 of
+// XCD g % kXcds, so all producers and consumers of one group share that
+// XCD's L2.  Correctness never depends on where a workgroup actually runs:
+// the exchange is coherent at agent scope.
+__device__ __forceinline__ int logical_wg(int place, int nwg, int ngroups) {
+  const int b = blockIdx.x;
+  if (place == 0) return b;
+  const int x = b % kXcds, k = b / kXcds;
+  const int row = k / nwg, j = k - row * nwg;
+  const int g = row * kXcds + x;
+  return g < ngroups ? g * nwg + j : -1;
+}
+
 // Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it
 // does not wait for the wave's outstanding global loads and stores.
 __device__ __forceinline__ void lds_barrier() {
@@ -97,17 +128,27 @@ __device__ __forceinline__ void lds_barrier() {
 // of the step was made by wave 0, so wave 0 alone waits for them and
 // publishes, with no workgroup barrier before the flag (the other waves meet
 // wave 0 again at the step's closing LDS barrier).
-__device__ __forceinline__ void publish(unsigned* flags, unsigned v, bool wave0_only = false) {
+// `id`: the workgroup's flag index (its logical index in the sweep's grid).
+// Ordering assumed of the hardware (gfx950): an agent-scope store is
+// written through to the device-coherent level, and s_waitcnt(0) returns only
+// once every earlier store of the wave has been acknowledged there; so a
+// consumer that sees the flag and then issues plain loads of lines it never
+// touched before reads the stored values.  Compiler fences keep the ring
+// stores before the wait and the flag store after it.
+__device__ __forceinline__ void publish(unsigned* flags, int id, unsigned v, bool wave0_only = false) {
+  compiler_fence();
   if (wave0_only) {
     if (threadIdx.x < 64) {
       __builtin_amdgcn_s_waitcnt(0);
-      if (threadIdx.x == 0) flag_store(flags + (size_t)blockIdx.x * kFlagStride, v);
+      compiler_fence();
+      if (threadIdx.x == 0) flag_store(flags + (size_t)id * kFlagStride, v);
     }
     return;
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) flag_store(flags + (size_t)blockIdx.x * kFlagStride, v);
+  compiler_fence();
+  if (threadIdx.x == 0) flag_store(flags + (size_t)id * kFlagStride, v);
 }
 
 // MFMA over the granules this wave holds.  K chunk kk takes granules

@@ -46,6 +46,7 @@ struct SweepPlan {
   RecConfig cfg{};
   int nchunk = 0, Bc = 0;   // batch chunks of Bc rows
   int U = 0, nwg = 0, groups = 0, grid = 0;
+  int place = 0;            // 1: XCD-local groups (sweep_grid)
   bool persistent = false;
   size_t lds = 0;   // dynamic LDS for staging ring entries (0: fragments read from global)
 };
@@ -134,31 +135,47 @@ void layout_weights(rnn_desc* h) {
 const RecConfig kFwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 1, 16, 4}, {1, 2, 16, 4}, {2, 1, 8, 4},
                               {2, 2, 8, 4},  {2, 1, 16, 4}, {2, 2, 16, 4}, {4, 1, 4, 8},  {4, 2, 4, 8},
                               {4, 1, 8, 8},  {4, 2, 8, 8},
-                              {1, 2, 32, 4}, {1, 2, 16, 8}, {2, 2, 16, 8}, {4, 2, 16, 8}};
+                              {1, 2, 32, 4}, {1, 2, 16, 8}, {2, 2, 16, 8}, {4, 2, 16, 8},
+                              {8, 1, 8, 4}};
 // (measured at the DS2 shapes: eight waves of 16 K chunks beat four waves
 // of 32 by 11-13 % in the backward sweep -- half the granules per wave; 32
 // chunks on eight waves spill, so fp32 keeps four waves of 64)
 const RecConfig kBwdCfgs[] = {{1, 1, 8, 4},  {1, 2, 8, 4},  {1, 1, 16, 4}, {1, 2, 16, 4},
                               {1, 1, 16, 8}, {1, 2, 16, 8}, {1, 1, 32, 4}, {1, 2, 32, 4},
-                              {1, 1, 64, 4}, {1, 2, 64, 4}, {1, 2, 32, 8}, {1, 1, 32, 8}};
+                              {1, 1, 64, 4}, {1, 2, 64, 4}, {1, 2, 32, 8}, {1, 1, 32, 8},
+                              {2, 1, 16, 4}, {2, 1, 32, 4}};
 
 // Units per workgroup are a multiple of the per-lane MFMA k run (8 bf16 / 4
 // fp32 values, 16 bytes) so that every A fragment of the exchange comes from
 // one producer's slice.
 int unit_quantum(const rnn_desc* h) { return h->wtype == RNN_W_BF16 ? 8 : 4; }
 
+// CUs of one XCD of an MI355X (256 CUs in 8 XCDs).
+constexpr int kCusPerXcd = 32;
+
+// Units per workgroup of an XCD-local group: the fewest that keep one
+// group's workgroups within the CUs of one XCD.
+int xcd_units(const rnn_desc* h) {
+  const int Q = unit_quantum(h);
+  return ceil_div(ceil_div(h->H, kCusPerXcd), Q) * Q;
+}
+
 // Pick a forward configuration: U so that all groups together use about
 // `target_wgs` workgroups, the gate columns of U units fit the MFMA tiles, the
 // K chunks fit the registers, and each epilogue thread owns one (row, unit).
-bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepPlan* sp) {
+// `Ureq` > 0: exactly that many units (XCD-local groups), with the wide
+// (eight-column-tile) configurations allowed; 0: the planner's choice.
+bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepPlan* sp, int Ureq = 0) {
   const int Q = unit_quantum(h);
   const int GB = (h->mode == RNN_GRU && inproj) ? 4 : h->G;
   const int target_wgs = std::max(1, env_int("RNN_FWD_TARGET_WGS", 256));
   int U = ceil_div(ceil_div(h->H * std::max(1, groups), target_wgs), Q) * Q;
   const int Uenv = env_int("RNN_FWD_UNITS", 0);
   if (Uenv > 0) U = ceil_div(Uenv, Q) * Q;
+  if (Ureq > 0) U = Ureq;
   U = std::max(Q, std::min(U, ceil_div(h->H, Q) * Q));
-  for (int tryU = U; tryU >= Q; tryU -= Q) {
+  const int Ulow = Ureq > 0 ? U : Q;
+  for (int tryU = U; tryU >= Ulow; tryU -= Q) {
     const int nwg = ceil_div(h->H, tryU);
     const int ngr = (inproj ? 2 : 1) * nwg * (tryU / Q);   // K granules
     // (measured: four waves with two load batches beat eight waves with one
@@ -166,7 +183,7 @@ bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepP
     const int force = env_int("RNN_FWD_CFG", -1);   // tuning: only this list entry
     for (const RecConfig& c : kFwdCfgs) {
       if (force >= 0 && &c != &kFwdCfgs[force % (int)(sizeof(kFwdCfgs) / sizeof(kFwdCfgs[0]))]) continue;
-      if (c.mt != mt) continue;
+      if (c.mt != mt || (c.nt > 4 && Ureq == 0)) continue;
       if (is_gru2(h) && !rnn_gru2_fwd_config_supported(h->wtype == RNN_W_BF16, c)) continue;
       if (GB * tryU > 16 * c.nt || Bc * tryU > 64 * c.nwaves) continue;
       if (ceil_div(ceil_div(ngr, c.nwaves), 4) > c.kpw) continue;
@@ -181,11 +198,13 @@ bool plan_fwd(const rnn_desc* h, int mt, int Bc, int groups, bool inproj, SweepP
   return false;
 }
 
-bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, SweepPlan* sp) {
+bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, SweepPlan* sp, int Ureq = 0) {
   const int Q = unit_quantum(h);
   int U = ceil_div(std::max(1, env_int("RNN_BWD_UNITS", 16)), Q) * Q;
+  if (Ureq > 0) U = Ureq;
   U = std::max(Q, std::min(U, ceil_div(h->H, Q) * Q));
-  for (int tryU = U; tryU >= Q; tryU -= Q) {
+  const int Ulow = Ureq > 0 ? U : Q;
+  for (int tryU = U; tryU >= Ulow; tryU -= Q) {
     const int nwg = ceil_div(h->H, tryU);
     const int ngr = h->G * nwg * (tryU / Q);   // K granules
     // the flavours with two exchanges hold two weight sets: the n gate
@@ -194,7 +213,7 @@ bool plan_bwd(const rnn_desc* h, int mt, int Bc, int groups, SweepPlan* sp) {
     const int force = env_int("RNN_BWD_CFG", -1);   // tuning: only this list entry
     for (const RecConfig& c : kBwdCfgs) {
       if (force >= 0 && &c != &kBwdCfgs[force % (int)(sizeof(kBwdCfgs) / sizeof(kBwdCfgs[0]))]) continue;
-      if (c.mt != mt || (c.kpw > 32 && h->wtype == RNN_W_BF16)) continue;
+      if (c.mt != mt || (c.kpw > 32 && h->wtype == RNN_W_BF16) || (c.nt > 1 && Ureq == 0)) continue;
       if (is_gru2(h) && !rnn_gru2_bwd_config_supported(h->wtype == RNN_W_BF16, c)) continue;
       if (tryU > 16 * c.nt || Bc * tryU > 64 * c.nwaves) continue;
       if (ceil_div(ceil_div(is_gru2(h) ? ngr2 : ngr, c.nwaves), 4) > c.kpw) continue;
@@ -282,6 +301,8 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
   };
   const int sched = h->sched;
   const bool allow_stage = env_int("RNN_NO_STAGE", 0) == 0;
+  // XCD-local recurrence groups (persistent sweeps only)
+  const bool place_req = env_int("RNN_PLACE", 0) == 1 && sched != RNN_SCHED_STEPPED;
   // co-residency: returns whether every workgroup of the sweep fits on the
   // GPU at once (with LDS staging if it fits, else without)
   auto fit = [&](SweepPlan& sp, bool fwd, size_t stage_bytes) {
@@ -318,18 +339,21 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
   // ---- forward sweep
   const bool wf0 = h->D == 1 && h->L > 1 && h->L <= kMaxLayersPerLaunch && !is_gru2(h) &&
                    env_int("RNN_NO_WAVEFRONT", 0) == 0;
-  auto plan_f = [&](int max_bc) {
+  // `Ux` > 0: XCD-local groups of Ux units per workgroup
+  auto plan_f = [&](int max_bc, int Ux) {
     chunk(max_bc, p.fwd);
     p.wavefront = wf0;
     const int fl = p.wavefront ? h->L : 1;
     const int fmt = ceil_div(p.fwd.Bc, 16);
-    if (!plan_fwd(h, fmt, p.fwd.Bc, fl * h->D * p.fwd.nchunk, p.wavefront, &p.fwd)) return false;
+    if (!plan_fwd(h, fmt, p.fwd.Bc, fl * h->D * p.fwd.nchunk, p.wavefront, &p.fwd, Ux)) return false;
     // wavefront: every workgroup polls its own and the layer below's flags
     if (p.wavefront && 2 * p.fwd.nwg > kMaxWaitFlags) p.wavefront = false;
     if (!p.wavefront && p.fwd.groups != h->D * p.fwd.nchunk &&
-        !plan_fwd(h, fmt, p.fwd.Bc, h->D * p.fwd.nchunk, false, &p.fwd))
+        !plan_fwd(h, fmt, p.fwd.Bc, h->D * p.fwd.nchunk, false, &p.fwd, Ux))
       return false;
     if (p.fwd.nwg > kMaxWaitFlags) return false;
+    p.fwd.place = Ux > 0 ? 1 : 0;
+    p.fwd.grid = sweep_grid(p.fwd.place, p.fwd.nwg, p.fwd.groups);
     // exchange rings: one entry per step, entries padded to 1 KB
     const int s_total = T + (p.wavefront ? h->L : 1) - 1;
     p.fgran = padded_rows(p.fwd.Bc, p.fwd.U / Q) * 16;
@@ -349,9 +373,16 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
     const bool gru = h->mode == RNN_GRU || is_gru2(h);
     const int fwd_pref = (bf && h->G >= 3 && (training || gru)) ? 4 : 16;
     bool ok = false, fits = false;
+    if (place_req) {   // XCD-local groups: enough batch chunks to give each XCD one group
+      const int per = std::max(1, kXcds / ((wf0 ? h->L : 1) * h->D));
+      ok = plan_f(env_int("RNN_PLACE_BC", ceil_div(Bq, per)), xcd_units(h));
+      fits = ok && fit(p.fwd, true, 0);
+      ok = fits;
+    }
     for (int mb : ladder(env_int("RNN_FWD_MAX_BC", fwd_pref), {16, 32})) {
+      if (fits) break;
       if (ok && Bq <= p.fwd.Bc) break;   // a larger cap changes nothing
-      ok = plan_f(mb);
+      ok = plan_f(mb, 0);
       // the forward reads its fragments straight from the ring
       fits = ok && fit(p.fwd, true, 0);
       if (fits) break;
@@ -368,11 +399,13 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
 
   // ---- backward sweep: the same ladder of batch chunk sizes
   if (training) {
-    auto plan_b = [&](int max_bc) {
+    auto plan_b = [&](int max_bc, int Ux) {
       chunk(max_bc, p.bwd);
-      if (!plan_bwd(h, ceil_div(p.bwd.Bc, 16), p.bwd.Bc, h->D * p.bwd.nchunk, &p.bwd) ||
+      if (!plan_bwd(h, ceil_div(p.bwd.Bc, 16), p.bwd.Bc, h->D * p.bwd.nchunk, &p.bwd, Ux) ||
           p.bwd.nwg > kMaxWaitFlags)
         return false;
+      p.bwd.place = Ux > 0 ? 1 : 0;
+      p.bwd.grid = sweep_grid(p.bwd.place, p.bwd.nwg, p.bwd.groups);
       // the flavours with two exchanges: da_n (one gate per slice) in the
       // first ring, [da_r, da_z] (two gates) in the second
       const int gpr = is_gru2(h) ? 1 : h->G;
@@ -389,9 +422,16 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
       return true;
     };
     bool ok = false, fits = false;
+    if (place_req) {
+      const int per = std::max(1, kXcds / h->D);
+      ok = plan_b(env_int("RNN_PLACE_BC", ceil_div(Bq, per)), xcd_units(h));
+      fits = ok && fit(p.bwd, false, p.bring_step);
+      ok = fits;
+    }
     for (int mb : ladder(env_int("RNN_BWD_MAX_BC", 4), {5, 7, 10, 16, 32})) {
+      if (fits) break;
       if (ok && Bq <= p.bwd.Bc) break;   // a larger cap changes nothing
-      ok = plan_b(mb);
+      ok = plan_b(mb, 0);
       fits = ok && fit(p.bwd, false, p.bring_step);
       if (fits) break;
     }
@@ -599,9 +639,11 @@ void gemm_consts(const rnn_desc* h, GemmParams& g, const void* ws, size_t off_he
 }
 
 
+// Polls a bounded wait makes before it expires (RNN_SPIN_LIMIT; 0 expires
+// every wait at once, a host-forced timeout for tests).
 unsigned spin_limit() {
   const int v = env_int("RNN_SPIN_LIMIT", 1 << 20);
-  return (unsigned)std::max(1, v);
+  return (unsigned)std::max(0, v);
 }
 
 const void* layer_w(const rnn_desc* h, const void* W, int which, int l) {
@@ -638,7 +680,9 @@ rnn_status_t gemm_input(rnn_desc* h, hipStream_t s, const Plan& p, int l, const 
   }
   g.B[0] = layer_w(h, W, RNN_W_IH, l);
   g.ldb = I_l;
-  g.b_vec = (I_l % EPV == 0);
+  // 16-byte row loads of W_ih need whole vectors per row and an aligned base
+  // (W may sit at any element offset of a caller's parameter arena)
+  g.b_vec = (I_l % EPV == 0) && ((uintptr_t)g.B[0] % 16 == 0);
   g.n_ones = -1;
   g.C[0] = gx;
   g.ldc = g.N;
@@ -712,6 +756,8 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   f.H = h->H;
   f.D = h->D;
   f.nchunk = p.fwd.nchunk;
+  f.place = p.fwd.place;
+  f.ngroups = p.fwd.groups;
   f.Bc = p.fwd.Bc;
   f.U = p.fwd.U;
   f.nwg = p.fwd.nwg;
@@ -741,7 +787,7 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
   auto run_sweep = [&](int nlayers) -> rnn_status_t {
     f.nlayers = nlayers;
     f.s_total = T + nlayers - 1;
-    const int grid = p.fwd.nwg * nlayers * h->D * p.fwd.nchunk;
+    const int grid = p.fwd.grid;   // (groups = nlayers * D * nchunk)
     if (f.persistent && !flags_clear) RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
     flags_clear = false;
     if (f.persistent) {
@@ -845,6 +891,8 @@ rnn_status_t exchange_probe_impl(rnn_desc* h, void* stream, int T, int B, int tr
   f.H = h->H;
   f.D = h->D;
   f.nchunk = p.fwd.nchunk;
+  f.place = p.fwd.place;
+  f.ngroups = p.fwd.groups;
   f.Bc = p.fwd.Bc;
   f.U = p.fwd.U;
   f.nwg = p.fwd.nwg;
@@ -864,7 +912,7 @@ rnn_status_t exchange_probe_impl(rnn_desc* h, void* stream, int T, int B, int tr
   f.flags = at<unsigned>(ws, p.off_flags);
   f.err = at<unsigned>(ws, p.off_err);
   f.spin_limit = spin_limit();
-  const int grid = p.fwd.nwg * f.nlayers * h->D * p.fwd.nchunk;
+  const int grid = p.fwd.grid;
   RNN_TRY(fill(h, s, {{at<void>(ws, p.off_flags), p.flags_bytes}}));
   ProfScope ps(h, s, K_PROBE);
   // (the flavours with two exchanges per step probe one of them)
@@ -968,6 +1016,20 @@ rnn_status_t rnn_workspace_size(rnn_handle_t h, int T, int B, int training, size
   return RNN_STATUS_SUCCESS;
 }
 
+rnn_status_t rnn_plan_info(rnn_handle_t h, int T, int B, int training, int* out) {
+  if (!h || !out || T < 0 || B < 0) return RNN_STATUS_INVALID_ARG;
+  Plan p = make_plan(h, T, B, training ? 1 : 0, training ? h->drop_p : 0.0);
+  if (p.status == RNN_STATUS_UNSUPPORTED) return p.status;
+  for (int i = 0; i < 16; ++i) out[i] = 0;
+  auto put = [&](int base, const SweepPlan& sp) {
+    const int v[8] = {sp.nchunk, sp.Bc, sp.U, sp.nwg, sp.groups, sp.grid, sp.place, sp.persistent ? 1 : 0};
+    for (int i = 0; i < 8; ++i) out[base + i] = v[i];
+  };
+  put(0, p.fwd);
+  if (training) put(8, p.bwd);
+  return RNN_STATUS_SUCCESS;
+}
+
 rnn_status_t rnn_forward_inference(rnn_handle_t h, void* stream, int T, int B, const float* x,
                                    const float* h0, const float* c0, const void* W, float* y,
                                    float* hy, float* cy, void* ws, size_t ws_bytes) {
@@ -1025,6 +1087,8 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
   b.H = h->H;
   b.D = h->D;
   b.nchunk = p.bwd.nchunk;
+  b.place = p.bwd.place;
+  b.ngroups = p.bwd.groups;
   b.Bc = p.bwd.Bc;
   b.U = p.bwd.U;
   b.nwg = p.bwd.nwg;
@@ -1135,8 +1199,8 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
 }
 
 rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, const float* x,
-                                  const float* h0, const float* y, const void* ws,
-                                  size_t ws_bytes, float* dW) {
+                                  const float* h0, const float* y, void* ws, size_t ws_bytes,
+                                  float* dW) {
   RNN_TRY(check_common(h, T, B, ws, ws_bytes));
   if (!ws || !dW) return RNN_STATUS_INVALID_ARG;
   if (T > 0 && B > 0 && (!x || !y)) return RNN_STATUS_INVALID_ARG;
@@ -1147,7 +1211,7 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
   Plan p = make_plan(h, T, B, 1, h->seq_drop_p);
   if (p.status != RNN_STATUS_SUCCESS) return p.status;
   if (ws_bytes < p.total) return RNN_STATUS_WORKSPACE_TOO_SMALL;
-  void* wsm = const_cast<void*>(ws);
+  void* wsm = ws;
   if (T == 0 || B == 0) return fill(h, s, {{dW, h->dwbytes}});
   const int bf = h->wtype == RNN_W_BF16;
   const size_t lstride = (size_t)h->D * B * h->H;

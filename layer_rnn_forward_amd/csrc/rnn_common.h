@@ -10,6 +10,13 @@ constexpr int kMaxLayersPerLaunch = 8;   // layers resident in one wavefront lau
 constexpr int kFlagStride = 32;          // u32 per flag slot (128 bytes)
 constexpr int kMaxWaitFlags = 512;       // flags one workgroup may poll per step
 constexpr int kWaitPerLane = kMaxWaitFlags / 64;
+constexpr int kXcds = 8;                 // XCDs of one MI355X (SPX mode), each with its own L2
+
+// Grid of a sweep with `groups` groups of `nwg` workgroups: linear, or
+// XCD-local (place 1: logical_wg in recurrent_util.h; idle slots exit at once).
+__host__ __device__ constexpr int sweep_grid(int place, int nwg, int groups) {
+  return place ? kXcds * ((groups + kXcds - 1) / kXcds) * nwg : nwg * groups;
+}
 
 enum Mode { MODE_TANH = 0, MODE_LSTM = 1, MODE_GRU = 2 };
 
@@ -98,6 +105,7 @@ struct FwdParams {
   int s_total;            // T + nlayers - 1
   int persistent, training, wavefront;
   int probe;              // 1: exchange only (waits, ring stores, flags); no weights, math or outputs
+  int place, ngroups;     // workgroup placement (sweep_grid) and the launch's group count
   const int* lengths;     // [B] valid steps per row (clamped to [0, T]), or null: all T
   void* xch2;             // GRU with (r*h) W_hn: rings of r*h, laid out as xch
   int paper;              // GRU with (r*h) W_hn: 1 for h = (1-z) h_prev + z n
@@ -139,6 +147,7 @@ struct BwdParams {
   int group_poll;         // 1: one wave polls every producer; 0: each wave its own
   int s_begin, s_end;     // processing steps; s == T is the final dh0 phase
   int persistent;
+  int place, ngroups;     // workgroup placement (sweep_grid) and the launch's group count
   const int* lengths;     // [B] valid steps per row (clamped to [0, T]), or null: all T
   // GRU with (r*h) W_hn: xch carries da_n (one gate per slice, gran/slice
   // above) and xch2 carries [da_r, da_z] (two gates per slice)
@@ -234,3 +243,17 @@ bool rnn_gru2_bwd_config_supported(int bf16, const RecConfig& c);
 int rnn_bwd_max_resident(int mode, int bf16, const RecConfig& c, size_t lds);
 bool rnn_fwd_config_supported(int mode, int bf16, const RecConfig& c);
 bool rnn_bwd_config_supported(int mode, int bf16, const RecConfig& c);
+
+// Per-mode entry points of the recurrent sweeps (recurrent_<mode>_<fwd|bwd>.hip).
+#define RNN_SWEEP_DECLS(NAME)                                                                         \
+  hipError_t rnn_fwd_launch_##NAME(const rnnk::FwdParams& p, int bf16, const RecConfig& c, int grid,   \
+                                   size_t lds, hipStream_t s);                                        \
+  int rnn_fwd_resident_##NAME(int bf16, const RecConfig& c, size_t lds);                              \
+  bool rnn_fwd_supported_##NAME(int bf16, const RecConfig& c);                                        \
+  hipError_t rnn_bwd_launch_##NAME(const rnnk::BwdParams& p, int bf16, const RecConfig& c, int grid,   \
+                                   size_t lds, hipStream_t s);                                        \
+  int rnn_bwd_resident_##NAME(int bf16, const RecConfig& c, size_t lds);                              \
+  bool rnn_bwd_supported_##NAME(int bf16, const RecConfig& c);
+RNN_SWEEP_DECLS(tanh)
+RNN_SWEEP_DECLS(lstm)
+RNN_SWEEP_DECLS(gru)

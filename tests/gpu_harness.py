@@ -110,17 +110,36 @@ def run_oracle(mode, L, D, case, backward=True, pass_state=True, pass_grads=True
     return out
 
 
-def compare(g, o, mode, L, D):
-    """Per-output normwise errors, {name: err}."""
-    errs = {}
+def elementwise(a, b, floor=1e-3):
+    """Largest elementwise relative error max |a - b| / max(|b|, floor): a
+    diagnostic next to the normwise gate (reported, never gated on)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    if a.size == 0:
+        return 0.0
+    return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), floor)))
+
+
+def compare(g, o, mode, L, D, report=True):
+    """Per-output normwise errors, {name: err} (the gate).  With ``report``
+    the elementwise diagnostic of every output is printed as well."""
+    errs, diag = {}, {}
+    pairs = []
     for k in ("y", "hy", "cy", "dx", "dh0", "dc0"):
         if k in g and k in o:
-            errs[k] = normwise(g[k], o[k])
+            pairs.append((k, g[k], o[k]))
     if "dW" in g and "dW" in o:
         for l in range(L):
             for d in range(D):
                 for n in ("w_ih", "w_hh", "b_ih", "b_hh"):
-                    errs[f"d{n}[{l},{d}]"] = normwise(g["dW"][l][d][n], o["dW"][l][d][n])
+                    pairs.append((f"d{n}[{l},{d}]", g["dW"][l][d][n], o["dW"][l][d][n]))
+    for k, a, b in pairs:
+        errs[k] = normwise(a, b)
+        diag[k] = elementwise(a, b)
+    if report and diag:
+        worst = max(diag, key=diag.get)
+        print(f"elementwise max |g-o|/max(|o|,1e-3): worst {worst} {diag[worst]:.2e}; "
+              f"normwise worst {max(errs.values()):.2e}", flush=True)
     return errs
 
 

@@ -167,3 +167,25 @@ def test_workspace_covers_split_k_partials(R, monkeypatch):
     monkeypatch.delenv("RNN_DW_SPLIT")
     assert R.rnn_workspace_size(h, T, B, 1) <= w8
     R.rnn_destroy(h)
+
+
+def test_plan_info_is_consistent(R, monkeypatch):
+    """The plan diagnostic reports a plan whose batch chunks cover the batch,
+    whose workgroups cover the hidden width and whose grid holds every group
+    (host only; without a GPU nothing is co-resident, so the sweeps are
+    stepped and the placement linear)."""
+    for mode, L, D, wtype in (("lstm", 1, 1, "bf16"), ("gru", 2, 2, "f32"), ("rnn_tanh", 5, 1, "bf16")):
+        h = R.rnn_create(mode, L, D, 800, 800, wtype)
+        for place in ("0", "1"):
+            monkeypatch.setenv("RNN_PLACE", place)
+            info = R.rnn_plan_info(h, 300, 20, True)
+            for kind in ("fwd", "bwd"):
+                p = info[kind]
+                assert p["nchunk"] * p["rows"] >= 20 > (p["nchunk"] - 1) * p["rows"]
+                assert p["nwg"] * p["units"] >= 800 > (p["nwg"] - 1) * p["units"]
+                assert p["grid"] >= p["nwg"] * p["groups"]
+                if p["place"] == 0:
+                    assert p["grid"] == p["nwg"] * p["groups"]
+        assert R.rnn_plan_info(h, 300, 20, False).keys() == {"fwd"}
+        R.rnn_destroy(h)
+    monkeypatch.delenv("RNN_PLACE")
