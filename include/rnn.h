@@ -227,6 +227,28 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
                                   const float* h0, const float* y, void* ws, size_t ws_bytes,
                                   float* dW);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * rnn_forward_inference with the workspace replaced by a fixed device array
+ * of the library, rnn_static_workspace_bytes() bytes (128 MiB: the
+ * single-layer Deep Speech 2 shape, T = 300, B = 20, input = hidden = 800,
+ * needs about 94 MiB), one per device, placed when the library's code is
+ * loaded on that device and held until the process ends.  Arguments and
+ * results as rnn_forward_inference (bitwise equal outputs).  The call
+ * allocates nothing (per-launch profiling events are not recorded in it) and
+ * sets what must start at zero (flags, error word) itself; nothing else
+ * carries over from one call to the next.  Every call on one device shares
+ * that device's array: calls that overlap in time on one device (two host
+ * threads, two streams) race and give undefined results.  An expired bounded
+ * wait (see rnn_device_status) is recorded in that array, where no call
+ * reports it.  Errors: as rnn_forward_inference, and
+ * WORKSPACE_TOO_SMALL when rnn_workspace_size(h, T, B, 0) exceeds the
+ * array. */
+rnn_status_t rnn_forward_inference_static(rnn_handle_t h, void* stream, int T, int B, const float* x,
+                                          const float* h0, const float* c0, const void* W, float* y,
+                                          float* hy, float* cy);
+size_t rnn_static_workspace_bytes(void);
+
 /* Diagnostic: the latency floor of the persistent forward sweep.  Runs the
  * launch that rnn_forward_inference (training = 0) or rnn_forward_training
  * (training = 1) would use for its first recurrent sweep -- the two passes

@@ -30,6 +30,8 @@ from ._binding import (  # noqa: F401
     rnn_workspace_size,
     rnn_forward_inference,
     rnn_forward_training,
+    rnn_forward_inference_static,
+    rnn_static_workspace_bytes,
     rnn_backward_data,
     rnn_exchange_floor,
     rnn_mfma_peak_probe,

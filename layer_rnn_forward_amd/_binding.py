@@ -53,6 +53,7 @@ def load_library():
         "rnn_workspace_size": [vp, i, i, i, psz],
         "rnn_forward_inference": [vp, vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp, sz],
         "rnn_forward_training": [vp, vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp, sz],
+        "rnn_forward_inference_static": [vp, vp, i, i, vp, vp, vp, vp, vp, vp, vp],
         "rnn_backward_data": [vp, vp, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz],
         "rnn_backward_weights": [vp, vp, i, i, vp, vp, vp, vp, sz, vp],
         "rnn_device_status": [vp, vp, vp, sz],
@@ -68,6 +69,8 @@ def load_library():
         f.restype = ctypes.c_int
     lib.rnn_status_string.argtypes = [ctypes.c_int]
     lib.rnn_status_string.restype = ctypes.c_char_p
+    lib.rnn_static_workspace_bytes.argtypes = []
+    lib.rnn_static_workspace_bytes.restype = ctypes.c_size_t
     _LIB = lib
     return lib
 
@@ -197,6 +200,19 @@ def rnn_forward_inference(h, T, B, x, h0, c0, W, y, hy, cy, ws):
 
 def rnn_forward_training(h, T, B, x, h0, c0, W, y, hy, cy, ws):
     _fwd("rnn_forward_training", h, T, B, x, h0, c0, W, y, hy, cy, ws, "rnn_forward_training")
+
+
+def rnn_forward_inference_static(h, T, B, x, h0, c0, W, y, hy, cy):
+    """rnn_forward_inference on the library's fixed device array instead of a
+    caller workspace (allocates nothing; calls on one device must not overlap)."""
+    lib = load_library()
+    _check(lib.rnn_forward_inference_static(h.ptr, _stream(), T, B, _ptr(x, "x"), _ptr(h0, "h0"),
+                                            _ptr(c0, "c0"), _ptr(W, "W", None), _ptr(y, "y"),
+                                            _ptr(hy, "hy"), _ptr(cy, "cy")), "rnn_forward_inference_static")
+
+
+def rnn_static_workspace_bytes() -> int:
+    return int(load_library().rnn_static_workspace_bytes())
 
 
 def rnn_backward_data(h, T, B, y, dy, dhy, dcy, W, h0, c0, dx, dh0, dc0, ws):

@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -921,6 +922,41 @@ rnn_status_t exchange_probe_impl(rnn_desc* h, void* stream, int T, int B, int tr
 
 }  // namespace
 
+// ------------------------------------------------ inference without allocation
+// The workspace of rnn_forward_inference_static: a fixed device array of the
+// library, one copy per device (the runtime places it when the code object is
+// loaded on that device; it is held until the process ends).  Host code never
+// uses the array's name as an address: its device address is looked up once
+// per device, with that device current, and kept.
+static constexpr size_t kStaticScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+rnn_status_t static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return RNN_STATUS_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return RNN_STATUS_DEVICE;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RNN_STATUS_SUCCESS;
+}
+}  // namespace
+
+
 // ================================================================== C ABI
 extern "C" {
 
@@ -1360,6 +1396,25 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
   }
   return RNN_STATUS_SUCCESS;
 }
+
+rnn_status_t rnn_forward_inference_static(rnn_handle_t h, void* stream, int T, int B, const float* x,
+                                          const float* h0, const float* c0, const void* W, float* y,
+                                          float* hy, float* cy) {
+  if (!h || T < 0 || B < 0) return RNN_STATUS_INVALID_ARG;
+  Plan p = make_plan(h, T, B, 0);
+  if (p.status != RNN_STATUS_SUCCESS) return p.status;
+  if (p.total > kStaticScratchBytes) return RNN_STATUS_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  RNN_TRY(static_scratch(&ws));
+  // per-launch timing events are created on demand: kept off here
+  const int prof = h->prof;
+  h->prof = 0;
+  const rnn_status_t st = forward_impl(h, stream, T, B, x, h0, c0, W, y, hy, cy, ws, kStaticScratchBytes, 0);
+  h->prof = prof;
+  return st;
+}
+
+size_t rnn_static_workspace_bytes(void) { return kStaticScratchBytes; }
 
 rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, int training, void* ws,
                                 size_t ws_bytes) {
