@@ -168,14 +168,20 @@ rnn_status_t rnn_weights_size(rnn_handle_t h, int grad, size_t* bytes);
 rnn_status_t rnn_weight_offset(rnn_handle_t h, int grad, int layer, int dir, rnn_param_t which,
                                size_t* byte_offset, size_t* elem_count);
 
-/* Workspace bytes for T steps and batch B: training = 0 for
+/* Source: oneDNN issue #218, the workspace protocol (query the size, then
+ * allocate).
+ * Workspace bytes for T steps and batch B: training = 0 for
  * rnn_forward_inference, training = 1 for the forward_training /
  * backward_data / backward_weights sequence (the size query of the oneDNN
  * workspace protocol).  The size depends on (handle, T, B, training) only.
  * Errors: INVALID_ARG for T < 0, B < 0 or NULL bytes. */
 rnn_status_t rnn_workspace_size(rnn_handle_t h, int T, int B, int training, size_t* bytes);
 
-/* Forward pass without saving intermediates.
+/* Forward pass without saving intermediates.  Source: the MXNet "fused RNN
+ * operator" page, Problem Statement (one fused call for stacked, optionally
+ * bidirectional vanilla / LSTM / GRU layers, inference); oneDNN issue #218 for
+ * the TNC input layout and the (num_layers*num_directions, batch, hidden)
+ * state shape; the GRU equations of its PyTorch snippet.
  *   x   [T, B, I] fp32 (TNC)             y   [T, B, D*H] fp32; direction 0 in
  *   h0  [L*D, B, H] fp32 or NULL (zeros)      columns [0,H), direction 1 in [H,2H)
  *   c0  [L*D, B, H] fp32 or NULL; LSTM only (must be NULL otherwise)
@@ -193,7 +199,11 @@ rnn_status_t rnn_forward_inference(rnn_handle_t h, void* stream, int T, int B, c
                                    const float* h0, const float* c0, const void* W, float* y,
                                    float* hy, float* cy, void* ws, size_t ws_bytes);
 
-/* As rnn_forward_inference, and additionally fills the workspace (at least
+/* Source: oneDNN issue #218, the workspace protocol (the forward-training
+ * call takes the workspace as an output); the MXNet "fused RNN operator" page,
+ * Operator Registration (forward intermediates kept for backward, the buffer
+ * reused across iterations).
+ * As rnn_forward_inference, and additionally fills the workspace (at least
  * rnn_workspace_size(h, T, B, 1) bytes) with what backward_data reuses:
  * post-activation gates and cell states per (layer, direction, step), GRU's
  * W_hn h + b_hn, and every inner layer's output.  The outputs y, hy, cy are
@@ -202,7 +212,11 @@ rnn_status_t rnn_forward_training(rnn_handle_t h, void* stream, int T, int B, co
                                   const float* h0, const float* c0, const void* W, float* y,
                                   float* hy, float* cy, void* ws, size_t ws_bytes);
 
-/* Backward through time, data part.  Must follow rnn_forward_training on the
+/* Source: oneDNN issue #218, the workspace protocol (the backward call takes
+ * the forward's workspace as an input); the MXNet "fused RNN operator" page,
+ * Operator Registration (backward reuses the saved intermediates).  The split
+ * into a data part and a weight part is this library's.
+ * Backward through time, data part.  Must follow rnn_forward_training on the
  * same handle with the same T, B and workspace (else BAD_CALL_ORDER).
  *   y    the forward's y; dy [T, B, D*H]; dhy, dcy [L*D, B, H] or NULL (zeros;
  *        dcy LSTM only); W, h0, c0 as given to the forward.
@@ -215,7 +229,10 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
                                const float* h0, const float* c0, float* dx, float* dh0,
                                float* dc0, void* ws, size_t ws_bytes);
 
-/* Backward through time, weight part.  Must follow rnn_backward_data with the
+/* Source: as rnn_backward_data; the weight gradients of all time steps as
+ * single products follow the "Combined GEMMs" and "Combining Inputs" rows of
+ * the cuDNN-5 optimisation table in Keras issue #3692.
+ * Backward through time, weight part.  Must follow rnn_backward_data with the
  * same T, B and workspace (else BAD_CALL_ORDER).  x, h0 and y are the
  * forward's.  dW (rnn_weights_size(h, 1, .) bytes, layout of
  * rnn_weight_offset with grad = 1) is OVERWRITTEN with dLoss/dW, dLoss/db.
