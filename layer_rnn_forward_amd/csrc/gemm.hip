@@ -31,6 +31,7 @@
 //    stored), and vectors past K read a 16-byte zero vector.
 //  * gemm_nt_kernel, the general fallback (any alignment and K), staging
 //    through registers with element-wise edge handling.
+#include <cstdlib>
 #include <type_traits>
 
 #include "device_util.h"
@@ -242,21 +243,33 @@ __device__ __forceinline__ uint4 lds_read16(const lds_char* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// NS: pipeline stages (LDS 32 KB each); GM: tiles are visited in groups of GM
-// tile rows, column by column inside a group, so that the workgroups running
-// at the same time on one XCD share few A and B row blocks (0: row-major).
-template <bool BF16, int EPI, int NS, int GM>
-__global__ __launch_bounds__(NTHR) void gemm_lds_kernel(const GemmParams p) {
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector memory
+// and `lgkm` LDS/scalar operations are outstanding; export count not waited on.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (((vm >> 4) & 3) << 14) | ((lgkm & 15) << 8) | (7 << 4) | (vm & 15);
+}
+
+// Block tile (64*WM) x (64*WN), WM x WN waves of 64x64; NS pipeline stages
+// of (64*WM + 64*WN) rows x 128 bytes of LDS; GM: tiles are visited in
+// groups of GM tile rows, column by column inside a group, so that the
+// workgroups running at the same time on one XCD share few A and B row
+// blocks (0: row-major).
+template <bool BF16, int EPI, int NS, int GM, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(const GemmParams p) {
   using T = typename Cfg<BF16>::T;
   constexpr int BK = Cfg<BF16>::BK, EPV = Cfg<BF16>::EPV;
-  constexpr int kStages = NS;
+  constexpr int NW = WM * WN;
+  constexpr int TBM = 64 * WM, TBN = 64 * WN;
+  constexpr int SA = TBM * kRowBytes, SB = TBN * kRowBytes;   // one stage of A / of B
+  constexpr int LA = TBM / (8 * NW), LB = TBN / (8 * NW);     // 1 KB loads per wave per stage
+  static_assert(LA * 8 * NW == TBM && LB * 8 * NW == TBN, "whole 8-row load groups per wave");
   static_assert(BK * sizeof(T) == kRowBytes, "one K step is 128 bytes of a row");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * NS * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[NS * (SA + SB)];
   lds_char* const lds = (lds_char*)smem;
 
   const int z = blockIdx.z;
   const int M = p.M, N = p.N, K = p.K;
-  const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
+  const int tm = (M + TBM - 1) / TBM, tn = (N + TBN - 1) / TBN;
   const int nsplit = p.split_k;
   const int total = tm * tn * nsplit;
   const int bid = blockIdx.x;
@@ -272,29 +285,32 @@ __global__ __launch_bounds__(NTHR) void gemm_lds_kernel(const GemmParams p) {
     mi = g * GM + in % gm;
     ni = in / gm;
   }
-  const int m0 = mi * BM, n0 = ni * BN;
+  const int m0 = mi * TBM, n0 = ni * TBN;
   const int kper = ((K + nsplit - 1) / nsplit + BK - 1) / BK * BK;
   const int kbeg = split * kper, kend = min(K, kbeg + kper);
   const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave / WN) * 64, wn = (wave % WN) * 64;
   const int fr = lane & 15, fq = lane >> 4;
 
-  // ---- loader: instruction j of wave w fills rows 8*(4j + w) .. +7 of a
-  // stage (64 lanes x 16 bytes); lane l takes row 8*(4j+w) + l/8, slot l%8,
+  // ---- loader: load j of wave w fills rows 8*(NW*j + w) .. +7 of a stage
+  // (64 lanes x 16 bytes); lane l takes row 8*(NW*j+w) + l/8, slot l%8,
   // i.e. k-vector (l%8) ^ (row & 7)
   const char* zero = reinterpret_cast<const char*>(p.zero16);
   const char* ones = reinterpret_cast<const char*>(p.ones16);
-  const char* arow[4];
-  const char* brow[4];
-  int kvo[4];
+  const char* arow[LA];
+  const char* brow[LB];
+  const int kvo = ((lane & 7) ^ ((lane >> 3) & 7)) * EPV;   // rows 8*g + lane/8: row & 7 == lane/8
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 8 * (4 * j + wave) + (lane >> 3);
-    kvo[j] = (((lane & 7) ^ (r & 7)) * EPV);
+  for (int j = 0; j < LA; ++j) {
+    const int r = 8 * (NW * j + wave) + (lane >> 3);
     arow[j] = reinterpret_cast<const char*>(reinterpret_cast<const T*>(p.A[z]) +
                                             (long long)min(m0 + r, M - 1) * p.lda);
+  }
+#pragma unroll
+  for (int j = 0; j < LB; ++j) {
+    const int r = 8 * (NW * j + wave) + (lane >> 3);
     // the ones row reads the ones vector, and so do rows past N (B may have
     // no real row to re-read when its last row is the ones row)
     const int n = n0 + r;
@@ -303,19 +319,21 @@ __global__ __launch_bounds__(NTHR) void gemm_lds_kernel(const GemmParams p) {
                   : reinterpret_cast<const char*>(reinterpret_cast<const T*>(p.B[z]) + (long long)n * p.ldb);
   }
   auto issue = [&](int st, int k0) {
-    lds_char* sa = lds + st * kStageBytes;
-    lds_char* sb = lds + (kStages + st) * kStageBytes;
+    lds_char* sa = lds + st * SA;
+    lds_char* sb = lds + NS * SA + st * SB;
+    const int k = k0 + kvo;
+    const bool kv = k < kend;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = k0 + kvo[j];
-      const bool kv = k < kend;
+    for (int j = 0; j < LA; ++j) {
       const char* ga = kv ? arow[j] + (size_t)k * sizeof(T) : zero;
-      const char* gb = kv ? (brow[j] ? brow[j] + (size_t)k * sizeof(T) : ones) : zero;
-      const int off = (4 * j + wave) * 1024;
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)ga,
-                                       (void __attribute__((address_space(3)))*)(sa + off), 16, 0, 0);
+                                       (void __attribute__((address_space(3)))*)(sa + (NW * j + wave) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < LB; ++j) {
+      const char* gb = kv ? (brow[j] ? brow[j] + (size_t)k * sizeof(T) : ones) : zero;
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gb,
-                                       (void __attribute__((address_space(3)))*)(sb + off), 16, 0, 0);
+                                       (void __attribute__((address_space(3)))*)(sb + (NW * j + wave) * 1024), 16, 0, 0);
     }
   };
 
@@ -338,21 +356,21 @@ __global__ __launch_bounds__(NTHR) void gemm_lds_kernel(const GemmParams p) {
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt % NS;
     // this thread's loads of step kt are complete once only those of the
-    // steps issued after it (8 each) remain outstanding, and its LDS reads of
-    // step kt-1 once lgkmcnt is 0; the barrier extends both to all threads.
-    // A bare barrier: __syncthreads() would also wait for the later steps'
-    // loads (its fence drains every memory operation).
+    // steps issued after it (LA + LB each) remain outstanding, and its LDS
+    // reads of step kt-1 once lgkmcnt is 0; the barrier extends both to all
+    // threads.  A bare barrier: __syncthreads() would also wait for the
+    // later steps' loads (its fence drains every memory operation).
     const int ahead = min(nk - 1 - kt, NS - 2);
     __builtin_amdgcn_sched_barrier(0);
-    if (NS >= 4 && ahead >= 2) __builtin_amdgcn_s_waitcnt(0x3070 | 16);   // vmcnt(16) lgkmcnt(0)
-    else if (NS >= 3 && ahead == 1) __builtin_amdgcn_s_waitcnt(0x3070 | 8);
-    else __builtin_amdgcn_s_waitcnt(0x3070);                              // vmcnt(0) lgkmcnt(0)
+    if (NS >= 4 && ahead >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * (LA + LB), 0));
+    else if (NS >= 3 && ahead >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_imm(LA + LB, 0));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // every wave has finished step kt-1, so its buffer can be refilled
     if (kt + NS - 1 < nk) issue((kt + NS - 1) % NS, kbeg + (kt + NS - 1) * BK);
-    const lds_char* sa = lds + st * kStageBytes + wm * kRowBytes;
-    const lds_char* sb = lds + (kStages + st) * kStageBytes + wn * kRowBytes;
+    const lds_char* sa = lds + st * SA + wm * kRowBytes;
+    const lds_char* sb = lds + NS * SA + st * SB + wn * kRowBytes;
 #pragma unroll
     for (int ch = 0; ch < CH; ++ch) {
       uint4 af[4], bfr[4];
@@ -383,20 +401,54 @@ __global__ void splitk_reduce_kernel(const GemmParams p) {
   }
 }
 
+// One configuration of the direct-to-LDS kernel: waves WM x WN, stages NS.
+template <bool BF16, int EPI, int NS, int GM, int WM, int WN>
+void launch_lds(const GemmParams& p, int batches, hipStream_t s) {
+  const int tiles = ((p.M + 64 * WM - 1) / (64 * WM)) * ((p.N + 64 * WN - 1) / (64 * WN)) * p.split_k;
+  const int grid = (tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_lds_kernel<BF16, EPI, NS, GM, WM, WN>), dim3(grid, 1, batches), dim3(64 * WM * WN), 0, s, p);
+}
+
 template <bool BF16, int EPI>
 hipError_t launch_one(const GemmParams& p, int batches, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.split_k;
   const int grid = (tiles + 7) / 8 * 8;
   const bool fast = p.a_vec && p.b_vec && p.zero16 && (p.n_ones < 0 || p.ones16) &&
                     p.K % Cfg<BF16>::EPV == 0 && !p.force_general;
-  // two stages (64 KB of LDS, two workgroups per CU) measured faster than
-  // three or four with one workgroup per CU; groups of 8 tile rows helped the
-  // single-pass products and not the split-K weight gradients
-  if (fast && p.split_k == 1)
-    hipLaunchKernelGGL((gemm_lds_kernel<BF16, EPI, 2, 8>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
-  else if (fast)
-    hipLaunchKernelGGL((gemm_lds_kernel<BF16, EPI, 2, 0>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
-  else hipLaunchKernelGGL((gemm_nt_kernel<BF16, EPI>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
+  // tuning: the direct-to-LDS kernel's shape (waves, stages)
+  static const int variant = [] {
+    const char* v = std::getenv("RNN_GEMM_VARIANT");
+    return v ? std::atoi(v) : 0;
+  }();
+  if (fast) {
+    const bool g8 = p.split_k == 1;   // groups of 8 tile rows help the single-pass products
+    int v = variant;
+    if (v == 0 && BF16 && EPI == EPI_BIAS && p.split_k == 1) {
+      // the input projection: 256x256 tiles on sixteen waves (one workgroup
+      // per CU) do a unit of work in 2/3 of the time of two 128x128
+      // workgroups per CU (measured: 33 us per round of 256x256 tiles vs
+      // 25 us per round of 2 x 128x128 per CU at K = 800), but come in
+      // rounds of 256 tiles instead of 512: take them when the rounds they
+      // need cost less
+      const int r128 = (((p.M + 127) / 128) * ((p.N + 127) / 128) + 511) / 512;
+      const int r256 = (((p.M + 255) / 256) * ((p.N + 255) / 256) + 255) / 256;
+      if (33.2 * r256 < 25.0 * r128) v = 3;
+    }
+    switch (v) {
+      case 1: g8 ? launch_lds<BF16, EPI, 3, 8, 4, 2>(p, batches, s) : launch_lds<BF16, EPI, 3, 0, 4, 2>(p, batches, s); break;
+      case 2: g8 ? launch_lds<BF16, EPI, 3, 8, 2, 4>(p, batches, s) : launch_lds<BF16, EPI, 3, 0, 2, 4>(p, batches, s); break;
+      case 3: g8 ? launch_lds<BF16, EPI, 2, 8, 4, 4>(p, batches, s) : launch_lds<BF16, EPI, 2, 0, 4, 4>(p, batches, s); break;
+      case 4: g8 ? launch_lds<BF16, EPI, 4, 8, 2, 2>(p, batches, s) : launch_lds<BF16, EPI, 4, 0, 2, 2>(p, batches, s); break;
+      case 5: g8 ? launch_lds<BF16, EPI, 3, 8, 2, 2>(p, batches, s) : launch_lds<BF16, EPI, 3, 0, 2, 2>(p, batches, s); break;
+      case 6: g8 ? launch_lds<BF16, EPI, 2, 8, 4, 2>(p, batches, s) : launch_lds<BF16, EPI, 2, 0, 4, 2>(p, batches, s); break;
+      default:
+        // two stages (64 KB of LDS, two workgroups per CU) measured faster
+        // than three or four with one workgroup per CU
+        g8 ? launch_lds<BF16, EPI, 2, 8, 2, 2>(p, batches, s) : launch_lds<BF16, EPI, 2, 0, 2, 2>(p, batches, s);
+    }
+  } else {
+    hipLaunchKernelGGL((gemm_nt_kernel<BF16, EPI>), dim3(grid, 1, batches), dim3(NTHR), 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.split_k <= 1) return e;
   size_t mn = (size_t)p.M * p.N;
