@@ -161,13 +161,12 @@ def cpu_baseline(w, synth, min_seconds):
 
 def source_hash():
     """sha256[:16] over every native source of the library (kernels, their
-    headers and the host planner, which decides grids and layouts) and the
-    public header: a counter figure taken under another hash is stale."""
+    headers and the host planner, which decides grids and layouts): a
+    counter figure taken under another hash is stale."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(root, "layer_rnn_forward_amd", "csrc")
     files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".cpp")))
-    files.append(os.path.join(root, "include", "rnn.h"))
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())

@@ -57,7 +57,16 @@ extern "C" {
 typedef struct rnn_desc* rnn_handle_t;
 typedef int rnn_status_t;
 
-typedef enum {
+/* The enums below are passed as ints.  C++ gives them an int underlying type,
+ * so that a value outside the listed ones (which the calls reject with
+ * INVALID_ARG) is still a valid value of the type. */
+#ifdef __cplusplus
+#define RNN_ENUM_BASE : int
+#else
+#define RNN_ENUM_BASE
+#endif
+
+typedef enum RNN_ENUM_BASE {
   RNN_TANH = 0,      /* h' = tanh(W_ih x + b_ih + W_hh h + b_hh) */
   RNN_LSTM = 1,      /* gates i, f, g, o in this memory order */
   RNN_GRU = 2,       /* gates r, z, n; n = tanh(W_in x + b_in + r*(W_hn h + b_hn)),
@@ -67,13 +76,13 @@ typedef enum {
   RNN_GRU_PAPER = 4  /* as RNN_GRU_TF with h' = (1-z)*h + z*n (original-paper flavour) */
 } rnn_mode_t;
 
-typedef enum { RNN_W_F32 = 0, RNN_W_BF16 = 1 } rnn_wtype_t;
+typedef enum RNN_ENUM_BASE { RNN_W_F32 = 0, RNN_W_BF16 = 1 } rnn_wtype_t;
 
 /* Which parameter tensor of one (layer, direction), for rnn_weight_offset. */
-typedef enum { RNN_W_IH = 0, RNN_W_HH = 1, RNN_B_IH = 2, RNN_B_HH = 3 } rnn_param_t;
+typedef enum RNN_ENUM_BASE { RNN_W_IH = 0, RNN_W_HH = 1, RNN_B_IH = 2, RNN_B_HH = 3 } rnn_param_t;
 
 /* Recurrent-sweep schedule (rnn_set_schedule). */
-typedef enum {
+typedef enum RNN_ENUM_BASE {
   RNN_SCHED_AUTO = 0,       /* persistent when every workgroup fits on the GPU at once, else stepped */
   RNN_SCHED_PERSISTENT = 1, /* one launch per sweep; error RNN_STATUS_NOT_CORESIDENT if it cannot fit */
   RNN_SCHED_STEPPED = 2     /* one launch per time step (no device-wide waits) */

@@ -25,7 +25,10 @@ class RNNError(RuntimeError):
 
 
 def lib_path() -> str:
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "librnn_mi355x.so")
+    """The in-tree library, or the build named by RNN_LIB (e.g. the
+    host-sanitizer build of build.build_sanitized)."""
+    return os.environ.get("RNN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "librnn_mi355x.so")
 
 
 def load_library():

@@ -48,25 +48,54 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# host-only sanitizers for the C-ABI translation unit (the planner and its
+# workspace carve); device code is built as usual
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+SAN_LIB = os.path.join(BUILD, "sanitize", "librnn_mi355x_san.so")
+
+
+def _build(out_lib: str, obj_dir: str, sanitize: bool, verbose: bool) -> str:
+    os.makedirs(obj_dir, exist_ok=True)
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
+        obj = os.path.join(obj_dir, src.replace(".", "_") + ".o")
         objs.append(obj)
         extra = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj])
-    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        san = SANITIZE if (sanitize and src == "rnn_api.cpp") else []
+        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), *san, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max_workers=min(16, len(cmds))) as ex:
         outs = list(ex.map(_run, cmds))
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    tmp = LIB + ".tmp"
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = out_lib + ".tmp"
+    link_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libsan"] \
+        if sanitize else []
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *link_san, "-o", tmp, *objs])
+    os.replace(tmp, out_lib)
+    return out_lib
+
+
+def build(verbose: bool = False) -> str:
+    return _build(LIB, BUILD, False, verbose)
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The same library with the host code of the C ABI built under
+    AddressSanitizer and UndefinedBehaviorSanitizer (run it with the ASan
+    runtime preloaded and RNN_LIB pointing at the returned path)."""
+    return _build(SAN_LIB, os.path.dirname(SAN_LIB), True, verbose)
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (for LD_PRELOAD)."""
+    r = subprocess.run([HIPCC.replace("hipcc", "amdclang++") if os.path.exists(HIPCC.replace("hipcc", "amdclang++"))
+                        else HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    return r.stdout.strip()
 
 
 if __name__ == "__main__":
