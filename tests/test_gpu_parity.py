@@ -319,3 +319,42 @@ def test_xcd_local_groups(monkeypatch, mode, D, wtype):
     g = run_gpu(mode, 1, D, case, wtype)
     o = run_oracle(mode, 1, D, case)
     check(compare(g, o, mode, 1, D), *TOL[wtype])
+
+
+@pytest.mark.parametrize("wtype", ["f32", "bf16"])
+def test_weights_at_unaligned_offset(wtype):
+    """W may sit at any 4-byte offset of a caller's parameter arena: with the
+    packed buffer 4 bytes past a 16-byte boundary the products must not take
+    their 16-byte vector loads of W_ih, and the results match the oracle."""
+    mode, L, D, T, B, I, H = "lstm", 2, 1, 9, 5, 64, 48
+    _announce("unaligned W", wtype)
+    case = _case(mode, L, D, T, B, I, H, wtype, seed=71)
+    h = R.rnn_create(mode, L, D, I, H, wtype)
+    packed = R.pack_weights(h, case["params"])
+    arena = torch.zeros(packed.numel() + 64, dtype=torch.uint8, device="cuda")
+    W = arena[4:4 + packed.numel()]
+    W.copy_(packed)
+    assert W.data_ptr() % 16 == 4
+    xd = torch.as_tensor(case["x"]).float().cuda()
+    h0 = torch.as_tensor(case["h0"]).float().cuda()
+    c0 = torch.as_tensor(case["c0"]).float().cuda()
+    y = torch.full((T, B, D * H), float("nan"), device="cuda")
+    hy = torch.full((L * D, B, H), float("nan"), device="cuda")
+    cy = torch.full((L * D, B, H), float("nan"), device="cuda")
+    ws = torch.empty(R.rnn_workspace_size(h, T, B, 1), dtype=torch.uint8, device="cuda")
+    R.rnn_forward_training(h, T, B, xd, h0, c0, W, y, hy, cy, ws)
+    dy = torch.as_tensor(case["dy"]).float().cuda()
+    dx = torch.full((T, B, I), float("nan"), device="cuda")
+    dh0 = torch.full((L * D, B, H), float("nan"), device="cuda")
+    dc0 = torch.full((L * D, B, H), float("nan"), device="cuda")
+    R.rnn_backward_data(h, T, B, y, dy, None, None, W, h0, c0, dx, dh0, dc0, ws)
+    dW = torch.full((R.rnn_weights_size(h, 1) // 4,), float("nan"), device="cuda")
+    R.rnn_backward_weights(h, T, B, xd, h0, y, ws, dW)
+    torch.cuda.synchronize()
+    assert R.rnn_device_status(h, ws) == 0
+    g = {"y": y.double().cpu().numpy(), "hy": hy.double().cpu().numpy(), "cy": cy.double().cpu().numpy(),
+         "dx": dx.double().cpu().numpy(), "dh0": dh0.double().cpu().numpy(), "dc0": dc0.double().cpu().numpy(),
+         "dW": R.unpack_weights(h, dW, grad=1)}
+    R.rnn_destroy(h)
+    o = run_oracle(mode, L, D, dict(case, dhy=None, dcy=None), pass_grads=False)
+    check(compare(g, o, mode, L, D), *TOL[wtype])
