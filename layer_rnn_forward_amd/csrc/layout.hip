@@ -78,7 +78,11 @@ __global__ __launch_bounds__(256) void transpose_kernel(const TransposeBatch bat
     const int rl = (tid >> 4) + 16 * i;
     const int r = r0 + rl, c = c0 + cg;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
-    const char* row = r < p.R ? src_row<IN_BF>(p, r) : nullptr;
+    // the input row of output index r (a permuted reduction index: map)
+    int rn = r;
+    if (p.map == 1) rn = gg_col_source(r, p.mU, p.mG, p.mH, p.mNwg);
+    else if (p.map == 2) rn = tb_k_source(r, p.mBc, p.mT, p.mB);
+    const char* row = (r < p.R && rn >= 0) ? src_row<IN_BF>(p, rn) : nullptr;
     if (row) {
       if (p.vec_in && c + 3 < p.C) {
         if constexpr (IN_BF) {

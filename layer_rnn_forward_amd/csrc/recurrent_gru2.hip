@@ -386,18 +386,26 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
       ring_store<BF16>(en, offB + (size_t)UJ * granB, qv ? daz : 0.f);
     }
     publish(p.flags, wg, (unsigned)(2 * s + 2));
-    if (qv) {
-      // gate gradients (dG_i = dG_h) for the dX and weight-gradient products
+    {
+      // gate gradients (dG_i = dG_h) for the dX product (dG, columns gg_col)
+      // and the weight-gradient products (dG^T, columns tb_k); units past H
+      // (dG) and rows past the batch (dG^T) get zeros
       using X = typename std::conditional<BF16, uint16_t, float>::type;
-      const float dgv[3] = {dar, daz, dan};
-      const size_t rowi = (size_t)t * B + qbg;
-      const size_t col0 = (size_t)d * GH + qu;
+      const float dgv[3] = {qv ? dar : 0.f, qv ? daz : 0.f, qv ? dan : 0.f};
+      if (qw) {
+        const size_t rowi = (size_t)t * B + qbg;
 #pragma unroll
-      for (int g = 0; g < 3; ++g) {
-        const size_t col = col0 + (size_t)g * H;
-        const X vi = to_x<BF16>(dgv[g]);
-        reinterpret_cast<X*>(p.dg)[rowi * p.dg_ld + col] = vi;
-        reinterpret_cast<X*>(p.dgT)[col * p.tb_ld + rowi] = vi;
+        for (int g = 0; g < 3; ++g)
+          reinterpret_cast<X*>(p.dg)[rowi * p.dg_ld + gg_col(d, slice, g, qj, U, 3, p.nwg)] = to_x<BF16>(dgv[g]);
+      }
+      const int zq = q - (q / U) * U;
+      if ((qv || q < p.Bc * U) && zq < Uact) {
+        const int kb = qw ? qb : q / U;
+        const size_t kp = (size_t)tb_k(c, t, kb, T, p.Bc);
+        const size_t col0 = (size_t)d * GH + u0 + zq;
+#pragma unroll
+        for (int g = 0; g < 3; ++g)
+          reinterpret_cast<X*>(p.dgT)[(col0 + (size_t)g * H) * p.tb_ld + kp] = to_x<BF16>(dgv[g]);
       }
     }
     lds_barrier();   // red and sh_dh are reused by the next step

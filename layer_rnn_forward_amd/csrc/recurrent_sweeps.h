@@ -621,19 +621,29 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
       }
     }
     if (p.persistent && !final_phase) publish(p.flags, wg, (unsigned)(s + 1), w0);
-    if (!final_phase && qv) {
-      // gate gradients for the dX product ([T*B, D*G*H]) and, transposed
-      // ([D*G*H, T*B]), for the weight-gradient products (later kernels)
+    if (!final_phase) {
+      // gate gradients for the dX product (dG, columns gg_col) and,
+      // transposed, for the weight-gradient products (dG^T, columns tb_k):
+      // read by later kernels; units past H (dG) and rows past the batch
+      // (dG^T) get zeros
       using X = XT<BF16>;
-      const size_t rowi = (size_t)t * B + qbg;
-      const size_t col0 = (size_t)d * GH + qu;
+      if (qw) {
+        const size_t rowi = (size_t)t * B + qbg;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const size_t col = col0 + (size_t)g * H;
-        const X vi = to_x<BF16>(dgi[g]);
-        reinterpret_cast<X*>(p.dg)[rowi * p.dg_ld + col] = vi;
-        reinterpret_cast<X*>(p.dgT)[col * p.tb_ld + rowi] = vi;
-        if (MODE == MODE_GRU) reinterpret_cast<X*>(p.dghT)[col * p.tb_ld + rowi] = to_x<BF16>(dgh[g]);
+        for (int g = 0; g < G; ++g)
+          reinterpret_cast<X*>(p.dg)[rowi * p.dg_ld + gg_col(d, slice, g, qj, U, G, p.nwg)] = to_x<BF16>(dgi[g]);
+      }
+      const int zq = q - (q / U) * U;
+      if ((qv || q < p.Bc * U) && zq < Uact) {
+        const int kb = qw ? qb : q / U;   // rows past the batch: zeros
+        const size_t kp = (size_t)tb_k(c, t, kb, T, p.Bc);
+        const size_t col0 = (size_t)d * GH + u0 + zq;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const size_t col = col0 + (size_t)g * H;
+          reinterpret_cast<X*>(p.dgT)[col * p.tb_ld + kp] = to_x<BF16>(qv ? dgi[g] : 0.f);
+          if (MODE == MODE_GRU) reinterpret_cast<X*>(p.dghT)[col * p.tb_ld + kp] = to_x<BF16>(qv ? dgh[g] : 0.f);
+        }
       }
     }
     lds_barrier();   // red and sh_* are reused by the next step

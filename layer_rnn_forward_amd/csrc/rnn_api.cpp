@@ -67,9 +67,10 @@ struct Plan {
   size_t off_yin = 0, yin_slot = 0;
   int yin_slots = 0;
   size_t off_res = 0, res_layer = 0;
-  // gate gradients in the compute type: dG [T*B][dg_ld], dG^T [D*G*H][tb_ld]
+  // gate gradients in the compute type: dG [T*B][dg_ld] (dg_k columns in
+  // gg_col order), dG^T [D*G*H][tb_ld] (tb_k columns in tb_k order)
   size_t off_dg = 0, off_dgT = 0, off_dghT = 0, dg_layer = 0, dgT_layer = 0;
-  int dg_ld = 0, tb_ld = 0;
+  int dg_ld = 0, tb_ld = 0, dg_k = 0, tb_k = 0;
   size_t off_dy = 0, dy_slot = 0;
   // dropped inputs of layers 1..L-1 (training with dropout), slot l-1
   size_t off_xd = 0, xd_slot = 0;
@@ -475,8 +476,12 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
   }
   // operand-preparation scratch (fwd: layer input in bf16)
   const size_t Ipad = input_pad(h);
-  p.dg_ld = ceil_div((int)dgh, 8) * 8;
-  p.tb_ld = ceil_div((int)std::max<size_t>(TB, 1), 8) * 8;
+  // reduction extents of the dX and dW products in the backward sweep's
+  // store orders (gg_col, tb_k): whole workgroup slices and batch chunks
+  p.dg_k = training ? h->D * p.bwd.nwg * h->G * p.bwd.U : (int)dgh;
+  p.tb_k = training ? p.bwd.nchunk * T * p.bwd.Bc : (int)TB;
+  p.dg_ld = ceil_div(p.dg_k, 8) * 8;
+  p.tb_ld = ceil_div(std::max(p.tb_k, 1), 8) * 8;
   size_t scr = bf ? align_up(TB * Ipad * 2) : 0;
   if (training) {
     const int R = reserve_slots(kmode(h));
@@ -499,7 +504,7 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
     size_t part_dx = 0;
     for (int l = 0; l < h->L; ++l) {
       const int I_l = in_width(h, l);
-      const int sdx = gemm_split(h, (int)TB, I_l, (int)dgh, 1);
+      const int sdx = gemm_split(h, (int)TB, I_l, p.dg_k, 1);
       if (sdx > 1) part_dx = std::max(part_dx, (size_t)sdx * TB * I_l * 4);
     }
     scr = std::max(scr, align_up(Ipad * p.dg_ld * es) + align_up(part_dx));
@@ -509,14 +514,14 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
     for (int l = 0; l < h->L; ++l) {
       const int I_l = in_width(h, l);
       if (dw_fused(h, l))
-        part = std::max(part, (size_t)gemm_split(h, h->G * h->H, h->H + 1, (int)TB, 2) * 2 *
+        part = std::max(part, (size_t)gemm_split(h, h->G * h->H, h->H + 1, p.tb_k, 2) * 2 *
                                   (size_t)h->G * h->H * (h->H + 1) * 4);
-      part = std::max(part, (size_t)gemm_split(h, (int)dgh, I_l + 1, (int)TB, 1) * dgh * (I_l + 1) * 4);
-      part = std::max(part, (size_t)gemm_split(h, h->G * h->H, h->H + 1, (int)TB, h->D) * h->D *
+      part = std::max(part, (size_t)gemm_split(h, (int)dgh, I_l + 1, p.tb_k, 1) * dgh * (I_l + 1) * 4);
+      part = std::max(part, (size_t)gemm_split(h, h->G * h->H, h->H + 1, p.tb_k, h->D) * h->D *
                                 (size_t)h->G * h->H * (h->H + 1) * 4);
       if (is_gru2(h))   // their dW_hh in two products, 2H and H rows
         for (int m = 1; m <= 2; ++m)
-          part = std::max(part, (size_t)gemm_split(h, m * h->H, h->H + 1, (int)TB, h->D) * h->D *
+          part = std::max(part, (size_t)gemm_split(h, m * h->H, h->H + 1, p.tb_k, h->D) * h->D *
                                     (size_t)m * h->H * (h->H + 1) * 4);
     }
     scr = std::max(scr, wts + align_up(part));
@@ -1159,8 +1164,13 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
     tp.alt_r0 = tp.alt_r1 = 0;
     tp.out = wT;
     tp.ld_out = p.dg_ld;
-    tp.R = (int)dgh;
+    tp.R = p.dg_k;   // columns in the sweep's dG order (gg_col)
     tp.C = in_width(h, l);
+    tp.map = 1;
+    tp.mU = p.bwd.U;
+    tp.mG = h->G;
+    tp.mH = h->H;
+    tp.mNwg = p.bwd.nwg;
     ProfScope ps(h, s, K_PREP);
     return dev(rnn_launch_transpose(tp, bf, bf, s, fill));
   };
@@ -1205,7 +1215,7 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
     GemmParams g{};
     g.M = T * B;
     g.N = I_l;
-    g.K = (int)dgh;
+    g.K = p.dg_k;
     g.A[0] = b.dg;
     g.lda = p.dg_ld;
     g.B[0] = wT;
@@ -1276,17 +1286,25 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
                                             : yl(l - 1));
     const char* dgT = at<char>(wsm, p.off_dgT + p.dgT_layer * l);
     const char* dghT = h->mode == RNN_GRU ? at<char>(wsm, p.off_dghT + p.dgT_layer * l) : dgT;
-    {  // X^T [I_l][T*B] and H_prev^T [D][H][T*B] (shifted one step, h0 at the start),
-       // in as few launches as the batched transpose allows
+    {  // X^T [I_l][tb_ld] and H_prev^T [D][H][tb_ld] (shifted one step, h0 at the
+       // start), columns in the sweep's dG^T order (tb_k), in as few launches as
+       // the batched transpose allows
       ProfScope ps(h, s, K_PREP);
       std::vector<TransposeParams> jobs;
+      auto kmap = [&](TransposeParams& q) {
+        q.R = p.tb_k;
+        q.map = 2;
+        q.mBc = p.bwd.Bc;
+        q.mT = T;
+        q.mB = B;
+      };
       TransposeParams tp{};
       tp.src = X;
       tp.ld_src = I_l;
       tp.out = xT;
       tp.ld_out = p.tb_ld;
-      tp.R = (int)TB;
       tp.C = I_l;
+      kmap(tp);
       jobs.push_back(tp);
       for (int d = 0; d < h->D; ++d) {
         TransposeParams th{};
@@ -1299,8 +1317,8 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
         th.alt_r1 = th.alt_r0 + B;
         th.out = hT + (size_t)d * h->H * p.tb_ld * es;
         th.ld_out = p.tb_ld;
-        th.R = (int)TB;
         th.C = h->H;
+        kmap(th);
         if (d == 1) {   // a row's first reverse step starts from h0
           th.lengths = h->lengths;
           th.len_B = B;
@@ -1313,8 +1331,8 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
           tr.ld_src = (long long)R * h->H;
           tr.out = rhT + (size_t)d * h->H * p.tb_ld * es;
           tr.ld_out = p.tb_ld;
-          tr.R = (int)TB;
           tr.C = h->H;
+          kmap(tr);
           jobs.push_back(tr);
         }
       }
@@ -1325,7 +1343,7 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
       GemmParams g{};
       g.M = GH;
       g.N = h->H + 1;
-      g.K = (int)TB;
+      g.K = p.tb_k;
       g.A[0] = dgT;
       g.A[1] = dghT;
       g.B[0] = xT;
@@ -1350,7 +1368,7 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
       GemmParams g{};
       g.M = dgh;
       g.N = I_l + 1;
-      g.K = (int)TB;
+      g.K = p.tb_k;
       g.A[0] = dgT;
       g.lda = p.tb_ld;
       g.B[0] = xT;
@@ -1375,7 +1393,7 @@ rnn_status_t rnn_backward_weights(rnn_handle_t h, void* stream, int T, int B, co
       GemmParams g{};
       g.M = rhT ? (part_i == 0 ? 2 * h->H : h->H) : GH;
       g.N = h->H + 1;
-      g.K = (int)TB;
+      g.K = p.tb_k;
       g.lda = p.tb_ld;
       g.ldb = p.tb_ld;
       g.n_ones = h->H;

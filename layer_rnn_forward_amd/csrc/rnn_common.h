@@ -84,7 +84,52 @@ struct TransposeParams {
   // set by the launcher: 16-byte (fp32) / 8-byte (bf16) row loads and
   // 16-byte stores of 8 output elements are aligned
   int vec_in, vec_out;
+  // the output's contiguous index r is a permuted reduction index of a
+  // product (gg_col / tb_k below); the input row it gathers is
+  //   map 1: gg_col_source(r, mU, mG, mH, mNwg)   (W_ih^T for the dX product)
+  //   map 2: tb_k_source(r, mBc, mT, mB)           (X^T, H_prev^T for dW)
+  // a hole (no input row) reads zeros; map 0: row r
+  int map;
+  int mU, mG, mH, mNwg;
+  int mBc, mT, mB;
 };
+
+// Reduction-index orders of the gate gradients, chosen so that each
+// workgroup of the backward sweep writes whole cache lines that no other
+// workgroup (on another XCD) shares:
+//  * dG [T*B][dg_ld], the A operand of the dX product: column
+//    gg_col(d, slice, g, j) = d*nwg*G*U + slice*G*U + g*U + j for unit
+//    slice*U + j of gate g, direction d -- the G*U values a workgroup makes
+//    for one row are contiguous;
+//  * dG^T [D*G*H][tb_ld] (rows in the natural gate order), the A operand of
+//    the weight-gradient products: column tb_k(c, t, bl) = c*T*Bc + t*Bc + bl
+//    for batch row c*Bc + bl of chunk c at step t -- one workgroup's values of
+//    a row at successive steps are adjacent.
+// The other operand of each product (W_ih^T; X^T, H_prev^T) is gathered in
+// the same order; positions of units past H or batch rows past B are zero in
+// both.
+__host__ __device__ inline long long gg_col(int d, int slice, int g, int j, int U, int G, int nwg) {
+  return (long long)d * nwg * G * U + (long long)slice * G * U + (long long)g * U + j;
+}
+__host__ __device__ inline long long tb_k(int c, int t, int bl, int T, int Bc) {
+  return (long long)c * T * Bc + (long long)t * Bc + bl;
+}
+// Natural row (d*G*H + g*H + u) of column r of dG, or -1 past H.
+__host__ __device__ inline int gg_col_source(int r, int U, int G, int H, int nwg) {
+  const int CG = nwg * G * U;
+  const int d = r / CG, rem = r - d * CG;
+  const int slice = rem / (G * U), r2 = rem - slice * G * U;
+  const int g = r2 / U, j = r2 - g * U;
+  const int u = slice * U + j;
+  return u < H ? d * G * H + g * H + u : -1;
+}
+// Natural row (t*B + b) of column k of dG^T, or -1 past B.
+__host__ __device__ inline int tb_k_source(int k, int Bc, int T, int B) {
+  const int c = k / (T * Bc), rem = k - c * T * Bc;
+  const int t = rem / Bc, bl = rem - t * Bc;
+  const int b = c * Bc + bl;
+  return b < B ? t * B + b : -1;
+}
 
 // ------------------------------------------------------------- recurrence
 // One forward launch covers `nlayers` layers (a wavefront when > 1) or one
@@ -163,11 +208,11 @@ struct BwdParams {
   const float* dy;        // [T, B, D*H]
   const float* dhy;       // [D, B, H] or null
   const float* dcy;
-  void* dg;               // dG_i [T*B, D*G*H] in the compute type (dX operand)
-  void* dgT;              // dG_i^T [D*G*H, T*B] (dW_ih operand)
-  void* dghT;             // GRU: dG_h^T [D*G*H, T*B] (dW_hh operand)
-  int dg_ld;              // row stride of dg (>= D*G*H)
-  int tb_ld;              // row stride of dgT / dghT (>= T*B)
+  void* dg;               // dG_i [T*B][dg_ld] in the compute type, columns gg_col (dX operand)
+  void* dgT;              // dG_i^T [D*G*H][tb_ld], columns tb_k (dW_ih operand)
+  void* dghT;             // GRU: dG_h^T, as dgT (dW_hh operand)
+  int dg_ld;              // row stride of dg (>= D*nwg*G*U)
+  int tb_ld;              // row stride of dgT / dghT (>= nchunk*T*Bc)
   float* dh0;             // [D, B, H] or null
   float* dc0;
   float* st_dh;           // carries between stepped launches [D*nchunk... ] laid out [D][B][H]
