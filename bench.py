@@ -521,17 +521,25 @@ def main():
                          "kernel_ms_per_step": {k: round(v["total_ms"] / 3, 4) for k, v in k2.items()}}
         out["workloads"] = sec
     if not args.no_small_batch and w.layers == 1:
-        # serving-size batches: forward-inference latency of the same layer
+        # serving-size batches: forward-inference latency of the same layer,
+        # and of the vanilla tanh RNN of the same size (whose small batches
+        # get XCD-local recurrence groups)
         import dataclasses
-        sb = {}
-        for Bs in (1, 2, 4):
-            rs = Runner(dataclasses.replace(w, B=Bs), torch, R, synth)
-            f_ms, _ = rs.timed(rs.fwd, max(5, args.steps // 2), args.warmup)
-            med = float(np.median(f_ms))
-            sb[str(Bs)] = {"fwd_ms": round(med, 4), "us_per_step": round(1000.0 * med / w.T, 3),
-                           "plan": R.rnn_plan_info(rs.h, w.T, Bs, False)["fwd"]}
-            del rs
-        out["small_batch_fwd"] = sb
+
+        def serving(wb):
+            sb = {}
+            for Bs in (1, 2, 4):
+                rs = Runner(dataclasses.replace(wb, B=Bs), torch, R, synth)
+                f_ms, _ = rs.timed(rs.fwd, max(5, args.steps // 2), args.warmup)
+                med = float(np.median(f_ms))
+                sb[str(Bs)] = {"fwd_ms": round(med, 4), "us_per_step": round(1000.0 * med / wb.T, 3),
+                               "plan": R.rnn_plan_info(rs.h, wb.T, Bs, False)["fwd"]}
+                del rs
+            return sb
+
+        out["small_batch_fwd"] = serving(w)
+        if w.mode != "rnn_tanh":
+            out["small_batch_fwd_tanh"] = serving(dataclasses.replace(w, mode="rnn_tanh", name=w.name + "_tanh"))
     if args.blas_reference and w.wtype == "bf16":
         out["vendor_gemm_reference"] = blas_reference(torch, w)
     if not args.no_cpu:
