@@ -321,6 +321,27 @@ def test_xcd_local_groups(monkeypatch, mode, D, wtype):
     check(compare(g, o, mode, 1, D), *TOL[wtype])
 
 
+def test_default_placement(monkeypatch):
+    """With no placement asked for, the bf16 tanh RNN takes XCD-local groups
+    (persistent sweeps) and the gated cells and fp32 weights the linear
+    placement; a stepped schedule keeps the plan's units on a linear grid."""
+    monkeypatch.delenv("RNN_PLACE", raising=False)
+    T, B, H = 300, 20, 800
+    for mode, wtype, want in (("rnn_tanh", "bf16", 1), ("rnn_tanh", "f32", 0), ("lstm", "bf16", 0),
+                              ("gru", "bf16", 0)):
+        h = R.rnn_create(mode, 1, 1, H, H, wtype)
+        info = R.rnn_plan_info(h, T, B, True)
+        assert info["fwd"]["place"] == want and info["bwd"]["place"] == want, (mode, wtype, info)
+        if want:
+            R.rnn_set_schedule(h, R.SCHED_STEPPED)
+            st = R.rnn_plan_info(h, T, B, True)
+            for k in ("fwd", "bwd"):
+                assert st[k]["place"] == 0 and st[k]["persistent"] == 0, st
+                assert (st[k]["units"], st[k]["nchunk"]) == (info[k]["units"], info[k]["nchunk"]), (st, info)
+                assert st[k]["grid"] == st[k]["nwg"] * st[k]["groups"], st
+        R.rnn_destroy(h)
+
+
 @pytest.mark.parametrize("wtype", ["f32", "bf16"])
 def test_weights_at_unaligned_offset(wtype):
     """W may sit at any 4-byte offset of a caller's parameter arena: with the
