@@ -162,7 +162,8 @@ __global__ __launch_bounds__(NTHR) void gemm_nt_kernel(const GemmParams p) {
   const T* __restrict__ A = reinterpret_cast<const T*>(p.A[z]);
   const T* __restrict__ Bm = reinterpret_cast<const T*>(p.B[z]);
   const long long lda = p.lda, ldb = p.ldb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index in a scalar register (the same in every lane)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int fr = lane & 15, fq = lane >> 4;
   const bool avec = p.a_vec, bvec = p.b_vec;
@@ -290,7 +291,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(const GemmParams
   const int kbeg = split * kper, kend = min(K, kbeg + kper);
   const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index in a scalar register (the same in every lane)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = (wave / WN) * 64, wn = (wave % WN) * 64;
   const int fr = lane & 15, fq = lane >> 4;
 

@@ -45,7 +45,9 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
   __shared__ float sh_h[NROW * NCOL];
   __shared__ int s_fail;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is the same in every lane: a scalar register keeps the
+  // wave's K range, loop bounds and branches scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
   const int wg = logical_wg(p.place, p.nwg, p.ngroups);
   if (wg < 0) return;   // an idle slot of the XCD-local placement
@@ -226,7 +228,9 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
   __shared__ float sh_dh[NROW * NCOL];
   __shared__ int s_fail;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is the same in every lane: a scalar register keeps the
+  // wave's K range, loop bounds and branches scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
   const int wg = logical_wg(p.place, p.nwg, p.ngroups);
   if (wg < 0) return;   // an idle slot of the XCD-local placement

@@ -96,6 +96,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   __shared__ float sh_c[NCOL * NROW];
   __shared__ int s_fail;
 
+  // (a scalar wave index, which helps the backward, measured 2-5 % slower here)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
 
@@ -408,7 +409,9 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
   __shared__ float sh_dc[NROW * NCOL];
   __shared__ int s_fail;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is the same in every lane: a scalar register keeps the
+  // wave's K range, loop bounds and branches scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
   const int wg = logical_wg(p.place, p.nwg, p.ngroups);
   if (wg < 0) return;   // an idle slot of the XCD-local placement
