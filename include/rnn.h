@@ -314,7 +314,8 @@ rnn_status_t rnn_mfma_peak_probe(void* stream, int kind, int blocks, int iters, 
  * out[8..15] the backward sweep (zeros when training = 0), each as: batch
  * chunks, rows per chunk, hidden units per workgroup, workgroups per group,
  * groups, grid (workgroups launched), placement (0: linear, 1: XCD-local
- * recurrence groups), persistent (1) or stepped (0).  Host only; touches no
+ * recurrence groups, r >= 2: runs of r consecutive workgroups per XCD),
+ * persistent (1) or stepped (0).  Host only; touches no
  * device memory.  Errors: INVALID_ARG for a NULL handle or out, T < 0 or
  * B < 0; UNSUPPORTED when no kernel configuration fits. */
 rnn_status_t rnn_plan_info(rnn_handle_t h, int T, int B, int training, int* out);

@@ -104,12 +104,22 @@ __device__ bool wave_wait(const unsigned* flags, unsigned* err, unsigned spin_li
 // (XCD-local groups): the dispatcher deals workgroups to the XCDs round-robin
 // (blockIdx.x % kXcds); group g gets slots (g / kXcds) * nwg .. + nwg - 1 of
 // XCD g % kXcds, so all producers and consumers of one group share that
-// XCD's L2.  Correctness never depends on where a workgroup actually runs:
-// the exchange is coherent at agent scope.
+// XCD's L2.  place r >= 2: runs of r consecutive logical workgroups on one
+// XCD, so that neighbouring slices, whose per-unit fp32 data (the input
+// projection, the reserve, dy) share 128-byte lines, are read through one
+// L2.  Correctness never depends on where a workgroup actually runs: the
+// exchange is coherent at agent scope.
 __device__ __forceinline__ int logical_wg(int place, int nwg, int ngroups) {
   const int b = blockIdx.x;
   if (place == 0) return b;
   const int x = b % kXcds, k = b / kXcds;
+  if (place >= 2) {
+    // runs of `place` consecutive workgroups per XCD: workgroup k of XCD x
+    // takes logical index (k / r) * 8r + x * r + k % r
+    const int r = place;
+    const int l = (k / r) * (kXcds * r) + x * r + k % r;
+    return l < nwg * ngroups ? l : -1;
+  }
   const int row = k / nwg, j = k - row * nwg;
   const int g = row * kXcds + x;
   return g < ngroups ? g * nwg + j : -1;

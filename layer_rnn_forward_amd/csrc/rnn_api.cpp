@@ -310,12 +310,25 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
   // at H = 800, T = 300: B = 1 inference 0.56 vs 0.68 ms, B = 20 training
   // step 1.39 vs 1.44 ms, the 5-layer bidirectional step 8.06 vs 8.34 ms);
   // the gated cells, whose slices are three or four times wider, and fp32
-  // weights measured slower.  RNN_PLACE=0 / 1 forces either placement.
+  // weights measured slower.  RNN_PLACE=1 forces XCD-local groups.
   const int place_env = env_int("RNN_PLACE", -1);
   const bool place_auto = h->G == 1 && bf;
   // (A stepped sweep takes the same units and chunks on a linear grid, so
   // that both schedules do bitwise the same arithmetic.)
   const bool place_req = place_env == 1 || (place_env < 0 && place_auto);
+  // Otherwise runs of consecutive slices per XCD whose units fill one
+  // 128-byte line of the fp32 per-unit data (input projection, reserve, dy),
+  // so that each line is fetched through one L2 instead of two to four:
+  // the default for the one-exchange forward sweeps (DS2 LSTM: inference
+  // sweep 503 -> 272 MB fetched, inference 0.835 -> 0.824 ms; GRU forward
+  // -1 %), the backward and the two-exchange GRU flavours (whose forward
+  // measured 1.8 % slower) only with RNN_PLACE=2 (LSTM backward 656 -> 530
+  // MB fetched but 0.4 % slower, GRU 1.2 %); RNN_PLACE=0 gives the plain
+  // linear grid to every sweep.
+  auto line_runs = [&](int U, bool fwd) {
+    const bool want = place_env == 2 || (fwd && place_env < 0 && !is_gru2(h));
+    return want && U < 32 && 32 % U == 0 ? 32 / U : 0;
+  };
   // co-residency: returns whether every workgroup of the sweep fits on the
   // GPU at once (with LDS staging if it fits, else without)
   auto fit = [&](SweepPlan& sp, bool fwd, size_t stage_bytes) {
@@ -365,7 +378,7 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
         !plan_fwd(h, fmt, p.fwd.Bc, h->D * p.fwd.nchunk, false, &p.fwd, Ux))
       return false;
     if (p.fwd.nwg > kMaxWaitFlags) return false;
-    p.fwd.place = Ux > 0 ? 1 : 0;
+    p.fwd.place = Ux > 0 ? 1 : line_runs(p.fwd.U, true);
     p.fwd.grid = sweep_grid(p.fwd.place, p.fwd.nwg, p.fwd.groups);
     // exchange rings: one entry per step, entries padded to 1 KB
     const int s_total = T + (p.wavefront ? h->L : 1) - 1;
@@ -421,7 +434,7 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
       if (!plan_bwd(h, ceil_div(p.bwd.Bc, 16), p.bwd.Bc, h->D * p.bwd.nchunk, &p.bwd, Ux) ||
           p.bwd.nwg > kMaxWaitFlags)
         return false;
-      p.bwd.place = Ux > 0 ? 1 : 0;
+      p.bwd.place = Ux > 0 ? 1 : line_runs(p.bwd.U, false);
       p.bwd.grid = sweep_grid(p.bwd.place, p.bwd.nwg, p.bwd.groups);
       // the flavours with two exchanges: da_n (one gate per slice) in the
       // first ring, [da_r, da_z] (two gates) in the second

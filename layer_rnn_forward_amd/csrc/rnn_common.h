@@ -12,10 +12,14 @@ constexpr int kMaxWaitFlags = 512;       // flags one workgroup may poll per ste
 constexpr int kWaitPerLane = kMaxWaitFlags / 64;
 constexpr int kXcds = 8;                 // XCDs of one MI355X (SPX mode), each with its own L2
 
-// Grid of a sweep with `groups` groups of `nwg` workgroups: linear, or
-// XCD-local (place 1: logical_wg in recurrent_util.h; idle slots exit at once).
+// Grid of a sweep with `groups` groups of `nwg` workgroups: linear (place
+// 0), XCD-local (place 1) or runs of `place` consecutive workgroups per XCD
+// (place >= 2); logical_wg in recurrent_util.h maps them, idle slots exit at
+// once.
 __host__ __device__ constexpr int sweep_grid(int place, int nwg, int groups) {
-  return place ? kXcds * ((groups + kXcds - 1) / kXcds) * nwg : nwg * groups;
+  return place == 1   ? kXcds * ((groups + kXcds - 1) / kXcds) * nwg
+         : place >= 2 ? (nwg * groups + kXcds * place - 1) / (kXcds * place) * (kXcds * place)
+                      : nwg * groups;
 }
 
 enum Mode { MODE_TANH = 0, MODE_LSTM = 1, MODE_GRU = 2 };

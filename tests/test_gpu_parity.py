@@ -321,17 +321,28 @@ def test_xcd_local_groups(monkeypatch, mode, D, wtype):
     check(compare(g, o, mode, 1, D), *TOL[wtype])
 
 
+def _runs(units):
+    # run placement: consecutive slices whose units fill one 128-byte line of fp32
+    return 32 // units if units < 32 and 32 % units == 0 else 0
+
+
 def test_default_placement(monkeypatch):
     """With no placement asked for, the bf16 tanh RNN takes XCD-local groups
-    (persistent sweeps) and the gated cells and fp32 weights the linear
-    placement; a stepped schedule keeps the plan's units on a linear grid."""
+    (persistent sweeps); the gated cells and fp32 weights take runs of
+    line-sharing slices per XCD in the forward (not the two-exchange GRU
+    flavours) and the linear placement in the backward; a stepped schedule
+    keeps the plan's units on a linear grid."""
     monkeypatch.delenv("RNN_PLACE", raising=False)
     T, B, H = 300, 20, 800
     for mode, wtype, want in (("rnn_tanh", "bf16", 1), ("rnn_tanh", "f32", 0), ("lstm", "bf16", 0),
-                              ("gru", "bf16", 0)):
+                              ("gru", "bf16", 0), ("gru_tf", "bf16", 0)):
         h = R.rnn_create(mode, 1, 1, H, H, wtype)
         info = R.rnn_plan_info(h, T, B, True)
-        assert info["fwd"]["place"] == want and info["bwd"]["place"] == want, (mode, wtype, info)
+        want_fwd = want or (0 if mode == "gru_tf" else _runs(info["fwd"]["units"]))
+        assert info["fwd"]["place"] == want_fwd and info["bwd"]["place"] == want, (mode, wtype, info)
+        if want_fwd >= 2:
+            assert info["fwd"]["grid"] % (8 * want_fwd) == 0, info
+            assert info["fwd"]["grid"] >= info["fwd"]["nwg"] * info["fwd"]["groups"], info
         if want:
             R.rnn_set_schedule(h, R.SCHED_STEPPED)
             st = R.rnn_plan_info(h, T, B, True)
@@ -340,6 +351,27 @@ def test_default_placement(monkeypatch):
                 assert (st[k]["units"], st[k]["nchunk"]) == (info[k]["units"], info[k]["nchunk"]), (st, info)
                 assert st[k]["grid"] == st[k]["nwg"] * st[k]["groups"], st
         R.rnn_destroy(h)
+
+
+@pytest.mark.parametrize("mode,D,wtype", list(itertools.product(MODES, (1, 2), ("bf16", "f32"))))
+def test_line_run_placement(monkeypatch, mode, D, wtype):
+    """Runs of line-sharing slices per XCD in both sweeps (RNN_PLACE=2; the
+    forward's default) at the DS2 hidden width: the plan takes them, the
+    padded grid's idle slots exit, and the results match the oracle."""
+    monkeypatch.setenv("RNN_PLACE", "2")
+    T, B, I, H = 24, 20, 96, 800
+    _announce("line_runs", mode, D, wtype, T, B, I, H)
+    h = R.rnn_create(mode, 1, D, I, H, wtype)
+    info = R.rnn_plan_info(h, T, B, True)
+    R.rnn_destroy(h)
+    print(info, flush=True)
+    for k in ("fwd", "bwd"):
+        assert info[k]["place"] == _runs(info[k]["units"]), info
+    assert info["fwd"]["place"] >= 2 or info["bwd"]["place"] >= 2, info
+    case = _case(mode, 1, D, T, B, I, H, wtype, seed=53)
+    g = run_gpu(mode, 1, D, case, wtype)
+    o = run_oracle(mode, 1, D, case)
+    check(compare(g, o, mode, 1, D), *TOL[wtype])
 
 
 @pytest.mark.parametrize("wtype", ["f32", "bf16"])
