@@ -53,9 +53,11 @@ def _run(cmd):
 SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
 SAN_LIB = os.path.join(BUILD, "sanitize", "librnn_mi355x_san.so")
+# the ordering-perturbation test build, in-tree beside the library
+PERTURB_LIB = os.path.join(PKG, "librnn_mi355x_perturb.so")
 
 
-def _build(out_lib: str, obj_dir: str, sanitize: bool, verbose: bool) -> str:
+def _build(out_lib: str, obj_dir: str, sanitize: bool, verbose: bool, defines=()) -> str:
     os.makedirs(obj_dir, exist_ok=True)
     objs = []
     cmds = []
@@ -64,7 +66,8 @@ def _build(out_lib: str, obj_dir: str, sanitize: bool, verbose: bool) -> str:
         objs.append(obj)
         extra = ["-x", "hip"] if src.endswith(".cpp") else []
         san = SANITIZE if (sanitize and src == "rnn_api.cpp") else []
-        cmds.append([HIPCC, *FLAGS, *EXTRA.get(src, []), *san, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC, *FLAGS, *defines, *EXTRA.get(src, []), *san, *extra, "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     with ThreadPoolExecutor(max_workers=min(16, len(cmds))) as ex:
         outs = list(ex.map(_run, cmds))
     if verbose:
@@ -81,6 +84,14 @@ def _build(out_lib: str, obj_dir: str, sanitize: bool, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     return _build(LIB, BUILD, False, verbose)
+
+
+def build_perturbed(verbose: bool = False) -> str:
+    """The same library with the exchange's ordering points perturbed
+    (-DRNN_PERTURB: pseudo-random pauses at every flag wait and flag
+    publication); its results must be bitwise those of the normal build.
+    Load it with RNN_LIB pointing at the returned path."""
+    return _build(PERTURB_LIB, os.path.join(BUILD, "perturb"), False, verbose, defines=("-DRNN_PERTURB",))
 
 
 def build_sanitized(verbose: bool = False) -> str:

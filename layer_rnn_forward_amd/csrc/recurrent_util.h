@@ -55,6 +55,35 @@ __device__ __forceinline__ void ring_store(char* base, size_t off, float v) {
 // given by the waits around it.
 __device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
+// Ordering-perturbation build (compiled with -DRNN_PERTURB, a test build):
+// a pseudo-random pause of 0 to ~6 us, half the time none, at every ordering
+// point of the exchange -- each wave's entry to a flag wait, each wave's
+// entry to a flag publication (before its stores are waited for) and a
+// workgroup's exit from it -- so that producers, consumers and the waves of
+// one workgroup run with skews they never have in the normal build.  It
+// changes no arithmetic: a correct protocol gives bitwise the results of the
+// normal build.  Without the macro it is empty.
+__device__ __forceinline__ void perturb_pause(unsigned a, unsigned b, unsigned site) {
+#ifdef RNN_PERTURB
+  unsigned x = a * 0x9E3779B1u ^ b * 0x85EBCA77u ^ (site + 1u) * 0xC2B2AE3Du;
+  x ^= x >> 15;
+  x *= 0x2C1B3C6Du;
+  x ^= x >> 12;
+  x *= 0x297A2D39u;
+  x ^= x >> 15;
+  const unsigned n = (x & 1u) ? 0u : (x >> 1) & 31u;
+  for (unsigned i = 0; i < __builtin_amdgcn_readfirstlane(n); ++i) __builtin_amdgcn_s_sleep(8);
+#else
+  (void)a;
+  (void)b;
+  (void)site;
+#endif
+}
+
+__device__ __forceinline__ unsigned wave_tag() {
+  return blockIdx.x * 16u + (unsigned)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
 // Bounded wait of one wave for the flags of two ranges of producers,
 // [a0, a0 + na) and [b0, b0 + nb) (flag indices), to reach `target`.
 // Returns false (uniformly over the wave) if the wait expired -- the error
@@ -70,6 +99,7 @@ __device__ bool wave_wait(const unsigned* flags, unsigned* err, unsigned spin_li
     flag_store(err, 1u);
     return false;
   }
+  perturb_pause(wave_tag(), target, 0u);
   const int lane = threadIdx.x & 63;
   const int total = na + nb;
   const int nper = (total + 63) / 64;   // flags per lane, uniform
@@ -147,18 +177,21 @@ __device__ __forceinline__ void lds_barrier() {
 // stores before the wait and the flag store after it.
 __device__ __forceinline__ void publish(unsigned* flags, int id, unsigned v, bool wave0_only = false) {
   compiler_fence();
+  perturb_pause(wave_tag(), v, 1u);
   if (wave0_only) {
     if (threadIdx.x < 64) {
       __builtin_amdgcn_s_waitcnt(0);
       compiler_fence();
       if (threadIdx.x == 0) flag_store(flags + (size_t)id * kFlagStride, v);
     }
+    perturb_pause(blockIdx.x, v, 2u);
     return;
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   compiler_fence();
   if (threadIdx.x == 0) flag_store(flags + (size_t)id * kFlagStride, v);
+  perturb_pause(blockIdx.x, v, 2u);
 }
 
 // MFMA over the granules this wave holds.  K chunk kk takes granules
