@@ -183,7 +183,13 @@ rnn_status_t rnn_weight_offset(rnn_handle_t h, int grad, int layer, int dir, rnn
  * rnn_forward_inference, training = 1 for the forward_training /
  * backward_data / backward_weights sequence (the size query of the oneDNN
  * workspace protocol).  The size depends on (handle, T, B, training) only.
- * Errors: INVALID_ARG for T < 0, B < 0 or NULL bytes. */
+ * Errors: INVALID_ARG for T < 0, B < 0 or NULL bytes; UNSUPPORTED when the
+ * recurrent sweeps have no kernel configuration for the shape (the compute
+ * calls return the same status): each workgroup keeps its slice of W_hh in
+ * registers, which bounds the hidden size.  Hidden sizes up to 1024 with
+ * fp32 weights and 2048 with bf16 weights are supported for every mode,
+ * stack and batch; larger ones only where the mode, the pass and the batch
+ * chunking leave room (at most 2048 / 4096). */
 rnn_status_t rnn_workspace_size(rnn_handle_t h, int T, int B, int training, size_t* bytes);
 
 /* Forward pass without saving intermediates.  Source: the MXNet "fused RNN
@@ -202,8 +208,10 @@ rnn_status_t rnn_workspace_size(rnn_handle_t h, int T, int B, int training, size
  * valid: hy/cy are copied from h0/c0 (zeros if NULL) and y is empty.
  * Using a workspace here invalidates a pending training sequence on the same
  * workspace.  Errors: INVALID_ARG (NULL required pointers, c0/cy given for a
- * non-LSTM mode, misaligned ws), WORKSPACE_TOO_SMALL, NOT_CORESIDENT (only
- * with RNN_SCHED_PERSISTENT), DEVICE (launch failure). */
+ * non-LSTM mode, misaligned ws), WORKSPACE_TOO_SMALL, UNSUPPORTED (hidden
+ * size beyond the kernels' limit, rnn_workspace_size), NOT_CORESIDENT (with
+ * RNN_SCHED_PERSISTENT, or for the two-exchange GRU flavours, when the
+ * sweep's workgroups cannot all be resident), DEVICE (launch failure). */
 rnn_status_t rnn_forward_inference(rnn_handle_t h, void* stream, int T, int B, const float* x,
                                    const float* h0, const float* c0, const void* W, float* y,
                                    float* hy, float* cy, void* ws, size_t ws_bytes);

@@ -371,7 +371,13 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
     p.wavefront = wf0;
     const int fl = p.wavefront ? h->L : 1;
     const int fmt = ceil_div(p.fwd.Bc, 16);
-    if (!plan_fwd(h, fmt, p.fwd.Bc, fl * h->D * p.fwd.nchunk, p.wavefront, &p.fwd, Ux)) return false;
+    if (!plan_fwd(h, fmt, p.fwd.Bc, fl * h->D * p.fwd.nchunk, p.wavefront, &p.fwd, Ux)) {
+      // a wavefront layer also holds its W_ih slice (twice the K range):
+      // when that fits no configuration, the layers run one launch each
+      if (!p.wavefront) return false;
+      p.wavefront = false;
+      if (!plan_fwd(h, fmt, p.fwd.Bc, h->D * p.fwd.nchunk, false, &p.fwd, Ux)) return false;
+    }
     // wavefront: every workgroup polls its own and the layer below's flags
     if (p.wavefront && 2 * p.fwd.nwg > kMaxWaitFlags) p.wavefront = false;
     if (!p.wavefront && p.fwd.groups != h->D * p.fwd.nchunk &&

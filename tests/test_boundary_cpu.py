@@ -102,6 +102,26 @@ def test_workspace_size_properties(R):
         R.rnn_workspace_size(h, -1, 20, 1)
 
 
+@pytest.mark.parametrize("mode", ["rnn_tanh", "lstm", "gru", "gru_tf", "gru_paper"])
+def test_hidden_size_limit(R, mode):
+    """The register-resident W_hh slices bound the hidden size: 1024 (fp32
+    weights) and 2048 (bf16 weights) are supported for every mode, stack and
+    batch, inference and training (a unidirectional stack whose wavefront
+    would not fit runs its layers one launch each); one unit more with one
+    row and one layer is UNSUPPORTED, cleanly."""
+    for wtype, hmax in (("f32", 1024), ("bf16", 2048)):
+        for L, D, B in ((1, 1, 1), (3, 1, 1), (3, 1, 20), (2, 2, 5), (1, 2, 128)):
+            h = R.rnn_create(mode, L, D, 64, hmax, wtype)
+            for training in (0, 1):
+                assert R.rnn_workspace_size(h, 16, B, training) > 0, (wtype, L, D, B, training)
+            R.rnn_destroy(h)
+        h = R.rnn_create(mode, 1, 1, 64, hmax + 1, wtype)
+        for training in (0, 1):
+            with pytest.raises(R.RNNError, match="unsupported"):
+                R.rnn_workspace_size(h, 16, 1, training)
+        R.rnn_destroy(h)
+
+
 def test_dropout_setter_and_workspace(R):
     h = R.rnn_create("lstm", 3, 2, 64, 48)
     base_tr = R.rnn_workspace_size(h, 20, 8, 1)

@@ -374,6 +374,37 @@ def test_line_run_placement(monkeypatch, mode, D, wtype):
     check(compare(g, o, mode, 1, D), *TOL[wtype])
 
 
+@pytest.mark.parametrize("mode,L,D,wtype,H", [
+    ("lstm", 1, 1, "bf16", 2048), ("gru", 1, 2, "f32", 1024), ("rnn_tanh", 2, 2, "bf16", 2048),
+    ("gru_tf", 1, 1, "bf16", 2048), ("lstm", 3, 1, "bf16", 2048), ("gru", 3, 1, "f32", 1024)])
+def test_maximum_hidden_size(mode, L, D, wtype, H):
+    """The largest hidden size supported for every shape (1024 with fp32
+    weights, 2048 with bf16), training end to end against the oracle; the
+    unidirectional stacks at that size are too wide for the layer wavefront
+    (each layer would hold W_ih and W_hh) and run one launch per layer."""
+    T, B, I = 5, 3, 64
+    _announce("max_hidden", mode, L, D, wtype, T, B, I, H)
+    h = R.rnn_create(mode, L, D, I, H, wtype)
+    info = R.rnn_plan_info(h, T, B, True)
+    R.rnn_destroy(h)
+    print(info, flush=True)
+    if D == 1 and L > 1:
+        assert info["fwd"]["groups"] == info["fwd"]["nchunk"], info   # no wavefront
+    case = _case(mode, L, D, T, B, I, H, wtype, seed=57)
+    g = run_gpu(mode, L, D, case, wtype)
+    o = run_oracle(mode, L, D, case)
+    check(compare(g, o, mode, L, D), *TOL[wtype])
+
+
+def test_wavefront_at_moderate_width():
+    """Below that width the unidirectional stack keeps the layer wavefront
+    (every layer's groups in one launch)."""
+    h = R.rnn_create("lstm", 3, 1, 64, 512, "bf16")
+    info = R.rnn_plan_info(h, 5, 3, True)
+    R.rnn_destroy(h)
+    assert info["fwd"]["groups"] == 3 * info["fwd"]["nchunk"], info
+
+
 @pytest.mark.parametrize("wtype", ["f32", "bf16"])
 def test_weights_at_unaligned_offset(wtype):
     """W may sit at any 4-byte offset of a caller's parameter arena: with the
