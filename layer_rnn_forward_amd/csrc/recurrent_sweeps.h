@@ -83,7 +83,14 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   constexpr bool RSWZ = NT == 4 && MT == 1;
   constexpr bool RSWZ2 = BF16 && NT == 2 && MT == 1;
   constexpr int RSTR = (RSWZ || RSWZ2) ? NCOL : (MT == 1 ? NCOL + 4 : NCOL + 1);
-  __shared__ float red[NW][NROW][RSTR];
+  __shared__ __attribute__((aligned(16))) float red[NW][NROW][RSTR];
+  // column order of the products and of red: unit-major (column n is gate
+  // n % GB of unit n / GB, so a unit's gates are adjacent and the LSTM
+  // epilogue reads them as one 16-byte value per wave) with one row tile;
+  // gate-major (gate n / U, unit n % U) with two, whose register-bound
+  // kernels spilled more weight fragments into the step loop with the
+  // unit-major order (5-layer wavefront sweep 1.81 -> 2.12 ms)
+  constexpr bool UMAJ = MT == 1;
   auto rcol = [](int row, int col) {
     if constexpr (RSWZ) return col ^ ((((row ^ (row >> 2)) & 3)) << 4);
     else if constexpr (RSWZ2) return col ^ ((((row >> 1) & 1) | (((row ^ (row >> 2)) & 1) << 1)) << 3);
@@ -166,7 +173,14 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int e = 0; e < PER; ++e) v[e] = 0u;
       const int n = nt * 16 + fr;
-      const int gb = n / U, j = n - gb * U;
+      int j, gb;
+      if constexpr (UMAJ) {
+        j = n / GB;
+        gb = n - j * GB;
+      } else {
+        gb = n / U;
+        j = n - gb * U;
+      }
       if (live && gl < nmine && gb < GB && j < Uact) {
         int gate = gb;
         bool use_x = true, use_h = true;
@@ -326,15 +340,25 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
       float gxv[4];
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) gxv[gi] = inproj ? bconst[gi] : gxl[gi];
-      float pre[4];
+      float pre[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (UMAJ && MODE == MODE_LSTM && RSTR % 4 == 0) {
+        // the unit's four gates are one 16-byte read per wave
 #pragma unroll
-      for (int gb = 0; gb < 4; ++gb) {
-        float v = 0.f;
-        if (gb < GB) {
-#pragma unroll
-          for (int w = 0; w < NW; ++w) v += red[w][qb][rcol(qb, gb * U + qj)];
+        for (int w = 0; w < NW; ++w) {
+          const float4 v4 = *reinterpret_cast<const float4*>(&red[w][qb][rcol(qb, qj * 4)]);
+          pre[0] += v4.x;
+          pre[1] += v4.y;
+          pre[2] += v4.z;
+          pre[3] += v4.w;
         }
-        pre[gb] = v;
+      } else {
+#pragma unroll
+        for (int gb = 0; gb < 4; ++gb) {
+          if (gb < GB) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) pre[gb] += red[w][qb][rcol(qb, UMAJ ? qj * GB + gb : gb * U + qj)];
+          }
+        }
       }
       const float hprev = sh_h[shix];
       const bool tv = t < qlen;
