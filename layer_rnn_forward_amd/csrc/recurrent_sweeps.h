@@ -346,17 +346,26 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           const float4 v4 = *reinterpret_cast<const float4*>(&red[w][qb][rcol(qb, qj * 4)]);
-          pre[0] += v4.x;
-          pre[1] += v4.y;
-          pre[2] += v4.z;
-          pre[3] += v4.w;
+          if (w == 0) {
+            pre[0] = v4.x;
+            pre[1] = v4.y;
+            pre[2] = v4.z;
+            pre[3] = v4.w;
+          } else {
+            pre[0] += v4.x;
+            pre[1] += v4.y;
+            pre[2] += v4.z;
+            pre[3] += v4.w;
+          }
         }
       } else {
 #pragma unroll
         for (int gb = 0; gb < 4; ++gb) {
           if (gb < GB) {
+            const int col = rcol(qb, UMAJ ? qj * GB + gb : gb * U + qj);
+            pre[gb] = red[0][qb][col];
 #pragma unroll
-            for (int w = 0; w < NW; ++w) pre[gb] += red[w][qb][rcol(qb, UMAJ ? qj * GB + gb : gb * U + qj)];
+            for (int w = 1; w < NW; ++w) pre[gb] += red[w][qb][col];
           }
         }
       }
