@@ -54,22 +54,35 @@ template <bool BF16> constexpr int kchunk() { return BF16 ? 32 : 16; }
 __device__ __forceinline__ float sigmoidf_(float a) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * a));
 }
+// SELECT: evaluate both forms and pick one (no divergent branch between the
+// lanes of the two ranges), else branch; which is faster depends on the
+// kernel's register allocation, so the caller chooses (same results).
+template <bool SELECT = true>
 __device__ __forceinline__ float tanhf_(float a) {
-  // both forms are evaluated and one is selected: no divergent branch
-  // between lanes of the two ranges
   const float x = fabsf(a);
-  const float z = a * a;
-  const float p = -1382.0f / 155925.0f;
-  float r = p * z + 62.0f / 2835.0f;
-  r = r * z - 17.0f / 315.0f;
-  r = r * z + 2.0f / 15.0f;
-  r = r * z - 1.0f / 3.0f;
-  float small = a + a * z * r;
-  float big = copysignf(1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(2.8853900817779268f * x)), a);
-  // (an empty asm statement that uses both keeps the compiler from sinking
-  // either form back into a branch)
-  asm volatile("" : "+v"(small), "+v"(big));
-  return x < 0.25f ? small : big;
+  if constexpr (SELECT) {
+    const float z = a * a;
+    float r = (-1382.0f / 155925.0f) * z + 62.0f / 2835.0f;
+    r = r * z - 17.0f / 315.0f;
+    r = r * z + 2.0f / 15.0f;
+    r = r * z - 1.0f / 3.0f;
+    float small = a + a * z * r;
+    float big = copysignf(1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(2.8853900817779268f * x)), a);
+    // (an empty asm statement that uses both keeps the compiler from sinking
+    // either form back into a branch)
+    asm volatile("" : "+v"(small), "+v"(big));
+    return x < 0.25f ? small : big;
+  } else {
+    if (x < 0.25f) {
+      const float z = a * a;
+      float r = (-1382.0f / 155925.0f) * z + 62.0f / 2835.0f;
+      r = r * z - 17.0f / 315.0f;
+      r = r * z + 2.0f / 15.0f;
+      r = r * z - 1.0f / 3.0f;
+      return a + a * z * r;
+    }
+    return copysignf(1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(2.8853900817779268f * x)), a);
+  }
 }
 
 // ---------------------------------------------------------------- coherence

@@ -91,6 +91,11 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   // kernels spilled more weight fragments into the step loop with the
   // unit-major order (5-layer wavefront sweep 1.81 -> 2.12 ms)
   constexpr bool UMAJ = MT == 1;
+  // tanh form (tanhf_): select in general; branch in the two-row-tile
+  // kernels and the eight-wave bf16 LSTM one (measured: 5-layer wavefront
+  // sweep 1.95 vs 2.03 ms, DS2 LSTM training forward 721 vs 735 us; the
+  // others 1-2 % faster with the select)
+  constexpr bool TSEL = !(MT == 2 || (MODE == MODE_LSTM && BF16 && NW == 8));
   auto rcol = [](int row, int col) {
     if constexpr (RSWZ) return col ^ ((((row ^ (row >> 2)) & 3)) << 4);
     else if constexpr (RSWZ2) return col ^ ((((row >> 1) & 1) | (((row ^ (row >> 2)) & 1) << 1)) << 3);
@@ -358,15 +363,28 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
             pre[3] += v4.w;
           }
         }
-      } else {
+      } else if constexpr (UMAJ) {
 #pragma unroll
         for (int gb = 0; gb < 4; ++gb) {
           if (gb < GB) {
-            const int col = rcol(qb, UMAJ ? qj * GB + gb : gb * U + qj);
+            const int col = rcol(qb, qj * GB + gb);
             pre[gb] = red[0][qb][col];
 #pragma unroll
             for (int w = 1; w < NW; ++w) pre[gb] += red[w][qb][col];
           }
+        }
+      } else {
+        // (the two-row-tile kernels sum from zero: seeding from the first
+        // wave changed their register allocation, 5-layer wavefront sweep
+        // 1.81 -> 1.94 ms)
+#pragma unroll
+        for (int gb = 0; gb < 4; ++gb) {
+          float v = 0.f;
+          if (gb < GB) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v += red[w][qb][rcol(qb, gb * U + qj)];
+          }
+          pre[gb] = v;
         }
       }
       const float hprev = sh_h[shix];
@@ -374,11 +392,11 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
       if (MODE == MODE_LSTM) {
         const float ig = sigmoidf_(pre[0] + gxv[0]);
         const float fg = sigmoidf_(pre[1] + gxv[1]);
-        const float gg = tanhf_(pre[2] + gxv[2]);
+        const float gg = tanhf_<TSEL>(pre[2] + gxv[2]);
         const float og = sigmoidf_(pre[3] + gxv[3]);
         const float cprev = sh_c[shix];
         const float cn = tv ? fg * cprev + ig * gg : cprev;
-        hnew = og * tanhf_(cn);
+        hnew = og * tanhf_<TSEL>(cn);
         sh_c[shix] = cn;
         rv[0] = ig; rv[1] = fg; rv[2] = gg; rv[3] = og; rv[4] = cn;
       } else if (MODE == MODE_GRU) {
@@ -387,11 +405,11 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         float ghn, gin;
         if (inproj) { gin = pre[2] + gxv[2]; ghn = pre[3] + gxv[3]; }
         else { gin = gxv[2]; ghn = pre[2] + bhn; }
-        const float ng = tanhf_(gin + rg * ghn);
+        const float ng = tanhf_<TSEL>(gin + rg * ghn);
         hnew = (1.f - zg) * ng + zg * hprev;
         rv[0] = rg; rv[1] = zg; rv[2] = ng; rv[3] = ghn;
       } else {
-        hnew = tanhf_(pre[0] + gxv[0]);
+        hnew = tanhf_<TSEL>(pre[0] + gxv[0]);
       }
       if (!tv) hnew = hprev;
       sh_h[shix] = hnew;
