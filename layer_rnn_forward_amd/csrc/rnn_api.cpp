@@ -321,12 +321,14 @@ Plan make_plan(const rnn_desc* h, int T, int B, int training, double drop = 0.0)
   // so that each line is fetched through one L2 instead of two to four:
   // the default for the one-exchange forward sweeps (DS2 LSTM: inference
   // sweep 503 -> 272 MB fetched, inference 0.835 -> 0.824 ms; GRU forward
-  // -1 %), the backward and the two-exchange GRU flavours (whose forward
-  // measured 1.8 % slower) only with RNN_PLACE=2 (LSTM backward 656 -> 530
-  // MB fetched but 0.4 % slower, GRU 1.2 %); RNN_PLACE=0 gives the plain
-  // linear grid to every sweep.
+  // -1 %) and the LSTM backward (656 -> 530 MB fetched, 801 -> 794 us);
+  // the other backward sweeps and the two-exchange GRU flavours (whose
+  // forward measured 1.8 % slower) take them only with RNN_PLACE=2 (GRU
+  // backward 788 -> 793 us); RNN_PLACE=0 gives the plain linear grid to
+  // every sweep.
   auto line_runs = [&](int U, bool fwd) {
-    const bool want = place_env == 2 || (fwd && place_env < 0 && !is_gru2(h));
+    const bool want = place_env == 2 ||
+                      (place_env < 0 && !is_gru2(h) && (fwd || h->mode == RNN_LSTM));
     return want && U < 32 && 32 % U == 0 ? 32 / U : 0;
   };
   // co-residency: returns whether every workgroup of the sweep fits on the

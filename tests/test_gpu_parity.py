@@ -330,8 +330,9 @@ def test_default_placement(monkeypatch):
     """With no placement asked for, the bf16 tanh RNN takes XCD-local groups
     (persistent sweeps); the gated cells and fp32 weights take runs of
     line-sharing slices per XCD in the forward (not the two-exchange GRU
-    flavours) and the linear placement in the backward; a stepped schedule
-    keeps the plan's units on a linear grid."""
+    flavours) and, for the LSTM, in the backward, the linear placement in
+    the other backward sweeps; a stepped schedule keeps the plan's units on
+    a linear grid."""
     monkeypatch.delenv("RNN_PLACE", raising=False)
     T, B, H = 300, 20, 800
     for mode, wtype, want in (("rnn_tanh", "bf16", 1), ("rnn_tanh", "f32", 0), ("lstm", "bf16", 0),
@@ -339,7 +340,8 @@ def test_default_placement(monkeypatch):
         h = R.rnn_create(mode, 1, 1, H, H, wtype)
         info = R.rnn_plan_info(h, T, B, True)
         want_fwd = want or (0 if mode == "gru_tf" else _runs(info["fwd"]["units"]))
-        assert info["fwd"]["place"] == want_fwd and info["bwd"]["place"] == want, (mode, wtype, info)
+        want_bwd = want or (_runs(info["bwd"]["units"]) if mode == "lstm" else 0)
+        assert info["fwd"]["place"] == want_fwd and info["bwd"]["place"] == want_bwd, (mode, wtype, info)
         if want_fwd >= 2:
             assert info["fwd"]["grid"] % (8 * want_fwd) == 0, info
             assert info["fwd"]["grid"] >= info["fwd"]["nwg"] * info["fwd"]["groups"], info
