@@ -316,6 +316,20 @@ rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, int 
  * iters <= 0 or a null `out`; DEVICE for a launch error. */
 rnn_status_t rnn_mfma_peak_probe(void* stream, int kind, int blocks, int iters, float* out);
 
+/* Diagnostic: checks the fp32 -> bf16 rounding that every bf16 product
+ * operand and exchanged value goes through (round to nearest even, the
+ * rounding the bf16-weight path states) on the device: for every fp32 bit
+ * pattern in
+ * [first, first + count) (within 0 .. 2^32) the library's conversion is
+ * compared with round-to-nearest-even written out on the bits, and a NaN
+ * must stay a NaN.  Adds the number of mismatches to *mismatches (a device
+ * pointer to one unsigned 64-bit integer that the caller initialises);
+ * enqueues on `stream` and returns.  Touches nothing else; needs no handle.
+ * Errors: INVALID_ARG for a NULL pointer or a range past 2^32; DEVICE for a
+ * launch error. */
+rnn_status_t rnn_bf16_rounding_check(void* stream, unsigned long long first, unsigned long long count,
+                                     unsigned long long* mismatches);
+
 /* Diagnostic: the launch plan of the recurrent sweeps for (T, B, training)
  * as the compute calls would make it now (environment and device included).
  * Writes 16 ints to `out` (host memory): out[0..7] the forward sweep and

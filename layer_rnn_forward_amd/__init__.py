@@ -35,6 +35,7 @@ from ._binding import (  # noqa: F401
     rnn_backward_data,
     rnn_exchange_floor,
     rnn_mfma_peak_probe,
+    rnn_bf16_rounding_check,
     MFMA_PROBES,
     rnn_plan_info,
     PLAN_FIELDS,

@@ -62,6 +62,7 @@ def load_library():
         "rnn_device_status": [vp, vp, vp, sz],
         "rnn_exchange_floor": [vp, vp, i, i, i, vp, sz],
         "rnn_mfma_peak_probe": [vp, i, i, i, vp],
+        "rnn_bf16_rounding_check": [vp, ctypes.c_ulonglong, ctypes.c_ulonglong, vp],
         "rnn_plan_info": [vp, i, i, i, ctypes.POINTER(ctypes.c_int)],
         "rnn_set_profiling": [vp, i],
         "rnn_profile_read": [vp, i, ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_double)],
@@ -272,6 +273,15 @@ def rnn_mfma_peak_probe(kind: str, blocks: int, iters: int, out):
         raise ValueError("out holds fewer than blocks*256 floats")
     _check(load_library().rnn_mfma_peak_probe(_stream(), MFMA_PROBES[kind], blocks, iters,
                                               _ptr(out, "out")), "rnn_mfma_peak_probe")
+
+
+def rnn_bf16_rounding_check(first: int, count: int, mismatches):
+    """Enqueue the device check of the fp32 -> bf16 rounding over the bit
+    patterns [first, first + count); adds the mismatch count to
+    `mismatches`, an int64 device tensor of one element the caller zeroes."""
+    _check(load_library().rnn_bf16_rounding_check(_stream(), first, count,
+                                                  _ptr(mismatches, "mismatches", torch.int64)),
+           "rnn_bf16_rounding_check")
 
 
 def rnn_set_profiling(h, enable: bool):

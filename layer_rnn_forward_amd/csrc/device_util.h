@@ -10,10 +10,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // fp32 -> bf16 bits, round to nearest even: gfx950's v_cvt_pk_bf16_f32
-// (one instruction; the software rounding it replaces -- add 0x7fff plus the
-// lowest kept bit, keep the upper half -- gave the same bits for every
-// non-NaN fp32 pattern in an exhaustive check on the device, and NaNs stay
-// NaN).
+// (one instruction in place of the software rounding -- add 0x7fff plus the
+// lowest kept bit, keep the upper half; rnn_bf16_rounding_check compares the
+// two over every fp32 pattern on the device: same bits for every non-NaN
+// value, NaNs stay NaN).
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 

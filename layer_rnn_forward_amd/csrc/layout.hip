@@ -246,7 +246,36 @@ __global__ __launch_bounds__(256) void mfma_peak_32_kernel(int iters, float* out
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Check of the library's fp32 -> bf16 rounding (f2bf, the hardware
+// conversion) against round-to-nearest-even written out on the bit pattern:
+// add 0x7fff plus the lowest kept bit, keep the upper 16 bits; a NaN must
+// stay a NaN.  Patterns [first, first + count) (count <= 2^32), grid-stride;
+// each thread adds its mismatch count to *mism once.
+__global__ __launch_bounds__(256) void bf16_round_check_kernel(unsigned long long first, unsigned long long count,
+                                                               unsigned long long* mism) {
+  unsigned long long bad = 0;
+  const unsigned long long stride = (unsigned long long)gridDim.x * blockDim.x;
+  for (unsigned long long i = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+    const uint32_t u = (uint32_t)(first + i);
+    const uint16_t got = f2bf(__uint_as_float(u));
+    const bool nan = (u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0u;
+    if (nan) {
+      bad += ((got & 0x7f80u) != 0x7f80u || (got & 0x007fu) == 0u) ? 1u : 0u;
+    } else {
+      const uint16_t want = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+      bad += got != want ? 1u : 0u;
+    }
+  }
+  if (bad) atomicAdd(mism, bad);
+}
+
 }  // namespace
+
+hipError_t rnn_launch_bf16_round_check(unsigned long long first, unsigned long long count, unsigned long long* mism,
+                                       hipStream_t s) {
+  hipLaunchKernelGGL(bf16_round_check_kernel, dim3(2048), dim3(256), 0, s, first, count, mism);
+  return hipGetLastError();
+}
 
 hipError_t rnn_launch_mfma_peak(int kind, int blocks, int iters, float* out, hipStream_t s) {
   if (kind == 2) hipLaunchKernelGGL(mfma_peak_32_kernel, dim3(blocks), dim3(256), 0, s, iters, out);

@@ -1479,6 +1479,14 @@ rnn_status_t rnn_exchange_floor(rnn_handle_t h, void* stream, int T, int B, int 
   return exchange_probe_impl(h, stream, T, B, training, ws, ws_bytes);
 }
 
+rnn_status_t rnn_bf16_rounding_check(void* stream, unsigned long long first, unsigned long long count,
+                                     unsigned long long* mismatches) {
+  if (!mismatches || count > (1ull << 32) || first >= (1ull << 32) || first + count > (1ull << 32))
+    return RNN_STATUS_INVALID_ARG;
+  if (count == 0) return RNN_STATUS_SUCCESS;
+  return dev(rnn_launch_bf16_round_check(first, count, mismatches, reinterpret_cast<hipStream_t>(stream)));
+}
+
 rnn_status_t rnn_mfma_peak_probe(void* stream, int kind, int blocks, int iters, float* out) {
   if (kind < 0 || kind > 2 || blocks <= 0 || iters <= 0 || !out) return RNN_STATUS_INVALID_ARG;
   return dev(rnn_launch_mfma_peak(kind, blocks, iters, out, reinterpret_cast<hipStream_t>(stream)));

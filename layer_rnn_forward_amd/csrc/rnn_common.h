@@ -243,6 +243,8 @@ hipError_t rnn_launch_gemm(const rnnk::GemmParams& p, int bf16, int epi, int bat
 // rounds of eight independent MFMA chains per wave; one float per thread.
 // kind 0: fp32 16x16x4, 1: bf16 16x16x32, 2: bf16 32x32x16.
 hipError_t rnn_launch_mfma_peak(int kind, int blocks, int iters, float* out, hipStream_t s);
+hipError_t rnn_launch_bf16_round_check(unsigned long long first, unsigned long long count, unsigned long long* mism,
+                                       hipStream_t s);
 // Up to four ranges to fill with 32-bit patterns in the same launch as
 // another job (bytes: multiples of 4; count 0: none).
 struct FillJob {

@@ -407,6 +407,23 @@ def test_wavefront_at_moderate_width():
     assert info["fwd"]["groups"] == 3 * info["fwd"]["nchunk"], info
 
 
+def test_bf16_rounding_is_round_to_nearest_even():
+    """Every fp32 bit pattern (all 2^32): the library's fp32 -> bf16 rounding
+    (the hardware conversion) equals round-to-nearest-even written out on
+    the bits, and NaNs stay NaNs; a sub-range adds up the same way."""
+    import torch
+
+    m = torch.zeros(1, dtype=torch.int64, device="cuda")
+    R.rnn_bf16_rounding_check(0, 1 << 32, m)
+    torch.cuda.synchronize()
+    assert int(m.item()) == 0
+    R.rnn_bf16_rounding_check((1 << 32) - 1000, 1000, m)
+    torch.cuda.synchronize()
+    assert int(m.item()) == 0
+    with pytest.raises(R.RNNError):
+        R.rnn_bf16_rounding_check((1 << 32) - 10, 11, m)
+
+
 @pytest.mark.parametrize("wtype", ["f32", "bf16"])
 def test_weights_at_unaligned_offset(wtype):
     """W may sit at any 4-byte offset of a caller's parameter arena: with the
