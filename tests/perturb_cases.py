@@ -10,8 +10,8 @@ only inserts pauses at the exchange's waits and flag publications, so any
 difference is an ordering fault.  The shapes span every XCD (the DS2 hidden
 width of 800 gives 50-100 workgroups per group) and each placement and
 exchange kind: linear and line-sharing runs, XCD-local groups (tanh), the
-two-exchange GRU flavour, the layer wavefront with dropout, packed rows,
-and a one-row serving batch.
+two-exchange GRU flavours, the layer wavefront with dropout, packed rows,
+several batch chunks, a one-row serving batch and the stepped schedule.
 """
 
 import os
@@ -33,6 +33,10 @@ CASES = [
     ("gru_tf_bi_bf16", "gru_tf", 1, 2, 12, 20, 64, 800, "bf16", {}),
     ("lstm_wavefront_dropout_bf16", "lstm", 3, 1, 12, 20, 64, 800, "bf16", {"dropout": (0.3, 5)}),
     ("lstm_serving_b1_bf16", "lstm", 1, 1, 24, 1, 64, 800, "bf16", {"training": False}),
+    ("gru_multichunk_f32", "gru", 2, 2, 8, 70, 37, 256, "f32", {}),
+    ("gru_paper_packed_bf16", "gru_paper", 2, 1, 10, 13, 64, 384, "bf16", {"lengths": [10, 3, 0, 7, 10, 1, 9, 10, 2, 5, 8, 10, 4]}),
+    ("tanh_wavefront_f32", "rnn_tanh", 3, 1, 12, 5, 16, 512, "f32", {}),
+    ("lstm_stepped_bf16", "lstm", 1, 2, 10, 20, 64, 800, "bf16", {"sched": 2}),
 ]
 
 
