@@ -337,7 +337,39 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
           red[wave][row][rcol(row, nt * 16 + fr)] = acc[mt][nt][r];
         }
     lds_barrier();
-    if (s_fail) return;   // every wave leaves after the same barrier
+    // The eight-wave LSTM kernels of one row tile read the failure word with
+    // the partial sums, not before them, so its LDS round trip overlaps
+    // theirs (every wave leaves after the same barrier): DS2 training forward
+    // 722 -> 713 us.  The others keep the check first (the reordering moved
+    // their register allocation: wavefront sweep 1.84 -> 2.04 ms, GRU
+    // forward 684 -> 692 us, four-wave LSTM inference 0.778 -> 0.786 ms).
+    constexpr bool EARLY = UMAJ && MODE == MODE_LSTM && RSTR % 4 == 0 && NW == 8;
+    float pre_e[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (EARLY) {
+      const int failed = s_fail;
+      if (qv && live) {
+        // the unit's four gates are one 16-byte read per wave, all issued
+        // before the first sum
+        float4 v4[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) v4[w] = *reinterpret_cast<const float4*>(&red[w][qb][rcol(qb, qj * 4)]);
+        __builtin_amdgcn_sched_barrier(0);
+        pre_e[0] = v4[0].x;
+        pre_e[1] = v4[0].y;
+        pre_e[2] = v4[0].z;
+        pre_e[3] = v4[0].w;
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+          pre_e[0] += v4[w].x;
+          pre_e[1] += v4[w].y;
+          pre_e[2] += v4[w].z;
+          pre_e[3] += v4[w].w;
+        }
+      }
+      if (failed) return;
+    } else {
+      if (s_fail) return;
+    }
 
     float hnew = 0.f;
     float rv[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
@@ -346,23 +378,9 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) gxv[gi] = inproj ? bconst[gi] : gxl[gi];
       float pre[4] = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (UMAJ && MODE == MODE_LSTM && RSTR % 4 == 0) {
-        // the unit's four gates are one 16-byte read per wave
+      if constexpr (EARLY) {
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const float4 v4 = *reinterpret_cast<const float4*>(&red[w][qb][rcol(qb, qj * 4)]);
-          if (w == 0) {
-            pre[0] = v4.x;
-            pre[1] = v4.y;
-            pre[2] = v4.z;
-            pre[3] = v4.w;
-          } else {
-            pre[0] += v4.x;
-            pre[1] += v4.y;
-            pre[2] += v4.z;
-            pre[3] += v4.w;
-          }
-        }
+        for (int gi = 0; gi < 4; ++gi) pre[gi] = pre_e[gi];
       } else if constexpr (UMAJ) {
 #pragma unroll
         for (int gb = 0; gb < 4; ++gb) {
@@ -614,11 +632,19 @@ __global__ __launch_bounds__(NW * 64) void rnn_bwd_kernel(const BwdParams p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) red[wave][mt * 16 + fq * 4 + r][nt * 16 + fr] = acc[mt][nt][r];
       lds_barrier();
-      if (s_fail) return;   // every wave leaves after the same barrier
+      // (the failure word is read with the partial sums, so its LDS round
+      // trip overlaps theirs; every wave leaves after the same barrier)
+      const int failed = s_fail;
       if (qv) {
+        // every wave's partial issued before the first sum
+        float part[NW];
 #pragma unroll
-        for (int w = 0; w < NW; ++w) dhrec += red[w][qb][qj];
+        for (int w = 0; w < NW; ++w) part[w] = red[w][qb][qj];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int w = 0; w < NW; ++w) dhrec += part[w];
       }
+      if (failed) return;
     }
 
     float dgi[4] = {0.f, 0.f, 0.f, 0.f}, dgh[4] = {0.f, 0.f, 0.f, 0.f};
