@@ -159,9 +159,14 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
     return s_fail == 0;
   };
   auto reduce = [&](int gb) {
+    // every wave's partial issued before the first sum
+    float part[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) part[w] = red[w][qb][rcol(qb, gb * U + qj)];
+    __builtin_amdgcn_sched_barrier(0);
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += red[w][qb][rcol(qb, gb * U + qj)];
+    for (int w = 0; w < NW; ++w) v += part[w];
     return v;
   };
 
@@ -333,8 +338,13 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
     lds_barrier();
     float v = 0.f;
     if (qv) {
+      // every wave's partial issued before the first sum
+      float part[NW];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) v += red[w][qb][qj];
+      for (int w = 0; w < NW; ++w) part[w] = red[w][qb][qj];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += part[w];
     }
     return v;
   };
