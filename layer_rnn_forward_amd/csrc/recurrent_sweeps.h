@@ -101,11 +101,8 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
     else if constexpr (RSWZ2) return col ^ ((((row >> 1) & 1) | (((row ^ (row >> 2)) & 1) << 1)) << 3);
     else return col;
   };
-  // per-(row, unit) state of the epilogue threads, indexed by the thread
-  // (row-major with the workgroup's unit count as stride): one wave's
-  // accesses are consecutive words
-  __shared__ float sh_h[NCOL * NROW];
-  __shared__ float sh_c[NCOL * NROW];
+  // the per-(row, unit) state h, c of an epilogue thread lives in its own
+  // registers (hst, cst below): only the owning thread ever touches it
   __shared__ int s_fail;
 
   // (a scalar wave index, which helps the backward, measured 2-5 % slower here)
@@ -214,7 +211,6 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   const bool qw = q < Bact * U;             // writes the ring (zeros for padded units)
   const int qb = qw ? q / U : 0, qj = qw ? q - (q / U) * U : 0;
   const bool qv = qw && qj < Uact;          // a real (row, unit)
-  const int shix = qw ? q : 0;              // its slot in sh_h / sh_c (qb * U + qj)
   const bool w0 = Bact * U <= 64;           // every ring store is made by wave 0
   const int qu = u0 + qj, qbg = b0 + qb;
   const size_t st_idx = (((size_t)li * D + d) * B + qbg) * H + qu;
@@ -223,21 +219,22 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
   // valid steps of this row (t < qlen); past them the state is carried and y is 0
   const int qlen = (p.lengths && qv && live) ? min(max(p.lengths[qbg], 0), T) : T;
 
+  float hst = 0.f, cst = 0.f;   // this thread's h and c
   if (tid == 0) s_fail = 0;
   if (p.s_begin < 0) {
     float hv = 0.f, cv = 0.f;
     if (qv && live) {
       hv = p.h0 ? p.h0[hx_idx] : 0.f;
       cv = (MODE == MODE_LSTM && p.c0) ? p.c0[hx_idx] : 0.f;
-      sh_h[shix] = hv;
-      sh_c[shix] = cv;
+      hst = hv;
+      cst = cv;
     }
     const int first = p.wavefront ? li : 0;
     if (qw) ring_store<BF16>(ring + (size_t)first * p.ring_step, my_off, hv);
     if (p.persistent) publish(p.flags, wg, 1u);
   } else if (qv && live) {
-    sh_h[shix] = p.st_h[st_idx];
-    if (MODE == MODE_LSTM) sh_c[shix] = p.st_c[st_idx];
+    hst = p.st_h[st_idx];
+    if (MODE == MODE_LSTM) cst = p.st_c[st_idx];
   }
   __syncthreads();
 
@@ -405,17 +402,17 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
           pre[gb] = v;
         }
       }
-      const float hprev = sh_h[shix];
+      const float hprev = hst;
       const bool tv = t < qlen;
       if (MODE == MODE_LSTM) {
         const float ig = sigmoidf_(pre[0] + gxv[0]);
         const float fg = sigmoidf_(pre[1] + gxv[1]);
         const float gg = tanhf_<TSEL>(pre[2] + gxv[2]);
         const float og = sigmoidf_(pre[3] + gxv[3]);
-        const float cprev = sh_c[shix];
+        const float cprev = cst;
         const float cn = tv ? fg * cprev + ig * gg : cprev;
         hnew = og * tanhf_<TSEL>(cn);
-        sh_c[shix] = cn;
+        cst = cn;
         rv[0] = ig; rv[1] = fg; rv[2] = gg; rv[3] = og; rv[4] = cn;
       } else if (MODE == MODE_GRU) {
         const float rg = sigmoidf_(pre[0] + gxv[0]);
@@ -430,7 +427,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         hnew = tanhf_<TSEL>(pre[0] + gxv[0]);
       }
       if (!tv) hnew = hprev;
-      sh_h[shix] = hnew;
+      hst = hnew;
     }
     // only the exchange store precedes the flag; y and the reserve are read
     // by later kernels, so they are written after it, off the critical path
@@ -450,11 +447,11 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
 
   if (qv && live) {
     if (p.s_end >= p.s_total) {
-      if (p.hy) p.hy[hx_idx] = sh_h[shix];
-      if (MODE == MODE_LSTM && p.cy) p.cy[hx_idx] = sh_c[shix];
+      if (p.hy) p.hy[hx_idx] = hst;
+      if (MODE == MODE_LSTM && p.cy) p.cy[hx_idx] = cst;
     } else {
-      p.st_h[st_idx] = sh_h[shix];
-      if (MODE == MODE_LSTM) p.st_c[st_idx] = sh_c[shix];
+      p.st_h[st_idx] = hst;
+      if (MODE == MODE_LSTM) p.st_c[st_idx] = cst;
     }
   }
 }
