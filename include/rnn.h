@@ -112,7 +112,9 @@ rnn_status_t rnn_create(rnn_handle_t* out, rnn_mode_t mode, int num_layers, int 
 rnn_status_t rnn_destroy(rnn_handle_t h);
 
 /* Choose how the recurrent sweeps are launched (default RNN_SCHED_AUTO).
- * Results are bitwise identical across schedules. */
+ * Results are bitwise identical across schedules.  The TensorFlow and
+ * original-paper GRU flavours run only persistently: with RNN_SCHED_STEPPED
+ * their compute calls return RNN_STATUS_NOT_CORESIDENT. */
 rnn_status_t rnn_set_schedule(rnn_handle_t h, rnn_schedule_t s);
 
 /* Variable-length (packed) batches: the packed-sequence question of oneDNN
@@ -210,8 +212,8 @@ rnn_status_t rnn_workspace_size(rnn_handle_t h, int T, int B, int training, size
  * workspace.  Errors: INVALID_ARG (NULL required pointers, c0/cy given for a
  * non-LSTM mode, misaligned ws), WORKSPACE_TOO_SMALL, UNSUPPORTED (hidden
  * size beyond the kernels' limit, rnn_workspace_size), NOT_CORESIDENT (with
- * RNN_SCHED_PERSISTENT, or for the two-exchange GRU flavours, when the
- * sweep's workgroups cannot all be resident), DEVICE (launch failure). */
+ * RNN_SCHED_PERSISTENT, or for the two-exchange GRU flavours with
+ * RNN_SCHED_STEPPED or when the sweep's workgroups cannot all be resident), DEVICE (launch failure). */
 rnn_status_t rnn_forward_inference(rnn_handle_t h, void* stream, int T, int B, const float* x,
                                    const float* h0, const float* c0, const void* W, float* y,
                                    float* hy, float* cy, void* ws, size_t ws_bytes);
