@@ -81,8 +81,8 @@ __device__ __forceinline__ uint4 ones_vec(int k, int K) {
 
 // Store one wave's 64x64 accumulator tile (rows mw0.., columns nw0..): the
 // fp32 split-K partial, or C with the epilogue EPI.
-template <int EPI>
-__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const f32x4 (&acc)[4][4], int z,
+template <int EPI, int FN = 4>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const f32x4 (&acc)[4][FN], int z,
                                               int split, int mw0, int nw0, int fr, int fq) {
   const int M = p.M, N = p.N;
   if (p.split_k > 1) {
@@ -90,7 +90,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const f32x4 (
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < FN; ++nt) {
         const int n = nw0 + nt * 16 + fr;
         if (n >= N) continue;
 #pragma unroll
@@ -102,10 +102,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const f32x4 (
     return;
   }
   float* __restrict__ C = p.C[z];
-  float badd[4] = {0.f, 0.f, 0.f, 0.f};
+  float badd[FN] = {};
   if constexpr (EPI == EPI_BIAS) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < FN; ++nt) {
       const int n = min(nw0 + nt * 16 + fr, N - 1);
       float b = p.bias1 ? p.bias1[n] : 0.f;
       if (p.bias2 && ((n % p.gh) / p.hh) != p.bias2_skip_gate) b += p.bias2[n];
@@ -115,7 +115,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const f32x4 (
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < FN; ++nt) {
       const int n = nw0 + nt * 16 + fr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -255,12 +255,12 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
 // groups of GM tile rows, column by column inside a group, so that the
 // workgroups running at the same time on one XCD share few A and B row
 // blocks (0: row-major).
-template <bool BF16, int EPI, int NS, int GM, int WM, int WN>
+template <bool BF16, int EPI, int NS, int GM, int WM, int WN, int FN = 4>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(const GemmParams p) {
   using T = typename Cfg<BF16>::T;
   constexpr int BK = Cfg<BF16>::BK, EPV = Cfg<BF16>::EPV;
   constexpr int NW = WM * WN;
-  constexpr int TBM = 64 * WM, TBN = 64 * WN;
+  constexpr int TBM = 64 * WM, TBN = 16 * FN * WN;   // waves of 64 x 16*FN
   constexpr int SA = TBM * kRowBytes, SB = TBN * kRowBytes;   // one stage of A / of B
   constexpr int LA = TBM / (8 * NW), LB = TBN / (8 * NW);     // 1 KB loads per wave per stage
   static_assert(LA * 8 * NW == TBM && LB * 8 * NW == TBN, "whole 8-row load groups per wave");
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(const GemmParams
 
   // the wave index in a scalar register (the same in every lane)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = (wave / WN) * 64, wn = (wave % WN) * 64;
+  const int wm = (wave / WN) * 64, wn = (wave % WN) * (16 * FN);
   const int fr = lane & 15, fq = lane >> 4;
 
   // ---- loader: load j of wave w fills rows 8*(NW*j + w) .. +7 of a stage
@@ -346,11 +346,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(const GemmParams
 #pragma unroll
   for (int ch = 0; ch < CH; ++ch) fo[ch] = fr * kRowBytes + (((ch * 4 + fq) ^ (fr & 7)) * 16);
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][FN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i)
@@ -375,18 +375,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(const GemmParams
     const lds_char* sb = lds + NS * SA + st * SB + wn * kRowBytes;
 #pragma unroll
     for (int ch = 0; ch < CH; ++ch) {
-      uint4 af[4], bfr[4];
+      uint4 af[4], bfr[FN];
 #pragma unroll
       for (int t = 0; t < 4; ++t) af[t] = lds_read16(sa + t * 16 * kRowBytes + fo[ch]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bfr[t] = lds_read16(sb + t * 16 * kRowBytes + fo[ch]);
+      for (int t = 0; t < FN; ++t) bfr[t] = lds_read16(sb + t * 16 * kRowBytes + fo[ch]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_chunk<BF16>(af[mt], bfr[nt], acc[mt][nt]);
+        for (int nt = 0; nt < FN; ++nt) acc[mt][nt] = mfma_chunk<BF16>(af[mt], bfr[nt], acc[mt][nt]);
     }
   }
-  gemm_epilogue<EPI>(p, acc, z, split, m0 + wm, n0 + wn, fr, fq);
+  gemm_epilogue<EPI, FN>(p, acc, z, split, m0 + wm, n0 + wn, fr, fq);
 }
 
 // Fixed-order sum of the split-K partials, then the dW epilogue.
@@ -404,11 +404,13 @@ __global__ void splitk_reduce_kernel(const GemmParams p) {
 }
 
 // One configuration of the direct-to-LDS kernel: waves WM x WN, stages NS.
-template <bool BF16, int EPI, int NS, int GM, int WM, int WN>
+template <bool BF16, int EPI, int NS, int GM, int WM, int WN, int FN = 4>
 void launch_lds(const GemmParams& p, int batches, hipStream_t s) {
-  const int tiles = ((p.M + 64 * WM - 1) / (64 * WM)) * ((p.N + 64 * WN - 1) / (64 * WN)) * p.split_k;
+  const int tbn = 16 * FN * WN;
+  const int tiles = ((p.M + 64 * WM - 1) / (64 * WM)) * ((p.N + tbn - 1) / tbn) * p.split_k;
   const int grid = (tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_lds_kernel<BF16, EPI, NS, GM, WM, WN>), dim3(grid, 1, batches), dim3(64 * WM * WN), 0, s, p);
+  hipLaunchKernelGGL((gemm_lds_kernel<BF16, EPI, NS, GM, WM, WN, FN>), dim3(grid, 1, batches), dim3(64 * WM * WN), 0,
+                     s, p);
 }
 
 template <bool BF16, int EPI>
@@ -436,6 +438,15 @@ hipError_t launch_one(const GemmParams& p, int batches, hipStream_t s) {
       const int r256 = (((p.M + 255) / 256) * ((p.N + 255) / 256) + 255) / 256;
       if (33.2 * r256 < 25.0 * r128) v = 3;
     }
+    if (v == 0 && BF16 && EPI == EPI_STORE && p.split_k == 1) {
+      // the data gradient: 128 x 160 tiles (waves of 64 x 80) when one round
+      // of them, one per CU, replaces more than one round of 128 x 128 tiles
+      // (the 800-wide DS2 product splits into 5 column tiles instead of 6.25:
+      // measured 46.4 -> 41.9 us; three or four stages 44.7 / 43.6 us)
+      const int tm = (p.M + 127) / 128;
+      const int t160 = tm * ((p.N + 159) / 160) * batches, t128 = tm * ((p.N + 127) / 128) * batches;
+      if (t160 <= 256 && t128 > 256) v = 7;
+    }
     switch (v) {
       case 1: g8 ? launch_lds<BF16, EPI, 3, 8, 4, 2>(p, batches, s) : launch_lds<BF16, EPI, 3, 0, 4, 2>(p, batches, s); break;
       case 2: g8 ? launch_lds<BF16, EPI, 3, 8, 2, 4>(p, batches, s) : launch_lds<BF16, EPI, 3, 0, 2, 4>(p, batches, s); break;
@@ -443,6 +454,9 @@ hipError_t launch_one(const GemmParams& p, int batches, hipStream_t s) {
       case 4: g8 ? launch_lds<BF16, EPI, 4, 8, 2, 2>(p, batches, s) : launch_lds<BF16, EPI, 4, 0, 2, 2>(p, batches, s); break;
       case 5: g8 ? launch_lds<BF16, EPI, 3, 8, 2, 2>(p, batches, s) : launch_lds<BF16, EPI, 3, 0, 2, 2>(p, batches, s); break;
       case 6: g8 ? launch_lds<BF16, EPI, 2, 8, 4, 2>(p, batches, s) : launch_lds<BF16, EPI, 2, 0, 4, 2>(p, batches, s); break;
+      case 7: g8 ? launch_lds<BF16, EPI, 2, 8, 2, 2, 5>(p, batches, s) : launch_lds<BF16, EPI, 2, 0, 2, 2, 5>(p, batches, s); break;
+      case 8: g8 ? launch_lds<BF16, EPI, 3, 8, 2, 2, 5>(p, batches, s) : launch_lds<BF16, EPI, 3, 0, 2, 2, 5>(p, batches, s); break;
+      case 9: g8 ? launch_lds<BF16, EPI, 4, 8, 2, 2, 5>(p, batches, s) : launch_lds<BF16, EPI, 4, 0, 2, 2, 5>(p, batches, s); break;
       default:
         // two stages (64 KB of LDS, two workgroups per CU) measured faster
         // than three or four with one workgroup per CU
