@@ -42,7 +42,6 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
     if constexpr (RSWZ) return col ^ ((((row ^ (row >> 2)) & 3)) << 4);
     else return col;
   };
-  __shared__ float sh_h[NROW * NCOL];
   __shared__ int s_fail;
 
   // the wave index is the same in every lane: a scalar register keeps the
@@ -114,12 +113,15 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
   const int qlen = (p.lengths && qv) ? min(max(p.lengths[qbg], 0), T) : T;
   const float bhn = qv ? p.b_hh[0][(size_t)d * GH + 2 * H + qu] : 0.f;
 
+  // the state h of (qb, qj) lives in its owning thread's registers: no
+  // other thread reads it
+  float hst = 0.f;
   if (tid == 0) s_fail = 0;
   {
     float hv = 0.f;
     if (qv) {
       hv = p.h0 ? p.h0[hx_idx] : 0.f;
-      sh_h[qb * NCOL + qj] = hv;
+      hst = hv;
     }
     if (qw) ring_store<BF16>(ring, my_off, hv);
     publish(p.flags, wg, 1u);
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
     }
     // (1) h -> r, z
     if (!exchange(ring + (size_t)s * p.ring_step, (unsigned)(2 * s + 1))) return;
-    const float hprev = qv ? sh_h[qb * NCOL + qj] : 0.f;
+    const float hprev = hst;
     float rg = 0.f, zg = 0.f, rh = 0.f;
     if (qv) {
       rg = sigmoidf_(reduce(0) + gxl[0]);
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
       ng = tanhf_(gxl[2] + reduce(2) + bhn);
       hnew = p.paper ? (1.f - zg) * hprev + zg * ng : (1.f - zg) * ng + zg * hprev;
       if (!tv) hnew = hprev;
-      sh_h[qb * NCOL + qj] = hnew;
+      hst = hnew;
     }
     if (qw) ring_store<BF16>(ring + (size_t)(s + 1) * p.ring_step, my_off, hnew);
     publish(p.flags, wg, (unsigned)(2 * s + 3));
@@ -212,9 +214,9 @@ __global__ __launch_bounds__(NW * 64) void gru2_fwd_kernel(const FwdParams p) {
         res[3 * (size_t)H] = rh;
       }
     }
-    lds_barrier();   // red and sh_h are reused by the next step
+    lds_barrier();   // red is reused by the next step
   }
-  if (qv && p.hy) p.hy[hx_idx] = sh_h[qb * NCOL + qj];
+  if (qv && p.hy) p.hy[hx_idx] = hst;
 }
 
 // ====================================================================== bwd

@@ -442,7 +442,7 @@ __global__ __launch_bounds__(NW * 64) void rnn_fwd_kernel(const FwdParams p) {
         for (int r = 0; r < R; ++r) res[(size_t)r * H] = rv[r];
       }
     }
-    lds_barrier();   // red and sh_* are reused by the next step
+    lds_barrier();   // red is reused by the next step
   }
 
   if (qv && live) {
