@@ -232,7 +232,6 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
   // rows padded by 4 floats with one row tile: the four row groups of one
   // write instruction fall in distinct 16-bank groups
   __shared__ float red[NW][NROW][MT == 1 ? NCOL + 4 : NCOL + 1];
-  __shared__ float sh_dh[NROW * NCOL];
   __shared__ int s_fail;
 
   // the wave index is the same in every lane: a scalar register keeps the
@@ -308,7 +307,9 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
   const size_t offA = (size_t)(slice * UJ + qj / PER) * granA + qb * 16 + (qj % PER) * ES;
   const size_t offB = (size_t)(slice * 2 * UJ + qj / PER) * granB + qb * 16 + (qj % PER) * ES;
   if (tid == 0) s_fail = 0;
-  if (qv) sh_dh[qb * NCOL + qj] = p.dhy ? p.dhy[sidx] : 0.f;
+  // the carried dh of (qb, qj) lives in its owning thread's registers
+  float dhst = 0.f;
+  if (qv) dhst = p.dhy ? p.dhy[sidx] : 0.f;
   __syncthreads();
 
   // one exchange over ring entry `e` with weights `wf`
@@ -374,11 +375,11 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
       if (s_fail) return;
     }
     if (final_phase) {
-      if (qv && p.dh0) p.dh0[sidx] = dhrec + sh_dh[qb * NCOL + qj];
+      if (qv && p.dh0) p.dh0[sidx] = dhrec + dhst;
       break;
     }
     const bool tv = t < qlen;
-    const float dh = dhrec + (tv ? dyv : 0.f) + sh_dh[qb * NCOL + qj];
+    const float dh = dhrec + (tv ? dyv : 0.f) + dhst;
     float dn, dz, direct;
     if (p.paper) { dn = dh * zg; dz = dh * (ng - hp); direct = dh * (1.f - zg); }
     else { dn = dh * (1.f - zg); dz = dh * (hp - ng); direct = dh * zg; }
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
       daz = dz * zg * (1.f - zg);
       carry = direct + drh * rg;
     }
-    if (qv) sh_dh[qb * NCOL + qj] = carry;
+    if (qv) dhst = carry;
     if (qw) {
       char* en = ringB + (size_t)(s + 1) * p.ring_step2;
       ring_store<BF16>(en, offB, qv ? dar : 0.f);
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(NW * 64) void gru2_bwd_kernel(const BwdParams p) {
           reinterpret_cast<X*>(p.dgT)[(col0 + (size_t)g * H) * p.tb_ld + kp] = to_x<BF16>(dgv[g]);
       }
     }
-    lds_barrier();   // red and sh_dh are reused by the next step
+    lds_barrier();   // red is reused by the next step
   }
 }
 
