@@ -676,6 +676,16 @@ FillJob head_fill_job(void* head, void* extra = nullptr, size_t extra_bytes = 0)
   return f;
 }
 
+// A launch that clears a sweep's flags alongside its own job.
+FillJob flags_fill_job(void* flags, size_t bytes) {
+  FillJob f{};
+  f.p[0] = flags;
+  f.bytes[0] = bytes;
+  f.v[0] = 0u;
+  f.count = 1;
+  return f;
+}
+
 // Constant vectors and the kernel choice of a GEMM on this workspace.
 void gemm_consts(const rnn_desc* h, GemmParams& g, const void* ws, size_t off_head) {
   const char* c = reinterpret_cast<const char*>(ws) + off_head;
@@ -892,7 +902,12 @@ rnn_status_t forward_impl(rnn_desc* h, void* stream, int T, int B, const float* 
                                        h->drop_seed, l, drop, s)));
         in = xd;
       }
-      RNN_TRY(gemm_input(h, s, p, l, in, W, gx, ws, l == 0 ? pre : nullptr));
+      // the bf16 rounding of an upper layer's input runs after the sweep
+      // below and clears the flags of this layer's sweep in the same launch
+      const FillJob flag_job = flags_fill_job(at<void>(ws, p.off_flags), p.flags_bytes);
+      const bool fold = l > 0 && bf && f.persistent;
+      RNN_TRY(gemm_input(h, s, p, l, in, W, gx, ws, l == 0 ? pre : (fold ? &flag_job : nullptr)));
+      if (fold) flags_clear = true;
       f.first_layer = l;
       f.gx = gx;
       f.w_ih[0] = layer_w(h, W, RNN_W_IH, l);
@@ -1251,7 +1266,14 @@ rnn_status_t rnn_backward_data(rnn_handle_t h, void* stream, int T, int B, const
     // dX_l = dG_i W_ih  (both directions in one product, K = D*G*H); B = W_ih^T
     // (the top layer's was transposed before its sweep)
     const int I_l = in_width(h, l);
-    if (!(head_in_transpose && l == h->L - 1)) RNN_TRY(transpose_w(l, nullptr));
+    // (layer l's transpose runs after its sweep: below the top it also
+    // clears the flags of the next sweep, layer l-1's)
+    if (!(head_in_transpose && l == h->L - 1)) {
+      const FillJob flag_job = flags_fill_job(at<void>(ws, p.off_flags), p.flags_bytes);
+      const bool fold = l > 0 && b.persistent;
+      RNN_TRY(transpose_w(l, fold ? &flag_job : nullptr));
+      if (fold) flags_clear = true;
+    }
     GemmParams g{};
     g.M = T * B;
     g.N = I_l;
