@@ -10,9 +10,10 @@
 //
 // One layout only: C[m, n] = sum_k A[m, k] * B[n, k], both operands
 // K-contiguous, both in the compute type (bf16 with fp32 accumulation, or
-// fp32).  Tile 128x128, K step 32 (fp32) / 64 (bf16) -- 128 bytes of every
-// tile row per step -- 256 threads as 2x2 waves of 64x64 built from 16x16
-// MFMA tiles.  Tiles are numbered m-major and dealt to the 8 XCDs in
+// fp32).  Default tile 128x128, K step 32 (fp32) / 64 (bf16) -- 128 bytes of
+// every tile row per step -- 256 threads as 2x2 waves of 64x64 built from
+// 16x16 MFMA tiles (the direct-to-LDS kernel also runs other wave grids and
+// 64 x 16*FN wave tiles, below).  Tiles are numbered m-major and dealt to the 8 XCDs in
 // contiguous runs so that the tiles sharing an A row-block share an L2.
 // Optional split-K writes fp32 partials that a second kernel sums in a fixed
 // order (deterministic).
@@ -79,8 +80,8 @@ __device__ __forceinline__ uint4 ones_vec(int k, int K) {
   return *reinterpret_cast<const uint4*>(v);
 }
 
-// Store one wave's 64x64 accumulator tile (rows mw0.., columns nw0..): the
-// fp32 split-K partial, or C with the epilogue EPI.
+// Store one wave's 64 x 16*FN accumulator tile (rows mw0.., columns nw0..):
+// the fp32 split-K partial, or C with the epilogue EPI.
 template <int EPI, int FN = 4>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const f32x4 (&acc)[4][FN], int z,
                                               int split, int mw0, int nw0, int fr, int fq) {
@@ -250,8 +251,8 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
   return (((vm >> 4) & 3) << 14) | ((lgkm & 15) << 8) | (7 << 4) | (vm & 15);
 }
 
-// Block tile (64*WM) x (64*WN), WM x WN waves of 64x64; NS pipeline stages
-// of (64*WM + 64*WN) rows x 128 bytes of LDS; GM: tiles are visited in
+// Block tile (64*WM) x (16*FN*WN), WM x WN waves of 64 x 16*FN (4 x FN MFMA
+// tiles); NS pipeline stages of (64*WM + 16*FN*WN) rows x 128 bytes of LDS; GM: tiles are visited in
 // groups of GM tile rows, column by column inside a group, so that the
 // workgroups running at the same time on one XCD share few A and B row
 // blocks (0: row-major).
@@ -403,7 +404,8 @@ __global__ void splitk_reduce_kernel(const GemmParams p) {
   }
 }
 
-// One configuration of the direct-to-LDS kernel: waves WM x WN, stages NS.
+// One configuration of the direct-to-LDS kernel: waves WM x WN of 64 x 16*FN,
+// stages NS.
 template <bool BF16, int EPI, int NS, int GM, int WM, int WN, int FN = 4>
 void launch_lds(const GemmParams& p, int batches, hipStream_t s) {
   const int tbn = 16 * FN * WN;
