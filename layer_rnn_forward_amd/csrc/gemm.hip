@@ -442,12 +442,14 @@ hipError_t launch_one(const GemmParams& p, int batches, hipStream_t s) {
     }
     if (v == 0 && BF16 && EPI == EPI_STORE && p.split_k == 1) {
       // the data gradient: 128 x 160 tiles (waves of 64 x 80) when one round
-      // of them, one per CU, replaces more than one round of 128 x 128 tiles
-      // (the 800-wide DS2 product splits into 5 column tiles instead of 6.25:
-      // measured 46.4 -> 41.9 us; three or four stages 44.7 / 43.6 us)
+      // of them, one per CU or two, replaces more than one round of 128 x 128
+      // tiles at the same occupancy (the 800-wide DS2 product splits into 5
+      // column tiles instead of 6.25: measured 46.4 -> 41.9 us, three or four
+      // stages 44.7 / 43.6 us; the 1600-wide inner layers of a bidirectional
+      // stack, 470 tiles instead of 611: 143.8 -> 107 us)
       const int tm = (p.M + 127) / 128;
       const int t160 = tm * ((p.N + 159) / 160) * batches, t128 = tm * ((p.N + 127) / 128) * batches;
-      if (t160 <= 256 && t128 > 256) v = 7;
+      if ((t160 <= 256 && t128 > 256) || (t160 <= 512 && t128 > 512)) v = 7;
     }
     switch (v) {
       case 1: g8 ? launch_lds<BF16, EPI, 3, 8, 4, 2>(p, batches, s) : launch_lds<BF16, EPI, 3, 0, 4, 2>(p, batches, s); break;
