@@ -352,6 +352,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(const GemmParams
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the bias gradient's row sums (the 64 x 80 wave tiles only, so the other
+  // instances compile without it): the waves of the first column tile whose
+  // columns start at 0 also multiply their A fragments by ones (A reads
+  // zeros past K, and rows past M are never stored)
+  constexpr bool BIAS_MFMA = EPI == EPI_DW && FN == 5;
+  const bool bias_wave = BIAS_MFMA && p.bias_mfma && ni == 0 && wn == 0;
+  f32x4 accb[4] = {};
+  const unsigned one2 = BF16 ? 0x3f803f80u : 0x3f800000u;
+  const uint4 ones_frag = {one2, one2, one2, one2};
 
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i)
@@ -385,9 +394,22 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(const GemmParams
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < FN; ++nt) acc[mt][nt] = mfma_chunk<BF16>(af[mt], bfr[nt], acc[mt][nt]);
+      if (bias_wave) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) accb[mt] = mfma_chunk<BF16>(af[mt], ones_frag, accb[mt]);
+      }
     }
   }
   gemm_epilogue<EPI, FN>(p, acc, z, split, m0 + wm, n0 + wn, fr, fq);
+  if (bias_wave && fr == 0) {   // every column of accb holds the row sums
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm + mt * 16 + fq * 4 + r;
+        if (m < M) p.cbias[z][m] = accb[mt][r];
+      }
+  }
 }
 
 // Fixed-order sum of the split-K partials, then the dW epilogue.
@@ -450,6 +472,22 @@ hipError_t launch_one(const GemmParams& p, int batches, hipStream_t s) {
       const int tm = (p.M + 127) / 128;
       const int t160 = tm * ((p.N + 159) / 160) * batches, t128 = tm * ((p.N + 127) / 128) * batches;
       if ((t160 <= 256 && t128 > 256) || (t160 <= 512 && t128 > 512)) v = 7;
+    }
+    if (v == 0 && BF16 && EPI == EPI_DW && p.split_k == 1 && p.n_ones == p.N - 1 && p.N > 1) {
+      // a weight gradient: the bias row sums by MFMA against ones, so that
+      // the product is N - 1 wide, on 128 x 160 tiles, when one round of
+      // them at two per CU replaces more than one round of 128 x 128 tiles
+      // with the ones row
+      const int tm = (p.M + 127) / 128;
+      const int t160 = tm * ((p.N - 1 + 159) / 160) * batches, t128 = tm * ((p.N + 127) / 128) * batches;
+      if (t160 <= 512 && t128 > 512) {
+        GemmParams q = p;
+        q.N = p.N - 1;
+        q.n_ones = -1;
+        q.bias_mfma = 1;
+        g8 ? launch_lds<BF16, EPI, 2, 8, 2, 2, 5>(q, batches, s) : launch_lds<BF16, EPI, 2, 0, 2, 2, 5>(q, batches, s);
+        return hipGetLastError();
+      }
     }
     switch (v) {
       case 1: g8 ? launch_lds<BF16, EPI, 3, 8, 4, 2>(p, batches, s) : launch_lds<BF16, EPI, 3, 0, 4, 2>(p, batches, s); break;

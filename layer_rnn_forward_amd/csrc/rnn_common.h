@@ -64,6 +64,10 @@ struct GemmParams {
   const void* zero16;  // 16 bytes of zeros (device), or null: general kernel only
   const void* ones16;  // 16 bytes of ones in the compute type (device)
   int force_general;   // 1: always use the general kernel
+  // set by the launcher only (direct-to-LDS kernel, EPI_DW, no split):
+  // cbias[z][m] = sum_k A[m,k], from extra MFMAs against a ones fragment in
+  // the first column tile, instead of a ones row of B
+  int bias_mfma;
 };
 
 // Row-gather transpose: out[c * ld_out + r] = src_row(r)[c] for r < R, c < C,
